@@ -1,0 +1,99 @@
+// gear_internal.h -- declarations shared by the HIP sources of libgear.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/gear.h"
+
+namespace gear {
+
+constexpr int kThreads = 256;        // every kernel here runs 4 waves of 64
+constexpr int kMaxTeam = 32;         // workgroups cooperating on one matrix
+constexpr int kMaxRank = 8;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
+
+// Resolved packed layout, with device pointers of one buffer.
+struct Packed {
+    int64_t M;         // compressed matrices
+    int32_t rows;      // tokens per compressed matrix
+    int32_t d, bits, group, rank, k;
+    uint8_t* codes;
+    float* scale;
+    float* zero;
+    int32_t* row_ptr;
+    uint16_t* col;
+    uint16_t* val;     // fp16 bits
+    float* A;
+    float* B;
+};
+
+// ---- compress -------------------------------------------------------------
+struct CompressArgs {
+    const uint16_t* x;     // matrices [0, m_split): [m][rows][d] fp16 bits
+    const uint16_t* x2;    // matrices [m_split, M) (a second tensor)
+    int64_t m_split;
+    Packed out;
+    int32_t iters;
+    uint64_t seed;
+    uint8_t* team_ws;      // num_teams areas of team_bytes each
+    uint32_t* err;         // device failure word
+    int32_t team;          // workgroups per matrix (T)
+    int32_t num_teams;
+    size_t team_bytes;
+    size_t slot_bytes;     // one workgroup's partial (W, G) in a team area
+};
+
+// Compile-time shape of one compress instantiation.
+struct CompressShape {
+    int d, rk, rpl;        // head_dim, padded rank (0,2,4,8), rows per lane
+    int rows_per_wg() const { return 4 * rpl * (64 / (d / 8)); }
+};
+
+CompressShape choose_compress_shape(int d, int rank, int rows);
+size_t compress_team_bytes(const CompressShape& cs, int team, size_t* slot_bytes);
+// Number of teams one launch runs with (device occupancy bound); 0 on error.
+hipError_t compress_plan(const CompressShape& cs, int team, int64_t M, int* num_teams);
+hipError_t launch_compress(const CompressShape& cs, const CompressArgs& a, hipStream_t st);
+
+// ---- decompress -----------------------------------------------------------
+hipError_t launch_decompress(const Packed& p, uint16_t* out, hipStream_t st);
+
+// ---- streaming cache kernels ---------------------------------------------
+// Copy n_new tokens per (tensor, b, h) into the fp16 buffer at position pos.
+hipError_t launch_buffer_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* buf,
+                                int B, int H, int d, int cap, int pos, int n_new,
+                                int src_tokens, int src_off, hipStream_t st);
+
+// One compressed segment kind as seen by decode attention.
+struct AttnSeg {
+    Packed p;              // matrices ordered (tensor, b, h, chunk)
+    int32_t chunks;        // chunks per (tensor, b, h)
+    int32_t count;         // number of such packed buffers laid out back to back
+    size_t stride;         // bytes between consecutive buffers (count > 1)
+};
+
+struct AttnArgs {
+    int B, Hkv, Hq, d;
+    float sm_scale;
+    const uint16_t* q;     // [B][Hq][d]
+    float* out;            // [B][Hq][d]
+    AttnSeg prompt;        // prompt.count is 0 or 1
+    AttnSeg fills;         // fills.count = number of fills
+    const uint16_t* buf;   // [2][B][Hkv][cap][d]
+    int32_t buf_cap, buf_len;
+    float* partial;        // workspace: [B*Hkv][splits][G][d + 2]
+    int32_t splits;
+    int32_t tokens_per_split;
+};
+// Split partials start after the workspace's first 256 bytes, which hold the
+// device failure word that compress kernels of the same cache report through.
+constexpr size_t kAttnPartialOffset = 256;
+size_t attn_workspace_bytes(int B, int Hkv, int Hq, int d, int64_t tokens, int* splits,
+                            int* tokens_per_split);
+hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t st);
+
+}  // namespace gear

@@ -284,6 +284,7 @@ class OracleCache:
         self.buf_v = np.zeros((batch, kv_heads, buf_tokens, head_dim), np.uint16)
         self.buf_len = 0
         self.fills = []          # list of per-fill Compressed lists (K then V)
+        self.fill_inputs = []    # the fp16 inputs of each fill, [2*B*H, n_b, d]
 
     def load_prompt(self, k, v):
         """k, v: fp16 [B, H, n, d]; compressed with the prompt settings."""
@@ -310,6 +311,7 @@ class OracleCache:
             x = np.concatenate([self.buf_k.reshape(B * H, nb, d),
                                 self.buf_v.reshape(B * H, nb, d)])
             segs = compress(x, Params(**{**self.fill_p.__dict__, "chunk_tokens": 0}))
+            self.fill_inputs.append(x)
             for t in range(2):
                 for b in range(B):
                     for h in range(H):
