@@ -62,12 +62,9 @@ gear_status check_params(const gear_params* p, int64_t rows, int d) {
     if (p->rank > mrows)
         return fail(GEAR_ERR_INVALID_ARG, "rank %d exceeds tokens per matrix %lld", p->rank,
                     (long long)mrows);
-    const CompressShape cs = choose_compress_shape(d, p->rank, (int)mrows);
-    const int64_t team = (mrows + cs.rows_per_wg() - 1) / cs.rows_per_wg();
-    if (team > kMaxTeam || mrows > (1 << 24))
-        return fail(GEAR_ERR_UNSUPPORTED,
-                    "%lld tokens per matrix is above this library's limit of %d; use chunk_tokens",
-                    (long long)mrows, kMaxTeam * cs.rows_per_wg());
+    if (mrows > (1 << 24))
+        return fail(GEAR_ERR_UNSUPPORTED, "%lld tokens per matrix is above this library's limit of %d",
+                    (long long)mrows, 1 << 24);
     return GEAR_OK;
 }
 
@@ -118,30 +115,13 @@ Packed make_packed(const gear_params* p, const gear_layout& L, int d, void* base
 }
 
 constexpr size_t kWsHeader = 256;          // device failure word
-constexpr int kMaxResidentWG = 4096;       // bound used to size team workspaces
 
 struct CompressPlan {
-    CompressShape cs;
-    int team;
-    int ws_teams;          // team areas the workspace holds
-    size_t team_bytes, slot_bytes, ws_bytes;
+    size_t ws_bytes;
 };
 
-CompressPlan plan_compress(const gear_params* p, const gear_layout& L, int d) {
-    CompressPlan pl;
-    pl.cs = choose_compress_shape(d, p->rank, L.rows);
-    pl.team = (L.rows + pl.cs.rows_per_wg() - 1) / pl.cs.rows_per_wg();
-    pl.team_bytes = compress_team_bytes(pl.cs, pl.team, &pl.slot_bytes);
-    if (pl.team == 1) {
-        pl.ws_teams = 0;
-    } else {
-        const int64_t by_m = (L.num_compressed + 7) / 8 * 8;
-        int64_t by_dev = (int64_t)(kMaxResidentWG / 8 / pl.team) * 8;
-        if (by_dev < 8) by_dev = 8;
-        pl.ws_teams = (int)(by_m < by_dev ? by_m : by_dev);
-    }
-    pl.ws_bytes = kWsHeader + (size_t)pl.ws_teams * pl.team_bytes;
-    return pl;
+CompressPlan plan_compress(const gear_params*, const gear_layout&, int) {
+    return CompressPlan{kWsHeader};
 }
 
 // Compress matrices [0, m_split) from x and [m_split, M) from x2.
@@ -161,16 +141,7 @@ gear_status run_compress(const gear_params* p, const gear_layout& L, int d, cons
     a.iters = p->power_iters;
     a.seed = p->seed;
     a.err = static_cast<uint32_t*>(ws);
-    a.team_ws = static_cast<uint8_t*>(ws) + kWsHeader;
-    a.team = pl.team;
-    a.team_bytes = pl.team_bytes;
-    a.slot_bytes = pl.slot_bytes;
-    int teams = 0;
-    hipError_t e = compress_plan(pl.cs, pl.team, L.num_compressed, &teams);
-    if (e != hipSuccess) return hip_fail(e, "compress occupancy query");
-    if (pl.team > 1 && teams > pl.ws_teams) teams = pl.ws_teams;
-    a.num_teams = teams;
-    e = launch_compress(pl.cs, a, st);
+    hipError_t e = launch_compress(a, st);
     if (e != hipSuccess) return hip_fail(e, "compress launch");
     return GEAR_OK;
 }

@@ -10,7 +10,6 @@
 namespace gear {
 
 constexpr int kThreads = 256;        // every kernel here runs 4 waves of 64
-constexpr int kMaxTeam = 32;         // workgroups cooperating on one matrix
 constexpr int kMaxRank = 8;
 constexpr size_t kAlign = 256;
 
@@ -39,25 +38,9 @@ struct CompressArgs {
     Packed out;
     int32_t iters;
     uint64_t seed;
-    uint8_t* team_ws;      // num_teams areas of team_bytes each
-    uint32_t* err;         // device failure word
-    int32_t team;          // workgroups per matrix (T)
-    int32_t num_teams;
-    size_t team_bytes;
-    size_t slot_bytes;     // one workgroup's partial (W, G) in a team area
+    uint32_t* err;         // device failure word (cleared by the launch)
 };
-
-// Compile-time shape of one compress instantiation.
-struct CompressShape {
-    int d, rk, rpl;        // head_dim, padded rank (0,2,4,8), rows per lane
-    int rows_per_wg() const { return 4 * rpl * (64 / (d / 8)); }
-};
-
-CompressShape choose_compress_shape(int d, int rank, int rows);
-size_t compress_team_bytes(const CompressShape& cs, int team, size_t* slot_bytes);
-// Number of teams one launch runs with (device occupancy bound); 0 on error.
-hipError_t compress_plan(const CompressShape& cs, int team, int64_t M, int* num_teams);
-hipError_t launch_compress(const CompressShape& cs, const CompressArgs& a, hipStream_t st);
+hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
 // ---- decompress -----------------------------------------------------------
 hipError_t launch_decompress(const Packed& p, uint16_t* out, hipStream_t st);

@@ -76,7 +76,7 @@ def test_layout_counts(p, M, n, d, Mc, rows, k):
     (gear.Params(rank=4, power_iters=0), 64, 128, 1),
     (gear.Params(rank=8), 4, 128, 1),
     (gear.Params(chunk_tokens=100), 256, 128, 1),
-    (gear.Params(), 100000, 128, 2),
+    (gear.Params(), 1 << 25, 128, 2),
     (gear.Params(), 0, 128, 1),
 ])
 def test_invalid_settings_rejected_on_host(p, n, d, status):
