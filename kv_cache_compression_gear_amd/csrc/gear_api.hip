@@ -120,8 +120,8 @@ struct CompressPlan {
     size_t ws_bytes;
 };
 
-CompressPlan plan_compress(const gear_params*, const gear_layout&, int) {
-    return CompressPlan{kWsHeader};
+CompressPlan plan_compress(const gear_params*, const gear_layout& L, int) {
+    return CompressPlan{kWsHeader + align_up((size_t)L.num_compressed * kSelStride * 4)};
 }
 
 // Compress matrices [0, m_split) from x and [m_split, M) from x2.
@@ -141,6 +141,7 @@ gear_status run_compress(const gear_params* p, const gear_layout& L, int d, cons
     a.iters = p->power_iters;
     a.seed = p->seed;
     a.err = static_cast<uint32_t*>(ws);
+    a.sel = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
     hipError_t e = launch_compress(a, st);
     if (e != hipSuccess) return hip_fail(e, "compress launch");
     return GEAR_OK;

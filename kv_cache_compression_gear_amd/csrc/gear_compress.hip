@@ -15,12 +15,13 @@
 //     D/8 lanes per token row.  Nothing is exchanged between workgroups, so
 //     no grid-level synchronisation or device-scope fence is needed, and
 //     thousands of entries are processed between the few workgroup barriers.
-//   * Pass 1: 1024-bin histogram of |x| >> 5 in LDS -> the coarse bin of the
-//     k-th largest magnitude.  Pass 2: per-wave 32-bin histograms inside that
+//   * Pass 1: 4096-bin histogram of |x| >> 3 in LDS -> the coarse bin of the
+//     k-th largest magnitude.  Pass 2: per-wave 8-bin histograms inside that
 //     bin -> the exact threshold key, the number of ties to take, and every
 //     wave's CSR start and tie quota (flat order = wave order, then row, lane).
 //   * Pass 3: outlier mask, CSR emit (wave-level prefix sums), bit-exact fp32
-//     group quantization (correctly rounded division, rint) with codes packed
+//     group quantization (rint of the correctly rounded quotient, taken from a
+//     reciprocal product away from rounding ties) with codes packed
 //     in registers and stored as one 32- or 16-bit word per lane per token,
 //     and the first power-iteration product.  Passes 4..: the remaining power
 //     steps, with R = D - deq(Q) recomputed from X and the stored codes.
@@ -44,6 +45,33 @@ __device__ __forceinline__ float h2f(uint32_t b) {
 __device__ __forceinline__ uint32_t half_of(const uint4& w, int e) {
     const uint32_t v = (e >> 1) == 0 ? w.x : (e >> 1) == 1 ? w.y : (e >> 1) == 2 ? w.z : w.w;
     return (v >> (16 * (e & 1))) & 0xffffu;
+}
+
+// DPP lane exchange (no LDS traffic).  quad_perm(1,0,3,2) = 0xB1,
+// quad_perm(2,3,0,1) = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N lanes (N = 8 or 16), result in every lane:
+// pairs, then quads, then the mirrored quad, then the mirrored half-row.
+template <int N>
+__device__ __forceinline__ float row_allreduce(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    if (N >= 8) v += dpp<0x141>(v);
+    if (N >= 16) v += dpp<0x140>(v);
+    return v;
+}
+
+// min and max over each aligned group of g lanes, g in {1, 2, 4, 8, 16}.
+__device__ __forceinline__ void group_minmax(float& mn, float& mx, int g) {
+    if (g >= 2) { mn = fminf(mn, dpp<0xB1>(mn)); mx = fmaxf(mx, dpp<0xB1>(mx)); }
+    if (g >= 4) { mn = fminf(mn, dpp<0x4E>(mn)); mx = fmaxf(mx, dpp<0x4E>(mx)); }
+    if (g >= 8) { mn = fminf(mn, dpp<0x141>(mn)); mx = fmaxf(mx, dpp<0x141>(mx)); }
+    if (g >= 16) { mn = fminf(mn, dpp<0x140>(mn)); mx = fmaxf(mx, dpp<0x140>(mx)); }
 }
 
 // Exclusive prefix sum over the 256 threads of the block; *total = full sum.
@@ -121,27 +149,25 @@ __device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, float* Mou
         alive[j] = (pre2 > 0.0) && (post2 > 1e-12 * pre2);
         c[j][j] = alive[j] ? sqrt(post2) : 0.0;
     }
-    double m[RK][RK];
+    // M = C^-1 in place (upper triangular; column j only needs columns < j of
+    // the inverse and column j of C, overwritten top to bottom); a dead pivot
+    // gives a zero row and column.
 #pragma unroll
     for (int j = 0; j < RK; ++j) {
         const double inv = alive[j] ? 1.0 / c[j][j] : 0.0;
 #pragma unroll
-        for (int a = 0; a < RK; ++a) {
-            if (a > j) {
-                m[a][j] = 0.0;
-                continue;
-            }
-            double v = (a == j) ? 1.0 : 0.0;
+        for (int i = 0; i < j; ++i) {
+            double v = 0.0;
 #pragma unroll
-            for (int i = 0; i < j; ++i)
-                if (a <= i) v -= m[a][i] * c[i][j];
-            m[a][j] = v * inv;
+            for (int k = i; k < j; ++k) v += c[i][k] * c[k][j];
+            c[i][j] = -v * inv;
         }
+        c[j][j] = inv;
     }
 #pragma unroll
     for (int a = 0; a < RK; ++a)
 #pragma unroll
-        for (int j = 0; j < RK; ++j) Mout[a * RK + j] = (float)m[a][j];
+        for (int j = 0; j < RK; ++j) Mout[a * RK + j] = a <= j ? (float)c[a][j] : 0.0f;
 }
 
 template <int RK>
@@ -152,6 +178,367 @@ struct PairLanes {
                             : NP <= 16 ? 4 : NP <= 32 ? 2 : 1;
 };
 
+constexpr int kCoarse = 4096;   // pass-1 bins: |x| bit pattern >> 3
+constexpr int kFine = 8;        // pass-2 bins inside the chosen coarse bin
+constexpr int kFineSlot = kFine + 1;
+constexpr int kSelThreads = 1024;
+
+// U consecutive row steps of one wave: the X words, and (after the first
+// pass) the stored code word and the group's scale and zero of each row.
+template <int U>
+struct StepBuf {
+    uint4 x[U];
+    uint32_t cw[U];
+    float sc[U], zp[U];
+};
+
+template <int D, int U, int RPS>
+__device__ __forceinline__ void load_steps(StepBuf<U>& b, const uint16_t* xm, const Packed& o,
+                                           int64_t mm, int rows, int wr0, int s0, int steps,
+                                           int rl, int colq, bool with_codes) {
+    const int ngr = D / o.group, gl = o.group / 8;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int row = wr0 + (s0 + u) * RPS + rl;
+        const bool ok = s0 + u < steps && row < rows;
+        b.x[u] = ok ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
+                    : make_uint4(0u, 0u, 0u, 0u);
+        b.cw[u] = 0u;
+        b.sc[u] = 0.0f;
+        b.zp[u] = 0.0f;
+        if (with_codes && ok) {
+            const size_t grow = (size_t)mm * rows + row;
+            b.cw[u] = o.bits == 4 ? reinterpret_cast<const uint32_t*>(o.codes)[grow * (D / 8) + colq]
+                                  : reinterpret_cast<const uint16_t*>(o.codes)[grow * (D / 8) + colq];
+            b.sc[u] = o.scale[grow * ngr + colq / gl];
+            b.zp[u] = o.zero[grow * ngr + colq / gl];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Outlier threshold: the k-th largest |x| of a matrix, with ties broken by
+// the lower flat index.  One 16-wave workgroup per matrix.  The rows are split
+// exactly as the compress kernel splits them over its 4 waves; each of those
+// row blocks is read here by 4 consecutive waves.  Output per matrix
+// (kSelStride words): threshold key, then for each of the 4 row blocks the
+// number of ties at the threshold it takes, then its first CSR position.
+//
+// Common path (one pass over X plus a 1/16 sample): a histogram of a sample
+// of rows gives a key L0 that at least ~1.25 k entries reach; one pass then
+// counts, per row block, every key in the window [L0, L0 + 4096) exactly and
+// every key above it.  If the k-th largest key lies in the window this is
+// the exact answer (checked from the counts); otherwise a two-pass radix
+// select over all keys (4096 coarse bins, then 8 fine bins) is used.
+template <int D, int U>
+__global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
+    constexpr int LPR = D / 8, RPS = 64 / LPR;
+    constexpr int NW = kSelThreads / 64;       // 16 waves
+    constexpr int kWin = 4096;                 // exact window of keys
+    constexpr int kSampleEvery = 16;           // sample = every 16th step
+    __shared__ uint32_t s_hist[kCoarse];
+    __shared__ uint32_t s_win[4 * kWin];
+    __shared__ uint32_t s_cnt[2 * NW];
+    __shared__ uint32_t s_fine[NW * kFineSlot];
+    __shared__ uint32_t s_tmp[NW];
+    __shared__ uint32_t s_res[12];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int colq = lane % LPR, rl = lane / LPR;
+    const Packed& o = a.out;
+    const int64_t mm = blockIdx.x;
+    const int rows = o.rows;
+    const uint32_t kk = (uint32_t)o.k;
+    uint32_t* sel = a.sel + (size_t)mm * kSelStride;
+    if (kk == 0) {
+        if (tid < kSelStride) sel[tid] = tid == 0 ? 0x8000u : 0u;
+        return;
+    }
+    const int rw = ((rows + 3) / 4 + RPS - 1) / RPS * RPS;
+    const int steps = rw / RPS;
+    const int mb = wv / 4, sub = wv % 4;
+    const int per = (steps + 3) / 4;
+    const int sb = min(steps, sub * per), se = min(steps, sb + per);
+    const int wr0 = mb * rw;
+    const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
+                                         : a.x2 + (size_t)(mm - a.m_split) * rows * D;
+    for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
+    for (int i = tid; i < 4 * kWin; i += kSelThreads) s_win[i] = 0u;
+    if (tid < NW * kFineSlot) s_fine[tid] = 0u;
+    if (tid < 12) s_res[tid] = 0u;
+    __syncthreads();
+
+    auto load = [&](uint4 (&xr)[U], bool (&ok)[U], int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = wr0 + (s0 + u) * RPS + rl;
+            ok[u] = s0 + u < se && row < rows;
+            xr[u] = ok[u] ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    // Thread t owns 4 consecutive bins of a 4096-bin table, the top ones first;
+    // returns the bin where the count from the top, started at `base`,
+    // reaches `target` (writes it to *out; no write if never reached).
+    auto find_bin = [&](const uint32_t (&h)[4], uint32_t base, uint32_t target, uint32_t* out) {
+        const int b0 = (kSelThreads - 1 - tid) * 4;
+        const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+        uint32_t x = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        __syncthreads();
+        if (lane == 63) s_tmp[wv] = x;
+        __syncthreads();
+        uint32_t cum = base + x - sum;
+        for (int w = 0; w < wv; ++w) cum += s_tmp[w];
+#pragma unroll
+        for (int q = 3; q >= 0; --q) {
+            if (cum < target && cum + h[q] >= target) *out = (uint32_t)(b0 + q);
+            cum += h[q];
+        }
+    };
+
+    // ---- sample: every 16th step of each wave's range
+    uint32_t nsamp = 0;
+    for (int s0 = sb; s0 < se; s0 += kSampleEvery) {
+        const int row = wr0 + s0 * RPS + rl;
+        if (row < rows) {
+            const uint4 xr = *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8);
+            const uint32_t w4[4] = {xr.x, xr.y, xr.z, xr.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                atomicAdd(&s_hist[__builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 19u : 3u, 12u)], 1u);
+            nsamp += 8;
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) nsamp += __shfl_xor(nsamp, off, 64);
+    if (lane == 0) s_cnt[wv] = nsamp;
+    __syncthreads();
+    uint32_t total_samp = 0;
+    for (int w = 0; w < NW; ++w) total_samp += s_cnt[w];
+    const double frac = (double)total_samp / ((double)rows * D);
+    const double expect = (double)kk * frac;
+    const uint32_t target = (uint32_t)(1.25 * expect + 4.0 * sqrt(expect) + 8.0);
+    uint32_t L0 = 0;
+    if (target <= total_samp) {
+        uint32_t h[4];
+        const int b0 = (kSelThreads - 1 - tid) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = s_hist[b0 + q];
+        find_bin(h, 0u, target, &s_res[0]);
+        __syncthreads();
+        L0 = s_res[0] << 3;
+    }
+
+    // ---- window pass: exact counts of keys in [L0, L0 + kWin), count above
+    uint32_t above = 0;
+    auto window = [&](const uint4 (&xr)[U], const bool (&ok)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (!ok[u]) continue;
+            const uint32_t w4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+            bool any = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t key = __builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 16u : 0u, 15u);
+                const uint32_t dlt = key - L0;
+                above += (key >= L0 + kWin) ? 1u : 0u;
+                any |= dlt < (uint32_t)kWin;
+            }
+            if (any) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t key = __builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 16u : 0u, 15u);
+                    const uint32_t dlt = key - L0;
+                    if (dlt < (uint32_t)kWin) atomicAdd(&s_win[mb * kWin + dlt], 1u);
+                }
+            }
+        }
+    };
+    {
+        uint4 xa[U], xb[U];
+        bool oka[U], okb[U];
+        load(xa, oka, sb);
+        for (int s0 = sb; s0 < se; s0 += 2 * U) {
+            load(xb, okb, s0 + U);
+            window(xa, oka);
+            load(xa, oka, s0 + 2 * U);
+            window(xb, okb);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) above += __shfl_xor(above, off, 64);
+    if (lane == 0) s_cnt[NW + wv] = above;
+    __syncthreads();
+    uint32_t above_b[4], above_tot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        above_b[b] = s_cnt[NW + 4 * b] + s_cnt[NW + 4 * b + 1] + s_cnt[NW + 4 * b + 2] + s_cnt[NW + 4 * b + 3];
+        above_tot += above_b[b];
+    }
+    {
+        uint32_t h[4];
+        const int b0 = (kSelThreads - 1 - tid) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            h[q] = s_win[b0 + q] + s_win[kWin + b0 + q] + s_win[2 * kWin + b0 + q] + s_win[3 * kWin + b0 + q];
+        s_res[1] = 0xffffffffu;
+        __syncthreads();
+        if (above_tot < kk) find_bin(h, above_tot, kk, &s_res[1]);
+        __syncthreads();
+    }
+    const uint32_t jstar = s_res[1];
+    if (jstar != 0xffffffffu) {
+        // exact threshold T = L0 + j*; per block: ties at T, count above T
+        const int b0 = (kSelThreads - 1 - tid) * 4;
+        uint32_t gtp[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if ((uint32_t)(b0 + q) > jstar) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b) gtp[b] += s_win[b * kWin + b0 + q];
+            }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) gtp[b] += __shfl_xor(gtp[b], off, 64);
+            if (lane == 0 && gtp[b]) atomicAdd(&s_res[4 + b], gtp[b]);
+        }
+        __syncthreads();
+        if (wv == 0) {
+            const uint32_t eq = lane < 4 ? s_win[lane * kWin + jstar] : 0u;
+            uint32_t gt = 0;
+            if (lane < 4) gt = s_res[4 + lane] + (lane == 0 ? above_b[0] : lane == 1 ? above_b[1]
+                                                 : lane == 2 ? above_b[2] : above_b[3]);
+            uint32_t tot_gt = gt;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) tot_gt += __shfl_xor(tot_gt, off, 64);
+            const uint32_t need = kk - tot_gt;   // ties to take, >= 1
+            uint32_t tt;
+            const uint32_t ties_before = wave_excl_scan(eq, lane, &tt);
+            const uint32_t take = (need > ties_before) ? min(eq, need - ties_before) : 0u;
+            const uint32_t before = wave_excl_scan(gt + take, lane, &tt);
+            if (lane == 0) sel[0] = L0 + jstar;
+            if (lane < 4) {
+                sel[1 + lane] = take;
+                sel[5 + lane] = before;
+            }
+        }
+        return;
+    }
+
+    // ---- fallback: radix select over all keys (4096 coarse bins, then 8 fine)
+    for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
+    __syncthreads();
+    auto hist = [&](const uint4 (&xr)[U], const bool (&ok)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) {
+                const uint32_t w4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    atomicAdd(&s_hist[__builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 19u : 3u, 12u)], 1u);
+            }
+    };
+    {
+        uint4 xa[U], xb[U];
+        bool oka[U], okb[U];
+        load(xa, oka, sb);
+        for (int s0 = sb; s0 < se; s0 += 2 * U) {
+            load(xb, okb, s0 + U);
+            hist(xa, oka);
+            load(xa, oka, s0 + 2 * U);
+            hist(xb, okb);
+        }
+    }
+    __syncthreads();
+    {
+        uint32_t h[4];
+        const int b0 = (kSelThreads - 1 - tid) * 4;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) h[q] = s_hist[b0 + q];
+        find_bin(h, 0u, kk, &s_res[2]);
+        __syncthreads();
+    }
+    const uint32_t bstar = s_res[2];
+    uint32_t my_above = 0;
+    auto fine = [&](const uint4 (&xr)[U], const bool (&ok)[U]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t w4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+            bool any = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t kb = __builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 19u : 3u, 12u);
+                my_above += (ok[u] && kb > bstar) ? 1u : 0u;
+                any |= kb == bstar;
+            }
+            if (__ballot(ok[u] && any) != 0ull && ok[u] && any) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t key = half_of(xr[u], e) & 0x7fffu;
+                    if ((key >> 3) == bstar) atomicAdd(&s_fine[wv * kFineSlot + (key & 7u)], 1u);
+                }
+            }
+        }
+    };
+    {
+        uint4 xa[U], xb[U];
+        bool oka[U], okb[U];
+        load(xa, oka, sb);
+        for (int s0 = sb; s0 < se; s0 += 2 * U) {
+            load(xb, okb, s0 + U);
+            fine(xa, oka);
+            load(xa, oka, s0 + 2 * U);
+            fine(xb, okb);
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) my_above += __shfl_xor(my_above, off, 64);
+    if (lane == 0) s_fine[wv * kFineSlot + kFine] = my_above;
+    __syncthreads();
+    if (wv == 0) {
+        uint32_t F = 0, abv = 0;
+        for (int w = 0; w < NW; ++w) {
+            if (lane < kFine) F += s_fine[w * kFineSlot + lane];
+            abv += s_fine[w * kFineSlot + kFine];
+        }
+        const uint32_t needk = kk - abv;   // >= 1 by the choice of the coarse bin
+        uint32_t suf = (lane < kFine) ? F : 0u;  // lane f: sum of F[f'] for f' >= f
+#pragma unroll
+        for (int off = 1; off < kFine; off <<= 1) {
+            const uint32_t y = __shfl_down(suf, off, 64);
+            if (lane + off < kFine) suf += y;
+        }
+        const uint32_t strictly_above = suf - ((lane < kFine) ? F : 0u);
+        const uint64_t bal = __ballot(lane < kFine && strictly_above < needk && suf >= needk);
+        const int fstar = bal ? (int)__builtin_ctzll(bal) : 0;
+        const uint32_t need = needk - __shfl(strictly_above, fstar, 64);   // ties to take
+        uint32_t eq = 0, gt = 0;
+        if (lane < 4) {
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t* f = s_fine + (lane * 4 + j) * kFineSlot;
+                eq += f[fstar];
+                gt += f[kFine];
+                for (int q = fstar + 1; q < kFine; ++q) gt += f[q];
+            }
+        }
+        uint32_t tt;
+        const uint32_t ties_before = wave_excl_scan(eq, lane, &tt);
+        const uint32_t take = (need > ties_before) ? min(eq, need - ties_before) : 0u;
+        const uint32_t before = wave_excl_scan(gt + take, lane, &tt);
+        if (lane == 0) sel[0] = (bstar << 3) | (uint32_t)fstar;
+        if (lane < 4) {
+            sel[1 + lane] = take;
+            sel[5 + lane] = before;
+        }
+    }
+}
+
 template <int D, int RK, int U>
 __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
@@ -160,12 +547,8 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     constexpr int NP = RKX * (RKX + 1) / 2;
     constexpr int LP = PairLanes<RKX>::LP;
     constexpr int RING_STEPS = kRing / RPS;
+    static_assert(RING_STEPS % (2 * U) == 0 || (2 * U) % RING_STEPS == 0, "ring/step blocking");
 
-    __shared__ uint32_t s_hist[1024];
-    __shared__ uint32_t s_fine[4 * 33];
-    __shared__ uint32_t s_tmp[8];
-    __shared__ uint32_t s_sel[4];
-    __shared__ uint32_t s_wave[4 * 2];
     __shared__ float s_b0[D * RKX];
     __shared__ float s_w[4 * D * RKX];
     __shared__ float s_ring[4 * kRing * RKX];
@@ -203,115 +586,18 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         }
     }
 
-    // ======================= outlier threshold ============================
-    uint32_t tkey = 0x8000u;   // above every finite key: nothing selected
+    StepBuf<U> ba, bb;
+
+    // ============ outlier threshold, from the select kernel ===================
+    uint32_t tkey = 0x8000u;      // above every finite key: nothing selected
+    float tf = __builtin_inff();   // |x| threshold as fp32
     uint32_t take_w = 0, csr_w = 0;
     if (kk > 0) {
-        for (int i = tid; i < 1024; i += kThreads) s_hist[i] = 0u;
-        if (tid < 4 * 33) s_fine[tid] = 0u;
-        __syncthreads();
-        // pass 1: coarse histogram
-        for (int s0 = 0; s0 < steps; s0 += U) {
-            uint4 xr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = wr0 + (s0 + u) * RPS + rl;
-                xr[u] = (s0 + u < steps && row < rows)
-                            ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = wr0 + (s0 + u) * RPS + rl;
-                if (s0 + u < steps && row < rows) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) atomicAdd(&s_hist[(half_of(xr[u], e) & 0x7fffu) >> 5], 1u);
-                }
-            }
-        }
-        __syncthreads();
-        {   // the coarse bin holding the k-th largest key
-            const int b0 = (255 - tid) * 4;
-            const uint32_t h0 = s_hist[b0], h1 = s_hist[b0 + 1], h2 = s_hist[b0 + 2],
-                           h3 = s_hist[b0 + 3];
-            uint32_t tot;
-            uint32_t cum = block_excl_scan(h0 + h1 + h2 + h3, s_tmp, &tot);
-            const uint32_t hh[4] = {h3, h2, h1, h0};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (cum < kk && cum + hh[q] >= kk) s_sel[0] = (uint32_t)(b0 + 3 - q);
-                cum += hh[q];
-            }
-        }
-        __syncthreads();
-        const uint32_t bstar = s_sel[0];
-        // pass 2: per-wave fine histograms inside the coarse bin
-        uint32_t my_above = 0;
-        for (int s0 = 0; s0 < steps; s0 += U) {
-            uint4 xr[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = wr0 + (s0 + u) * RPS + rl;
-                xr[u] = (s0 + u < steps && row < rows)
-                            ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = wr0 + (s0 + u) * RPS + rl;
-                if (s0 + u < steps && row < rows) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t key = half_of(xr[u], e) & 0x7fffu;
-                        const uint32_t kb = key >> 5;
-                        if (kb == bstar) atomicAdd(&s_fine[wv * 33 + (key & 31u)], 1u);
-                        my_above += (kb > bstar) ? 1u : 0u;
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) my_above += __shfl_xor(my_above, off, 64);
-        if (lane == 0) s_fine[wv * 33 + 32] = my_above;
-        __syncthreads();
-        if (wv == 0) {
-            uint32_t F = 0, above = 0;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (lane < 32) F += s_fine[w * 33 + lane];
-                above += s_fine[w * 33 + 32];
-            }
-            const uint32_t needk = kk - above;   // >= 1 by the choice of the coarse bin
-            uint32_t suf = (lane < 32) ? F : 0u;  // lane f: sum of F[f'] for f' >= f
-#pragma unroll
-            for (int off = 1; off < 32; off <<= 1) {
-                const uint32_t y = __shfl_down(suf, off, 64);
-                if (lane + off < 32) suf += y;
-            }
-            const uint32_t strictly_above = suf - ((lane < 32) ? F : 0u);
-            const uint64_t bal = __ballot(lane < 32 && strictly_above < needk && suf >= needk);
-            const int fstar = bal ? (int)__builtin_ctzll(bal) : 0;
-            const uint32_t need = needk - __shfl(strictly_above, fstar, 64);   // ties to take
-            uint32_t eq = 0, gt = 0;
-            if (lane < 4) {
-                eq = s_fine[lane * 33 + fstar];
-                gt = s_fine[lane * 33 + 32];
-                for (int f = fstar + 1; f < 32; ++f) gt += s_fine[lane * 33 + f];
-            }
-            uint32_t tt;
-            const uint32_t ties_before = wave_excl_scan(eq, lane, &tt);
-            const uint32_t take = (need > ties_before) ? min(eq, need - ties_before) : 0u;
-            const uint32_t before = wave_excl_scan(gt + take, lane, &tt);
-            if (lane < 4) {
-                s_wave[lane * 2] = take;
-                s_wave[lane * 2 + 1] = before;
-            }
-            if (lane == 0) s_sel[1] = (bstar << 5) | (uint32_t)fstar;
-        }
-        __syncthreads();
-        tkey = s_sel[1];
-        take_w = s_wave[wv * 2];
-        csr_w = s_wave[wv * 2 + 1];
+        const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
+        tkey = sel[0];
+        tf = h2f(tkey);
+        take_w = sel[1 + wv];
+        csr_w = sel[5 + wv];
     }
 
     // ============ quantization pass, then the power-iteration passes =========
@@ -341,62 +627,44 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         double gacc = 0.0;
         uint32_t ties_seen = 0, csr = csr_w;
 
-        for (int s0 = 0; s0 < steps; s0 += U) {
-            uint4 xr[U];
-            uint32_t cw[U];
-            float scl[U], zpt[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int row = wr0 + (s0 + u) * RPS + rl;
-                const bool ok = s0 + u < steps && row < rows;
-                const size_t grow = (size_t)mm * rows + (ok ? row : 0);
-                xr[u] = ok ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
-                           : make_uint4(0u, 0u, 0u, 0u);
-                cw[u] = 0u;
-                scl[u] = 0.0f;
-                zpt[u] = 0.0f;
-                if (!first && ok) {
-                    cw[u] = bits == 4 ? reinterpret_cast<const uint32_t*>(o.codes)[grow * (D / 8) + colq]
-                                      : reinterpret_cast<const uint16_t*>(o.codes)[grow * (D / 8) + colq];
-                    scl[u] = o.scale[grow * ngr + colq / gl];
-                    zpt[u] = o.zero[grow * ngr + colq / gl];
-                }
-            }
+        auto step_block = [&](const StepBuf<U>& b, int s0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int s = s0 + u;
                 if (s >= steps) break;   // wave-uniform
                 const int row = wr0 + s * RPS + rl;
-                const bool valid = row < rows;
+                const bool valid = row < rows;   // rows past the end hold zeros
                 const size_t grow = (size_t)mm * rows + (valid ? row : 0);
-                // ---- outlier mask: key > threshold, or a tie within the quota
-                uint32_t om = 0u, eqm = 0u;
-                if (valid) {
+                // ---- outliers: |x| > T, or |x| == T within the wave's tie quota
+                // (|x| compared in fp32: fp16 -> fp32 is exact and monotone)
+                float xf[8];
+                bool gt[8];
+                bool any_eq = false;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const uint32_t key = half_of(xr[u], e) & 0x7fffu;
-                        om |= (key > tkey) ? (1u << e) : 0u;
-                        eqm |= (key == tkey) ? (1u << e) : 0u;
-                    }
+                for (int e = 0; e < 8; ++e) {
+                    xf[e] = h2f(half_of(b.x[u], e));
+                    gt[e] = fabsf(xf[e]) > tf;
+                    any_eq |= fabsf(xf[e]) == tf;
                 }
-                if (__ballot(eqm != 0u) != 0ull && ties_seen < take_w) {
-                    uint32_t tot;
-                    const uint32_t c = __builtin_popcount(eqm);
-                    uint32_t rank0 = ties_seen + wave_excl_scan(c, lane, &tot);
-                    if (ties_seen + tot <= take_w) {
-                        om |= eqm;
-                    } else {
+                if (__ballot(any_eq) != 0ull && ties_seen < take_w) {   // rare
+                    uint32_t eqm = 0u;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if ((eqm >> e) & 1u) {
-                                if (rank0 < take_w) om |= 1u << e;
-                                ++rank0;
-                            }
-                    }
+                    for (int e = 0; e < 8; ++e) eqm |= (fabsf(xf[e]) == tf) ? (1u << e) : 0u;
+                    uint32_t tot;
+                    uint32_t rank0 = ties_seen + wave_excl_scan(__builtin_popcount(eqm), lane, &tot);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if ((eqm >> e) & 1u) {
+                            gt[e] = gt[e] || rank0 < take_w;
+                            ++rank0;
+                        }
                     ties_seen += tot;
                 }
                 // ---- CSR (first pass only)
                 if (first && kk > 0) {
+                    uint32_t om = 0u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) om |= gt[e] ? (1u << e) : 0u;
                     uint32_t pre = 0, tot = 0;
                     if (__ballot(om != 0u) != 0ull) pre = wave_excl_scan(__builtin_popcount(om), lane, &tot);
                     if (valid && colq == 0) rp[row] = (int32_t)(csr + pre);
@@ -406,7 +674,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                         for (int e = 0; e < 8; ++e)
                             if (((om >> e) & 1u) && pos < kk) {
                                 cm[pos] = (uint16_t)(colq * 8 + e);
-                                vm[pos] = (uint16_t)half_of(xr[u], e);
+                                vm[pos] = (uint16_t)half_of(b.x[u], e);
                                 ++pos;
                             }
                     }
@@ -417,28 +685,36 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                 // ---- D = X - S; quantize (first pass) or reload codes; R
                 float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = ((om >> e) & 1u) ? 0.0f : h2f(half_of(xr[u], e));
+                for (int e = 0; e < 8; ++e) v[e] = gt[e] ? 0.0f : xf[e];
                 float R[8];
                 if (first) {
-                    float mn = v[0], mx = v[0];
-#pragma unroll
-                    for (int e = 1; e < 8; ++e) {
-                        mn = fminf(mn, v[e]);
-                        mx = fmaxf(mx, v[e]);
-                    }
-                    for (int off = 1; off < gl; off <<= 1) {
-                        mn = fminf(mn, __shfl_xor(mn, off, 64));
-                        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-                    }
+                    float mn = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])),
+                                     fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
+                    float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                                     fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+                    group_minmax(mn, mx, gl);
                     const float sc = (mx - mn) / qmax;
+                    const float inv = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
+                    float t[8], cf[8];
+                    bool near_tie = false;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        t[e] = v[e] - mn;
+                        const float q = t[e] * inv;
+                        cf[e] = rintf(q);
+                        near_tie |= fabsf(q - cf[e]) > 0.49999f;
+                    }
+                    if (__ballot(near_tie) != 0ull && near_tie) {
+                        // within 1e-5 of a half-integer: round the exact quotient
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) cf[e] = rintf(t[e] / sc);
+                    }
                     uint32_t word = 0;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float t = v[e] - mn;
-                        uint32_t c = 0;
-                        if (sc != 0.0f) c = (uint32_t)fminf(fmaxf(rintf(t / sc), 0.0f), qmax);
-                        word |= c << (e * bits);
-                        R[e] = valid ? fmaf(-(float)c, sc, t) : 0.0f;
+                        cf[e] = __builtin_amdgcn_fmed3f(cf[e], 0.0f, qmax);
+                        word |= (uint32_t)cf[e] << (e * bits);
+                        R[e] = fmaf(-cf[e], sc, t[e]);
                     }
                     if (valid) {
                         if (bits == 4)
@@ -453,9 +729,8 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                 } else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float t = v[e] - zpt[u];
-                        const float c = (float)((cw[u] >> (e * bits)) & cmask);
-                        R[e] = valid ? fmaf(-c, scl[u], t) : 0.0f;
+                        const float c = (float)((b.cw[u] >> (e * bits)) & cmask);
+                        R[e] = fmaf(-c, b.sc[u], v[e] - b.zp[u]);
                     }
                 }
                 if (!lowrank) continue;
@@ -466,12 +741,8 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                     float acc = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) acc = fmaf(R[e], Bm[e][c], acc);
-                    p[c] = acc;
+                    p[c] = row_allreduce<LPR>(acc);
                 }
-#pragma unroll
-                for (int off = 1; off < LPR; off <<= 1)
-#pragma unroll
-                    for (int c = 0; c < RKX; ++c) p[c] += __shfl_xor(p[c], off, 64);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
 #pragma unroll
@@ -505,6 +776,13 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                     __builtin_amdgcn_wave_barrier();
                 }
             }
+        };
+        load_steps<D, U, RPS>(ba, xm, o, mm, rows, wr0, 0, steps, rl, colq, !first);
+        for (int s0 = 0; s0 < steps; s0 += 2 * U) {
+            load_steps<D, U, RPS>(bb, xm, o, mm, rows, wr0, s0 + U, steps, rl, colq, !first);
+            step_block(ba, s0);
+            load_steps<D, U, RPS>(ba, xm, o, mm, rows, wr0, s0 + 2 * U, steps, rl, colq, !first);
+            step_block(bb, s0 + U);
         }
         if (first && tid == 0) rp[rows] = (int32_t)kk;
         if (!lowrank) break;
@@ -588,7 +866,12 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
 
 template <int D, int RK>
 hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
-    constexpr int U = RK >= 8 ? 4 : 8;
+    if (a.out.k > 0) {
+        hipLaunchKernelGGL((select_kernel<D, 4>), dim3((unsigned)a.out.M), dim3(kSelThreads), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int U = RK >= 8 ? 1 : 4;
     hipLaunchKernelGGL((compress_kernel<D, RK, U>), dim3((unsigned)a.out.M), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }

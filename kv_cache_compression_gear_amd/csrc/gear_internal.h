@@ -39,7 +39,9 @@ struct CompressArgs {
     int32_t iters;
     uint64_t seed;
     uint32_t* err;         // device failure word (cleared by the launch)
+    uint32_t* sel;         // [M][kSelStride] outlier threshold and per-block quotas
 };
+constexpr int kSelStride = 16;
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
 // ---- decompress -----------------------------------------------------------
