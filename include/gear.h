@@ -21,8 +21,9 @@
  *   - Pointers named *_f16 / *_f32 / packed / workspace / arena are DEVICE
  *     pointers, 256-byte aligned (torch allocations are).  `stream` is a
  *     hipStream_t (NULL = the default stream).  Every call is asynchronous on
- *     `stream`: none allocates, frees or synchronises device memory, except
- *     gear_workspace_error(), which says so.
+ *     `stream`: none allocates, frees or synchronises device memory (the
+ *     opt-in kernel timing below records HIP events, and reading it waits
+ *     for them).
  *   - The caller owns all device memory.  The library owns only the host-side
  *     gear_cache object.
  *   - Every check (null or misaligned pointers, shapes, parameters, workspace
@@ -54,8 +55,7 @@ typedef enum {
     GEAR_ERR_UNSUPPORTED = 2,  /* valid GEAR setting outside this library's limits */
     GEAR_ERR_CAPACITY = 3,     /* cache arena or token capacity exhausted */
     GEAR_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
-    GEAR_ERR_WORKSPACE = 5,    /* workspace too small */
-    GEAR_ERR_DEVICE = 6        /* a kernel reported a failure (gear_workspace_error) */
+    GEAR_ERR_WORKSPACE = 5     /* workspace too small */
 } gear_status;
 
 /* GEAR settings.  Outlier share s = outlier_ppm / 1e6; k = floor(n*d*s). */
@@ -119,19 +119,14 @@ size_t gear_compress_workspace_bytes(const gear_params* p, const gear_shape* s);
  * Compress: x_f16 (the stack described by s) -> packed (gear_packed_bytes).
  * Runs the outlier filter, group quantization and the low-rank fit of every
  * matrix.  workspace: >= gear_compress_workspace_bytes, contents need not be
- * initialised; it must not be shared by calls that may run concurrently.
+ * initialised (it carries per-matrix results between the call's kernels: 64
+ * bytes of outlier-selection results and head_dim x 8 floats of the low-rank
+ * fit per compressed matrix); it must not be shared by calls that may run
+ * concurrently.
  */
 gear_status gear_compress(const gear_params* p, const gear_shape* s, const void* x_f16,
                           void* packed, void* workspace, size_t workspace_bytes,
                           void* stream);
-
-/*
- * Reads the device-side failure word a gear_compress (or a cache call that
- * compresses) left in `workspace`, after synchronising `stream`.  GEAR_OK if
- * none; GEAR_ERR_DEVICE if a cross-workgroup wait inside the kernel timed
- * out (its outputs are then not valid).  This call blocks.
- */
-gear_status gear_workspace_error(const void* workspace, void* stream);
 
 /*
  * Decompress: packed -> out_f16 (the stack described by s), each entry
@@ -212,6 +207,19 @@ gear_status gear_decode_attn(const gear_cache* cache, const void* q_f16, int32_t
 gear_status gear_cache_get_info(const gear_cache* cache, gear_cache_info* out);
 
 /* Status name, and the detail of this thread's last non-OK status. */
+/*
+ * Kernel timing with HIP events, for profiling; off by default.  While it is
+ * on, every kernel launch of the library is bracketed by two events recorded
+ * on the launch stream.  gear_timing_enable(1) starts a new measurement (0
+ * stops it and drops what was recorded).  gear_timing_read() waits for the
+ * recorded events and returns, for the kernel named `kernel` -- one of
+ * "select", "compress", "lowrank_a", "decompress", "attn_split",
+ * "attn_combine", "buffer_append" -- the launches and their summed duration
+ * in milliseconds since the measurement started.  It blocks; host-thread-safe.
+ */
+gear_status gear_timing_enable(int on);
+gear_status gear_timing_read(const char* kernel, int64_t* launches, double* total_ms);
+
 const char* gear_status_str(gear_status s);
 const char* gear_last_error(void);
 

@@ -23,8 +23,7 @@ LIB_PATH = os.path.join(_HERE, "libgear.so")
 
 GEAR_OK = 0
 _STATUS = {0: "GEAR_OK", 1: "GEAR_ERR_INVALID_ARG", 2: "GEAR_ERR_UNSUPPORTED",
-           3: "GEAR_ERR_CAPACITY", 4: "GEAR_ERR_HIP", 5: "GEAR_ERR_WORKSPACE",
-           6: "GEAR_ERR_DEVICE"}
+           3: "GEAR_ERR_CAPACITY", 4: "GEAR_ERR_HIP", 5: "GEAR_ERR_WORKSPACE"}
 
 
 class GearError(RuntimeError):
@@ -70,10 +69,15 @@ class _CacheInfo(ctypes.Structure):
 
 # Every symbol include/gear.h declares (checked by the tests).
 EXPORTS = ["gear_packed_layout", "gear_packed_bytes", "gear_compress_workspace_bytes",
-           "gear_compress", "gear_workspace_error", "gear_decompress",
+           "gear_compress", "gear_decompress",
            "gear_cache_arena_bytes", "gear_cache_workspace_bytes", "gear_cache_create",
            "gear_cache_destroy", "gear_cache_load_prompt", "gear_append_tokens",
-           "gear_decode_attn", "gear_cache_get_info", "gear_status_str", "gear_last_error"]
+           "gear_decode_attn", "gear_cache_get_info", "gear_timing_enable", "gear_timing_read",
+           "gear_status_str", "gear_last_error"]
+
+# Kernel names accepted by gear_timing_read.
+KERNELS = ["select", "compress", "lowrank_a", "decompress", "attn_split", "attn_combine",
+           "buffer_append"]
 
 _lib = None
 
@@ -97,8 +101,6 @@ def lib():
         L.gear_compress_workspace_bytes.argtypes = [pp, ps]
         L.gear_compress.restype = S
         L.gear_compress.argtypes = [pp, ps, P, P, P, sz, P]
-        L.gear_workspace_error.restype = S
-        L.gear_workspace_error.argtypes = [P, P]
         L.gear_decompress.restype = S
         L.gear_decompress.argtypes = [pp, ps, P, P, P]
         L.gear_cache_arena_bytes.restype = sz
@@ -117,6 +119,11 @@ def lib():
         L.gear_decode_attn.argtypes = [P, P, i32, ctypes.c_float, P, P, sz, P]
         L.gear_cache_get_info.restype = S
         L.gear_cache_get_info.argtypes = [P, ctypes.POINTER(_CacheInfo)]
+        L.gear_timing_enable.restype = S
+        L.gear_timing_enable.argtypes = [S]
+        L.gear_timing_read.restype = S
+        L.gear_timing_read.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_double)]
         L.gear_status_str.restype = ctypes.c_char_p
         L.gear_status_str.argtypes = [S]
         L.gear_last_error.restype = ctypes.c_char_p
@@ -257,9 +264,20 @@ def compress(x: torch.Tensor, p: Params, out: Packed | None = None,
     return out
 
 
-def workspace_error(workspace: torch.Tensor):
-    """Raises GearError if a compress that used `workspace` reported a device failure."""
-    _check(lib().gear_workspace_error(_ptr(workspace), _stream()))
+def timing_enable(on: bool = True):
+    """Start (or stop and drop) per-kernel HIP-event timing inside the library."""
+    _check(lib().gear_timing_enable(1 if on else 0))
+
+
+def timing_read() -> dict:
+    """{kernel: (launches, total_ms)} since timing_enable(True); waits for the events."""
+    out = {}
+    for name in KERNELS:
+        n, ms = ctypes.c_int64(), ctypes.c_double()
+        _check(lib().gear_timing_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)))
+        if n.value:
+            out[name] = (n.value, ms.value)
+    return out
 
 
 def decompress(packed: Packed, out: torch.Tensor | None = None) -> torch.Tensor:

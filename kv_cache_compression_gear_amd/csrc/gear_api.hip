@@ -5,8 +5,11 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "gear_internal.h"
 
@@ -114,14 +117,12 @@ Packed make_packed(const gear_params* p, const gear_layout& L, int d, void* base
     return k;
 }
 
-constexpr size_t kWsHeader = 256;          // device failure word
-
 struct CompressPlan {
     size_t ws_bytes;
 };
 
-CompressPlan plan_compress(const gear_params*, const gear_layout& L, int) {
-    return CompressPlan{kWsHeader + align_up((size_t)L.num_compressed * kSelStride * 4)};
+CompressPlan plan_compress(const gear_params* p, const gear_layout& L, int d) {
+    return CompressPlan{compress_workspace(L.num_compressed, d, p->rank)};
 }
 
 // Compress matrices [0, m_split) from x and [m_split, M) from x2.
@@ -140,14 +141,74 @@ gear_status run_compress(const gear_params* p, const gear_layout& L, int d, cons
     a.out = make_packed(p, L, d, packed);
     a.iters = p->power_iters;
     a.seed = p->seed;
-    a.err = static_cast<uint32_t*>(ws);
-    a.sel = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + kWsHeader);
+    a.sel = static_cast<uint32_t*>(ws);
+    a.bf = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
+                                    align_up((size_t)L.num_compressed * kSelStride * 4));
     hipError_t e = launch_compress(a, st);
     if (e != hipSuccess) return hip_fail(e, "compress launch");
     return GEAR_OK;
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Kernel timing
+
+namespace {
+
+const char* const kKernelNames[kKernelCount] = {
+    "select", "compress", "lowrank_a", "decompress", "attn_split", "attn_combine", "buffer_append"};
+
+struct TimingRec {
+    KernelId k;
+    hipEvent_t start, stop;
+};
+
+std::atomic<bool> g_timing{false};
+std::mutex g_timing_mu;
+std::vector<TimingRec> g_pending;
+int64_t g_launches[kKernelCount];
+double g_total_ms[kKernelCount];
+
+void timing_drop_locked() {
+    for (const TimingRec& r : g_pending) {
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_pending.clear();
+    for (int i = 0; i < kKernelCount; ++i) {
+        g_launches[i] = 0;
+        g_total_ms[i] = 0.0;
+    }
+}
+
+}  // namespace
+
+namespace gear {
+
+bool timing_on() { return g_timing.load(std::memory_order_relaxed); }
+
+hipEvent_t timing_begin(hipStream_t st) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    if (hipEventRecord(e, st) != hipSuccess) {
+        hipEventDestroy(e);
+        return nullptr;
+    }
+    return e;
+}
+
+void timing_end(KernelId k, hipEvent_t start, hipStream_t st) {
+    hipEvent_t e = timing_begin(st);
+    if (!e) {
+        hipEventDestroy(start);
+        return;
+    }
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_pending.push_back(TimingRec{k, start, e});
+}
+
+}  // namespace gear
 
 // ---------------------------------------------------------------------------
 
@@ -208,12 +269,41 @@ const char* gear_status_str(gear_status s) {
         case GEAR_ERR_CAPACITY: return "GEAR_ERR_CAPACITY";
         case GEAR_ERR_HIP: return "GEAR_ERR_HIP";
         case GEAR_ERR_WORKSPACE: return "GEAR_ERR_WORKSPACE";
-        case GEAR_ERR_DEVICE: return "GEAR_ERR_DEVICE";
     }
     return "GEAR_ERR_UNKNOWN";
 }
 
 const char* gear_last_error(void) { return g_last_error.c_str(); }
+
+gear_status gear_timing_enable(int on) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    timing_drop_locked();
+    g_timing.store(on != 0, std::memory_order_relaxed);
+    return GEAR_OK;
+}
+
+gear_status gear_timing_read(const char* kernel, int64_t* launches, double* total_ms) {
+    if (!kernel || !launches || !total_ms) return fail(GEAR_ERR_INVALID_ARG, "NULL argument");
+    int id = -1;
+    for (int i = 0; i < kKernelCount; ++i)
+        if (std::string(kernel) == kKernelNames[i]) id = i;
+    if (id < 0) return fail(GEAR_ERR_INVALID_ARG, "unknown kernel name '%s'", kernel);
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    for (const TimingRec& r : g_pending) {
+        hipError_t e = hipEventSynchronize(r.stop);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.start, r.stop);
+        if (e != hipSuccess) return hip_fail(e, "kernel timing event");
+        g_launches[r.k] += 1;
+        g_total_ms[r.k] += ms;
+        hipEventDestroy(r.start);
+        hipEventDestroy(r.stop);
+    }
+    g_pending.clear();
+    *launches = g_launches[id];
+    *total_ms = g_total_ms[id];
+    return GEAR_OK;
+}
 
 gear_status gear_packed_layout(const gear_params* p, const gear_shape* s, gear_layout* out) {
     if (!out) return fail(GEAR_ERR_INVALID_ARG, "out is NULL");
@@ -246,17 +336,6 @@ gear_status gear_compress(const gear_params* p, const gear_shape* s, const void*
     const int64_t half = s->num_mats * (s->n_tokens / L.rows);
     return run_compress(p, L, s->head_dim, x_f16, x_f16, half, packed, workspace, workspace_bytes,
                         static_cast<hipStream_t>(stream));
-}
-
-gear_status gear_workspace_error(const void* workspace, void* stream) {
-    if (!workspace) return fail(GEAR_ERR_INVALID_ARG, "workspace is NULL");
-    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    uint32_t word = 0;
-    e = hipMemcpy(&word, workspace, sizeof word, hipMemcpyDeviceToHost);
-    if (e != hipSuccess) return hip_fail(e, "hipMemcpy");
-    if (word != 0) return fail(GEAR_ERR_DEVICE, "a cross-workgroup wait timed out (word %u)", word);
-    return GEAR_OK;
 }
 
 gear_status gear_decompress(const gear_params* p, const gear_shape* s, const void* packed,
@@ -454,7 +533,7 @@ gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_h
     a.buf = reinterpret_cast<const uint16_t*>(g->arena + g->off_buf);
     a.buf_cap = c.buf_tokens;
     a.buf_len = g->buf_len;
-    a.partial = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + kAttnPartialOffset);
+    a.partial = static_cast<float*>(workspace);
     hipError_t e = launch_decode_attn(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode attention launch");
     return GEAR_OK;

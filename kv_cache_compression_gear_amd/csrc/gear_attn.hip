@@ -428,11 +428,19 @@ __global__ void attn_combine_kernel(AttnArgs a) {
 template <int D, int G>
 hipError_t launch_dg(const AttnArgs& a, hipStream_t st) {
     const unsigned grid = (unsigned)(a.B * a.Hkv * a.splits);
-    hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(grid), dim3(kThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    {
+        Timed t(kKAttnSplit, st);
+        hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(grid), dim3(kThreads), 0, st, a);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a);
-    return hipGetLastError();
+    {
+        Timed t(kKAttnCombine, st);
+        hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <int D>
@@ -478,7 +486,7 @@ size_t attn_workspace_bytes(int B, int Hkv, int Hq, int d, int64_t tokens, int* 
     if (splits) *splits = (int)s;
     if (tokens_per_split) *tokens_per_split = kTPS;
     const int G = Hkv > 0 ? Hq / Hkv : 1;
-    return kAttnPartialOffset + align_up((size_t)B * Hkv * s * G * (d + 2) * sizeof(float));
+    return align_up((size_t)B * Hkv * s * G * (d + 2) * sizeof(float));
 }
 
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t st) {
@@ -495,6 +503,7 @@ hipError_t launch_buffer_append(const uint16_t* k_new, const uint16_t* v_new, ui
     if (total == 0) return hipSuccess;
     size_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 4096) blocks = 4096;
+    Timed t(kKBufferAppend, st);
     hipLaunchKernelGGL(buffer_append_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, k_new,
                        v_new, buf, B, H, d, cap, pos, n_new, src_tokens, src_off);
     return hipGetLastError();

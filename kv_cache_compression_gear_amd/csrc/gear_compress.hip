@@ -9,34 +9,26 @@
 //       (zero-point = group min, scale = (max-min)/(2^b-1), round half even);
 //   A, B = t PowerSGD steps on R = D - deq(Q) from a fixed B0, L = A B^T.
 //
-// Design (MI355X):
-//   * One workgroup (4 waves) owns one matrix and streams its rows in passes;
-//     each wave owns a contiguous quarter of the rows, 8 columns per lane and
-//     D/8 lanes per token row.  Nothing is exchanged between workgroups, so
-//     no grid-level synchronisation or device-scope fence is needed, and
-//     thousands of entries are processed between the few workgroup barriers.
-//   * Pass 1: 4096-bin histogram of |x| >> 3 in LDS -> the coarse bin of the
-//     k-th largest magnitude.  Pass 2: per-wave 8-bin histograms inside that
-//     bin -> the exact threshold key, the number of ties to take, and every
-//     wave's CSR start and tie quota (flat order = wave order, then row, lane).
-//   * Pass 3: outlier mask, CSR emit (wave-level prefix sums), bit-exact fp32
-//     group quantization (rint of the correctly rounded quotient, taken from a
-//     reciprocal product away from rounding ties) with codes packed
-//     in registers and stored as one 32- or 16-bit word per lane per token,
-//     and the first power-iteration product.  Passes 4..: the remaining power
-//     steps, with R = D - deq(Q) recomputed from X and the stored codes.
-//   * A power step is one pass: P = R B and W = R^T P together, G = P^T P in
-//     fp64 from a small per-wave LDS ring of P rows; then G = C^T C (Cholesky,
-//     one thread), M = C^-1, B' = W M, and after the last step A = P M.  In
-//     exact arithmetic this equals modified Gram-Schmidt on P, B = R^T A.
-//   * The products are bandwidth-shaped (r <= 8 columns): plain fp32 VALU
-//     FMAs; a token's dot product is finished with a butterfly over its lanes.
+// Design (MI355X): three launches per call.
+//   * select_kernel (16 waves per matrix): the threshold key T of the k-th
+//     largest |x|, each row block's share of the ties at T and its first CSR
+//     position.  A 1/16 row sample places a 4096-key window that one exact
+//     counting pass resolves; a two-pass radix select is the fallback.
+//   * compress_kernel (4 waves per matrix, one pass over X): outlier mask, CSR
+//     emit (DPP prefix sums), bit-exact fp32 group quantization (rint of the
+//     correctly rounded quotient, taken from a reciprocal product away from
+//     rounding ties), codes packed in registers, and C = R^T R on the matrix
+//     cores from an fp16 hi/lo split of the scaled residual; then the t power
+//     steps on C in fp64 and the output B.
+//   * lowrank_a_kernel (many workgroups per matrix): A = R (B_prev M), the
+//     one product that needs R itself after the power steps.
+//   The power steps are those of PowerSGD, with P = R B, A = orth(P),
+//   B = R^T A; orth is a Cholesky factorisation of P^T P = B^T C B, which in
+//   exact arithmetic is modified Gram-Schmidt on P, so L = A B^T is the same.
 #include "gear_internal.h"
 
 namespace gear {
 namespace {
-
-constexpr int kRing = 64;   // P rows buffered per wave before the fp64 Gram update
 
 __device__ __forceinline__ float h2f(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
@@ -74,29 +66,6 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx, int g) {
     if (g >= 16) { mn = fminf(mn, dpp<0x140>(mn)); mx = fmaxf(mx, dpp<0x140>(mx)); }
 }
 
-// Exclusive prefix sum over the 256 threads of the block; *total = full sum.
-__device__ uint32_t block_excl_scan(uint32_t v, uint32_t* s_tmp, uint32_t* total) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        uint32_t y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    __syncthreads();
-    if (lane == 63) s_tmp[w] = x;
-    __syncthreads();
-    uint32_t base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint32_t t = s_tmp[i];
-        base += (i < w) ? t : 0u;
-        tot += t;
-    }
-    *total = tot;
-    return base + x - v;
-}
-
 // Exclusive prefix sum over the 64 lanes of the wave (lane order).
 __device__ __forceinline__ uint32_t wave_excl_scan(uint32_t v, int lane, uint32_t* total) {
     uint32_t x = v;
@@ -126,7 +95,7 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
 // zero, so later columns do not project on it (the modified Gram-Schmidt zero
 // rule with threshold 1e-6 on norms).  fp64, fully unrolled, one thread.
 template <int RK>
-__device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, float* Mout /* LDS */) {
+__device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, double* Mout /* LDS */) {
     double c[RK][RK];
     bool alive[RK];
 #pragma unroll
@@ -167,21 +136,14 @@ __device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, float* Mou
 #pragma unroll
     for (int a = 0; a < RK; ++a)
 #pragma unroll
-        for (int j = 0; j < RK; ++j) Mout[a * RK + j] = a <= j ? (float)c[a][j] : 0.0f;
+        for (int j = 0; j < RK; ++j) Mout[a * RK + j] = a <= j ? c[a][j] : 0.0;
 }
-
-template <int RK>
-struct PairLanes {
-    static constexpr int NP = RK * (RK + 1) / 2;
-    // lanes per Gram pair: the largest power of two with NP * LP <= 64
-    static constexpr int LP = NP <= 1 ? 64 : NP <= 2 ? 32 : NP <= 4 ? 16 : NP <= 8 ? 8
-                            : NP <= 16 ? 4 : NP <= 32 ? 2 : 1;
-};
 
 constexpr int kCoarse = 4096;   // pass-1 bins: |x| bit pattern >> 3
 constexpr int kFine = 8;        // pass-2 bins inside the chosen coarse bin
 constexpr int kFineSlot = kFine + 1;
 constexpr int kSelThreads = 1024;
+constexpr int kSelBound = 13;   // selection word holding the magnitude bound
 
 // U consecutive row steps of one wave: the X words, and (after the first
 // pass) the stored code word and the group's scale and zero of each row.
@@ -219,10 +181,13 @@ __device__ __forceinline__ void load_steps(StepBuf<U>& b, const uint16_t* xm, co
 // ---------------------------------------------------------------------------
 // Outlier threshold: the k-th largest |x| of a matrix, with ties broken by
 // the lower flat index.  One 16-wave workgroup per matrix.  The rows are split
-// exactly as the compress kernel splits them over its 4 waves; each of those
-// row blocks is read here by 4 consecutive waves.  Output per matrix
-// (kSelStride words): threshold key, then for each of the 4 row blocks the
-// number of ties at the threshold it takes, then its first CSR position.
+// exactly as the compress kernel splits them over its 4 waves (wave_rows);
+// each of those row blocks is read here by 4 consecutive waves.  Output per
+// matrix (kSelStride words): [0] threshold key T (|x| bits); [1..4] per row
+// block, the number of entries with key T it takes; [5..8] its first CSR
+// position; [9..12] the number of entries with key T it holds; [13] a key
+// bounding |x| over the entries that are not outliers (T, or the largest key
+// when k = 0, which only the low-rank fit needs).
 //
 // Common path (one pass over X plus a 1/16 sample): a histogram of a sample
 // of rows gives a key L0 that at least ~1.25 k entries reach; one pass then
@@ -250,11 +215,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     const int rows = o.rows;
     const uint32_t kk = (uint32_t)o.k;
     uint32_t* sel = a.sel + (size_t)mm * kSelStride;
-    if (kk == 0) {
-        if (tid < kSelStride) sel[tid] = tid == 0 ? 0x8000u : 0u;
-        return;
-    }
-    const int rw = ((rows + 3) / 4 + RPS - 1) / RPS * RPS;
+    const int rw = wave_rows(rows);
     const int steps = rw / RPS;
     const int mb = wv / 4, sub = wv % 4;
     const int per = (steps + 3) / 4;
@@ -262,6 +223,30 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     const int wr0 = mb * rw;
     const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
                                          : a.x2 + (size_t)(mm - a.m_split) * rows * D;
+    if (kk == 0) {
+        // no outliers: only the largest key, which bounds |R| for the low-rank fit
+        uint32_t mx = 0;
+        for (int s = sb; s < se; ++s) {
+            const int row = wr0 + s * RPS + rl;
+            if (row >= rows) break;
+            const uint4 xr = *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8);
+            const uint32_t w4[4] = {xr.x, xr.y, xr.z, xr.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                mx = max(mx, max(w4[q] & 0x7fffu, (w4[q] >> 16) & 0x7fffu));
+        }
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+        if (lane == 0) s_tmp[wv] = mx;
+        __syncthreads();
+        if (tid < kSelStride) {
+            uint32_t v = tid == 0 ? 0x8000u : 0u;
+            if (tid == kSelBound)
+                for (int w = 0; w < NW; ++w) v = max(v, s_tmp[w]);
+            sel[tid] = v;
+        }
+        return;
+    }
     for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
     for (int i = tid; i < 4 * kWin; i += kSelThreads) s_win[i] = 0u;
     if (tid < NW * kFineSlot) s_fine[tid] = 0u;
@@ -422,10 +407,14 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
             const uint32_t ties_before = wave_excl_scan(eq, lane, &tt);
             const uint32_t take = (need > ties_before) ? min(eq, need - ties_before) : 0u;
             const uint32_t before = wave_excl_scan(gt + take, lane, &tt);
-            if (lane == 0) sel[0] = L0 + jstar;
+            if (lane == 0) {
+                sel[0] = L0 + jstar;
+                sel[kSelBound] = L0 + jstar;
+            }
             if (lane < 4) {
                 sel[1 + lane] = take;
                 sel[5 + lane] = before;
+                sel[9 + lane] = eq;
             }
         }
         return;
@@ -531,30 +520,182 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         const uint32_t ties_before = wave_excl_scan(eq, lane, &tt);
         const uint32_t take = (need > ties_before) ? min(eq, need - ties_before) : 0u;
         const uint32_t before = wave_excl_scan(gt + take, lane, &tt);
-        if (lane == 0) sel[0] = (bstar << 3) | (uint32_t)fstar;
+        if (lane == 0) {
+            sel[0] = (bstar << 3) | (uint32_t)fstar;
+            sel[kSelBound] = (bstar << 3) | (uint32_t)fstar;
+        }
         if (lane < 4) {
             sel[1 + lane] = take;
             sel[5 + lane] = before;
+            sel[9 + lane] = eq;
         }
     }
 }
 
-template <int D, int RK, int U>
+// ---------------------------------------------------------------------------
+// Compress: one workgroup (4 waves) per matrix, one pass over its rows.
+//
+// Wave w owns rows [w * wave_rows(n), (w + 1) * wave_rows(n)); a lane holds 8
+// consecutive columns of a token row, D/8 lanes per row.  The rows are taken
+// in slabs of 16 rows per wave (64 per workgroup).  For each row the wave
+// applies the outlier mask, emits the row's CSR entries, quantizes the groups
+// and forms the residual R = D - deq(Q).  With a low-rank term, R (scaled by
+// 2^ex so that fp16 covers it) is split into fp16 hi + lo parts and written
+// row-major into an LDS slab; after a workgroup barrier every wave adds its
+// share of the 32x32 blocks of C = R^T R over the slab with
+// v_mfma_f32_32x32x16_f16 (hi*hi + hi*lo + lo*hi; the products are exact in
+// fp32, lo*lo is below 2^-22 of the total).  The operands are read with
+// ds_read_b64_tr_b16, which turns the row-major slab into the MFMA's
+// "8 consecutive k per lane" layout; chunks of 8 bytes are XOR-swizzled by row
+// so that the transposing reads hit distinct LDS banks.
+//
+// After the pass C is in LDS and the t power steps of the PowerSGD-style fit
+// run on it in fp64: W = C B (= R^T P with P = R B), G = B^T W (= P^T P),
+// Cholesky G = C_g^T C_g with the dead-column rule, M = C_g^-1, B' = W M.
+// The last step's B' is the output B; A = P M = R (B_prev M) needs R once more
+// and is formed by lowrank_a_kernel from the d x r matrix B_prev M left in the
+// workspace.
+// ---------------------------------------------------------------------------
+
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef short s4v __attribute__((ext_vector_type(4)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) s4v lds_s4v;
+
+constexpr int kSlabRows = 64;     // 16 rows from each of the 4 waves
+
+// 8-byte chunk c8 of slab row `row`, XOR-swizzled: the 4 rows a half-wave
+// reads in one transposing load land in 4 disjoint groups of 16 banks.
+template <int D>
+__device__ __forceinline__ int swz_chunk(int row, int c8) {
+    return D == 128 ? (c8 ^ ((row & 3) << 3)) : (c8 ^ (((row >> 1) & 1) << 3));
+}
+
+// MFMA operand for columns [cb, cb + 32) over slab rows [kb, kb + 16): lane l
+// receives R[kb + 8 (l / 32) + i][cb + l % 32], i = 0..7.  Each transposing
+// load serves 4 rows: within a group of 16 lanes, lane p supplies the address
+// of 4 consecutive columns of row p / 4 and receives column p of the 4 rows.
+template <int D>
+__device__ __forceinline__ h8v read_operand(const unsigned char* plane, int kb, int cb, int lane) {
+    const int g = lane >> 4, p = lane & 15;
+    const int c8 = (cb + 16 * (g & 1) + 4 * (p & 3)) >> 2;
+    const int r0 = kb + 8 * (g >> 1) + (p >> 2);
+    const int r1 = r0 + 4;
+    const s4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4v*)(plane + r0 * (D * 2) + swz_chunk<D>(r0, c8) * 8));
+    const s4v v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s4v*)(plane + r1 * (D * 2) + swz_chunk<D>(r1, c8) * 8));
+    return __builtin_shufflevector(__builtin_bit_cast(h4v, v0), __builtin_bit_cast(h4v, v1),
+                                   0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f16v mma3(const h8v& hi_i, const h8v& lo_i, const h8v& hi_j,
+                                     const h8v& lo_j, f16v acc) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi_i, hi_j, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi_i, lo_j, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo_i, hi_j, acc, 0, 0, 0);
+    return acc;
+}
+
+// This wave's 32x32 blocks (I, J), I <= J, of C = R^T R, in column units of 32.
+// D = 128: waves 0, 1 take (a,a) (a,a+1) (a+1,a+1) for a = 0, 2; waves 2, 3
+// take (c,2) (c,3) for c = 0, 1.  D = 64: waves 0..2 take (0,0) (0,1) (1,1).
+template <int D>
+__device__ __forceinline__ void block_of(int wv, int b, int& I, int& J) {
+    if (D == 128) {
+        if (wv < 2) {
+            I = 2 * wv + (b == 2 ? 1 : 0);
+            J = 2 * wv + (b == 0 ? 0 : 1);
+        } else {
+            I = wv - 2;
+            J = 2 + b;
+        }
+    } else {
+        I = wv == 2 ? 1 : 0;
+        J = wv == 0 ? 0 : 1;
+    }
+}
+template <int D>
+__device__ __forceinline__ int blocks_of(int wv) {
+    return D == 128 ? (wv < 2 ? 3 : 2) : (wv < 3 ? 1 : 0);
+}
+
+template <int D>
+__device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane, f16v (&acc)[3]) {
+    constexpr int kPlane = kSlabRows * D * 2;
+    const unsigned char* hi = slab;
+    const unsigned char* lo = slab + kPlane;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+        const int kb = 16 * kc;
+        if (D == 128) {
+            if (wv < 2) {
+                const int c0 = 64 * wv, c1 = c0 + 32;
+                const h8v h0 = read_operand<D>(hi, kb, c0, lane), l0 = read_operand<D>(lo, kb, c0, lane);
+                const h8v h1 = read_operand<D>(hi, kb, c1, lane), l1 = read_operand<D>(lo, kb, c1, lane);
+                acc[0] = mma3(h0, l0, h0, l0, acc[0]);
+                acc[1] = mma3(h0, l0, h1, l1, acc[1]);
+                acc[2] = mma3(h1, l1, h1, l1, acc[2]);
+            } else {
+                const int c0 = 32 * (wv - 2);
+                const h8v h0 = read_operand<D>(hi, kb, c0, lane), l0 = read_operand<D>(lo, kb, c0, lane);
+                const h8v h2 = read_operand<D>(hi, kb, 64, lane), l2 = read_operand<D>(lo, kb, 64, lane);
+                const h8v h3 = read_operand<D>(hi, kb, 96, lane), l3 = read_operand<D>(lo, kb, 96, lane);
+                acc[0] = mma3(h0, l0, h2, l2, acc[0]);
+                acc[1] = mma3(h0, l0, h3, l3, acc[1]);
+            }
+        } else {
+            if (wv == 1) {
+                const h8v h0 = read_operand<D>(hi, kb, 0, lane), l0 = read_operand<D>(lo, kb, 0, lane);
+                const h8v h1 = read_operand<D>(hi, kb, 32, lane), l1 = read_operand<D>(lo, kb, 32, lane);
+                acc[0] = mma3(h0, l0, h1, l1, acc[0]);
+            } else if (wv != 3) {
+                const int c = wv == 0 ? 0 : 32;
+                const h8v h0 = read_operand<D>(hi, kb, c, lane), l0 = read_operand<D>(lo, kb, c, lane);
+                acc[0] = mma3(h0, l0, h0, l0, acc[0]);
+            }
+        }
+    }
+}
+
+// Inclusive prefix sum over the wave in lane order with DPP only: shifts of
+// 1, 2, 4, 8 within rows of 16 lanes, then row_bcast:15 and row_bcast:31.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
+    return x;
+}
+
+// Largest power-of-two exponent e with bound * 2^e < 2^14 (0 for bound 0):
+// every |R| <= bound / (2^b - 1) then scales into fp16's normal range.
+__device__ __forceinline__ int residual_exponent(float bound) {
+    if (!(bound > 0.0f)) return 0;
+    int E;
+    frexpf(bound, &E);
+    return 14 - E;
+}
+
+template <int D, int RK>
 __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPS = 64 / LPR;           // rows per wave per step
-    constexpr int RKX = RK > 0 ? RK : 1;
+    constexpr int SS = 16 / RPS;            // steps per 16-row slab slice
+    constexpr bool LR = RK > 0;
+    constexpr int RKX = LR ? RK : 1;
     constexpr int NP = RKX * (RKX + 1) / 2;
-    constexpr int LP = PairLanes<RKX>::LP;
-    constexpr int RING_STEPS = kRing / RPS;
-    static_assert(RING_STEPS % (2 * U) == 0 || (2 * U) % RING_STEPS == 0, "ring/step blocking");
-
-    __shared__ float s_b0[D * RKX];
-    __shared__ float s_w[4 * D * RKX];
-    __shared__ float s_ring[4 * kRing * RKX];
-    __shared__ double s_g[4 * NP];
-    __shared__ double s_gt[RKX * RKX];
-    __shared__ float s_m[RKX * RKX];
+    constexpr int NH = kThreads / D;        // threads per row of C in the power steps
+    constexpr int kPlane = kSlabRows * D * 2;
+    constexpr int kBig = LR ? (4 * kPlane > D * D * 4 ? 4 * kPlane : D * D * 4) : 16;
+    __shared__ __attribute__((aligned(16))) unsigned char s_big[kBig];  // 2 slabs, then C
+    __shared__ float s_b[LR ? D * RKX : 1];
+    __shared__ double s_w[LR ? (NH - 1) * D * RKX : 1];
+    __shared__ double s_g[RKX * RKX];
+    __shared__ double s_m[RKX * RKX];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
@@ -566,321 +707,441 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     const uint32_t cmask = (1u << bits) - 1u;
     const float qmax = (float)cmask;
     const int rank = o.rank;
-    // each wave owns rows [wr0, wr0 + rw); rw is a multiple of RPS
-    const int rw = ((rows + 3) / 4 + RPS - 1) / RPS * RPS;
-    const int steps = rw / RPS;
+    const int rw = wave_rows(rows);
+    const int nslab = rw / 16;
     const int wr0 = wv * rw;
     const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
                                          : a.x2 + (size_t)(mm - a.m_split) * rows * D;
 
-    if (mm == 0 && tid == 0) *a.err = 0u;
-    if (RK > 0) {
-        for (int i = tid; i < D * RKX; i += kThreads) {
-            const int j = i / RKX, c = i % RKX;
-            float v = 0.0f;
-            if (c < rank) {
-                const uint64_t u = splitmix64(a.seed, (uint64_t)(j * rank + c + 1)) >> 40;
-                v = (float)u * 0x1p-23f - 1.0f;
-            }
-            s_b0[i] = v;
-        }
-    }
-
-    StepBuf<U> ba, bb;
-
-    // ============ outlier threshold, from the select kernel ===================
-    uint32_t tkey = 0x8000u;      // above every finite key: nothing selected
-    float tf = __builtin_inff();   // |x| threshold as fp32
-    uint32_t take_w = 0, csr_w = 0;
+    // ---- outlier rule from the selection: |x| > thr, plus (in the one row
+    // block whose quota splits the ties at key T) ties ranked in flat order
+    uint32_t take_w = 0, csr = 0;
+    float thr = __builtin_inff(), tf = __builtin_inff();
+    bool split = false;
+    float bound = 0.0f;
+    const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
     if (kk > 0) {
-        const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
-        tkey = sel[0];
-        tf = h2f(tkey);
+        const uint32_t tkey = sel[0];
         take_w = sel[1 + wv];
-        csr_w = sel[5 + wv];
+        csr = sel[5 + wv];
+        const uint32_t eq_w = sel[9 + wv];
+        tf = h2f(tkey);
+        split = take_w > 0 && take_w < eq_w;
+        thr = (take_w > 0 && take_w == eq_w) ? (tkey > 0 ? h2f(tkey - 1) : -1.0f) : tf;
     }
+    if (LR) bound = h2f(sel[kSelBound]);
+    const int ex = LR ? residual_exponent(bound) : 0;
+    const float sx = ldexpf(1.0f, ex), rsx = ldexpf(1.0f, -ex);
+    const float thr_s = thr * sx, tf_s = tf * sx;
 
-    // ============ quantization pass, then the power-iteration passes =========
     int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     uint16_t* cm = o.col + (size_t)mm * kk;
     uint16_t* vm = o.val + (size_t)mm * kk;
-    float* Am = o.A + (size_t)mm * rows * rank;
-    const bool lowrank = RK > 0 && rank > 0 && a.iters > 0;
-    const int passes = lowrank ? a.iters : 1;
+    f16v acc[3];
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+    uint32_t ties_seen = 0;
 
-    float Bm[8][RKX];
-    if (RK > 0) {
-        __syncthreads();
+    auto load_slab = [&](uint4 (&xr)[SS], int sl) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-#pragma unroll
-            for (int c = 0; c < RKX; ++c) Bm[e][c] = s_b0[(colq * 8 + e) * RKX + c];
-    }
+        for (int u = 0; u < SS; ++u) {
+            const int row = wr0 + sl * 16 + u * RPS + rl;
+            const bool ok = sl < nslab && row < rows;
+            xr[u] = ok ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
+                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
 
-    for (int pass = 0; pass < passes; ++pass) {
-        const bool first = pass == 0, last = pass == passes - 1;
-        float W[8][RKX];
+    auto do_slab = [&](const uint4 (&xr)[SS], int sl) {
+        unsigned char* slab = s_big + (sl & 1) * 2 * kPlane;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+        for (int u = 0; u < SS; ++u) {
+            const int row = wr0 + sl * 16 + u * RPS + rl;
+            const bool valid = row < rows;
+            const size_t grow = (size_t)mm * rows + (valid ? row : 0);
+            float xf[8];
+            bool gt[8];
 #pragma unroll
-            for (int c = 0; c < RKX; ++c) W[e][c] = 0.0f;
-        double gacc = 0.0;
-        uint32_t ties_seen = 0, csr = csr_w;
-
-        auto step_block = [&](const StepBuf<U>& b, int s0) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int s = s0 + u;
-                if (s >= steps) break;   // wave-uniform
-                const int row = wr0 + s * RPS + rl;
-                const bool valid = row < rows;   // rows past the end hold zeros
-                const size_t grow = (size_t)mm * rows + (valid ? row : 0);
-                // ---- outliers: |x| > T, or |x| == T within the wave's tie quota
-                // (|x| compared in fp32: fp16 -> fp32 is exact and monotone)
-                float xf[8];
-                bool gt[8];
+            for (int e = 0; e < 8; ++e) {
+                xf[e] = h2f(half_of(xr[u], e)) * sx;
+                gt[e] = valid && fabsf(xf[e]) > thr_s;
+            }
+            if (split) {   // wave-uniform
                 bool any_eq = false;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xf[e] = h2f(half_of(b.x[u], e));
-                    gt[e] = fabsf(xf[e]) > tf;
-                    any_eq |= fabsf(xf[e]) == tf;
-                }
-                if (__ballot(any_eq) != 0ull && ties_seen < take_w) {   // rare
+                for (int e = 0; e < 8; ++e) any_eq |= valid && fabsf(xf[e]) == tf_s;
+                if (__ballot(any_eq) != 0ull && ties_seen < take_w) {
                     uint32_t eqm = 0u;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) eqm |= (fabsf(xf[e]) == tf) ? (1u << e) : 0u;
+                    for (int e = 0; e < 8; ++e)
+                        eqm |= (valid && fabsf(xf[e]) == tf_s) ? (1u << e) : 0u;
                     uint32_t tot;
                     uint32_t rank0 = ties_seen + wave_excl_scan(__builtin_popcount(eqm), lane, &tot);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         if ((eqm >> e) & 1u) {
-                            gt[e] = gt[e] || rank0 < take_w;
+                            gt[e] = rank0 < take_w;
                             ++rank0;
                         }
                     ties_seen += tot;
                 }
-                // ---- CSR (first pass only)
-                if (first && kk > 0) {
-                    uint32_t om = 0u;
+            }
+            // ---- CSR: row pointer, then this lane's outliers in column order
+            if (kk > 0) {
+                uint32_t om = 0u;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) om |= gt[e] ? (1u << e) : 0u;
-                    uint32_t pre = 0, tot = 0;
-                    if (__ballot(om != 0u) != 0ull) pre = wave_excl_scan(__builtin_popcount(om), lane, &tot);
-                    if (valid && colq == 0) rp[row] = (int32_t)(csr + pre);
-                    if (om) {
-                        uint32_t pos = csr + pre;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (((om >> e) & 1u) && pos < kk) {
-                                cm[pos] = (uint16_t)(colq * 8 + e);
-                                vm[pos] = (uint16_t)half_of(b.x[u], e);
-                                ++pos;
-                            }
+                for (int e = 0; e < 8; ++e) om |= gt[e] ? (1u << e) : 0u;
+                const uint32_t cnt = __builtin_popcount(om);
+                const uint32_t inc = wave_incl_scan_dpp(cnt);
+                const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+                uint32_t pos = csr + inc - cnt;
+                if (valid && colq == 0) rp[row] = (int32_t)pos;
+                while (om) {
+                    const int e = __builtin_ctz(om);
+                    om &= om - 1u;
+                    if (pos < kk) {
+                        cm[pos] = (uint16_t)(colq * 8 + e);
+                        vm[pos] = (uint16_t)half_of(xr[u], e);
                     }
-                    csr += tot;
-                } else if (first && valid && colq == 0) {
-                    rp[row] = 0;
+                    ++pos;
                 }
-                // ---- D = X - S; quantize (first pass) or reload codes; R
-                float v[8];
+                csr += tot;
+            } else if (valid && colq == 0) {
+                rp[row] = 0;
+            }
+            // ---- D = X - S, group quantization (in units scaled by 2^ex: every
+            // step below is exact under the scaling), R = D - deq
+            float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = gt[e] ? 0.0f : xf[e];
-                float R[8];
-                if (first) {
-                    float mn = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])),
-                                     fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
-                    float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                                     fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-                    group_minmax(mn, mx, gl);
-                    const float sc = (mx - mn) / qmax;
-                    const float inv = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
-                    float t[8], cf[8];
-                    bool near_tie = false;
+            for (int e = 0; e < 8; ++e) v[e] = gt[e] ? 0.0f : xf[e];
+            float mn = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])),
+                             fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
+            float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                             fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+            group_minmax(mn, mx, gl);
+            const float sc = (mx - mn) / qmax;
+            const float inv = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
+            float t[8], cf[8];
+            bool near_tie = false;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        t[e] = v[e] - mn;
-                        const float q = t[e] * inv;
-                        cf[e] = rintf(q);
-                        near_tie |= fabsf(q - cf[e]) > 0.49999f;
-                    }
-                    if (__ballot(near_tie) != 0ull && near_tie) {
-                        // within 1e-5 of a half-integer: round the exact quotient
+            for (int e = 0; e < 8; ++e) {
+                t[e] = v[e] - mn;
+                const float q = t[e] * inv;
+                cf[e] = rintf(q);
+                near_tie |= fabsf(q - cf[e]) > 0.49999f;
+            }
+            if (__ballot(near_tie) != 0ull && near_tie) {
+                // within 1e-5 of a half-integer: round the exact quotient
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) cf[e] = rintf(t[e] / sc);
-                    }
-                    uint32_t word = 0;
+                for (int e = 0; e < 8; ++e) cf[e] = rintf(t[e] / sc);
+            }
+            uint32_t word = 0;
+            float R[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        cf[e] = __builtin_amdgcn_fmed3f(cf[e], 0.0f, qmax);
-                        word |= (uint32_t)cf[e] << (e * bits);
-                        R[e] = fmaf(-cf[e], sc, t[e]);
-                    }
-                    if (valid) {
-                        if (bits == 4)
-                            reinterpret_cast<uint32_t*>(o.codes)[grow * (D / 8) + colq] = word;
-                        else
-                            reinterpret_cast<uint16_t*>(o.codes)[grow * (D / 8) + colq] = (uint16_t)word;
-                        if ((colq % gl) == 0) {
-                            o.scale[grow * ngr + colq / gl] = sc;
-                            o.zero[grow * ngr + colq / gl] = mn;
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float c = (float)((b.cw[u] >> (e * bits)) & cmask);
-                        R[e] = fmaf(-c, b.sc[u], v[e] - b.zp[u]);
-                    }
-                }
-                if (!lowrank) continue;
-                // ---- P = R B (row dot products), W += R^T P, ring of P rows
-                float p[RKX];
-#pragma unroll
-                for (int c = 0; c < RKX; ++c) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) acc = fmaf(R[e], Bm[e][c], acc);
-                    p[c] = row_allreduce<LPR>(acc);
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-#pragma unroll
-                    for (int c = 0; c < RKX; ++c) W[e][c] = fmaf(R[e], p[c], W[e][c]);
-                const int slot = s % RING_STEPS;
-                if (colq == 0) {
-#pragma unroll
-                    for (int c = 0; c < RKX; ++c) s_ring[(wv * kRing + slot * RPS + rl) * RKX + c] = p[c];
-                    if (last && valid) {
-#pragma unroll
-                        for (int c = 0; c < RKX; ++c)
-                            if (c < rank) Am[(size_t)row * rank + c] = p[c];
-                    }
-                }
-                if (slot == RING_STEPS - 1 || s == steps - 1) {
-                    // fp64 Gram update from the ring (wave-local LDS, in order)
-                    __builtin_amdgcn_wave_barrier();
-                    const int nr = (slot + 1) * RPS;
-                    const int q = lane / LP, sub = lane % LP;
-                    if (q < NP) {
-                        int c1 = 0, rem = q;
-                        while (rem >= RKX - c1) {
-                            rem -= RKX - c1;
-                            ++c1;
-                        }
-                        const int c2 = c1 + rem;
-                        const float* rg = s_ring + wv * kRing * RKX;
-                        for (int r2 = sub; r2 < nr; r2 += LP)
-                            gacc += (double)rg[r2 * RKX + c1] * (double)rg[r2 * RKX + c2];
-                    }
-                    __builtin_amdgcn_wave_barrier();
+            for (int e = 0; e < 8; ++e) {
+                cf[e] = __builtin_amdgcn_fmed3f(cf[e], 0.0f, qmax);
+                word |= (uint32_t)cf[e] << (e * bits);
+                R[e] = fmaf(-cf[e], sc, t[e]);
+            }
+            if (valid) {
+                if (bits == 4)
+                    reinterpret_cast<uint32_t*>(o.codes)[grow * (D / 8) + colq] = word;
+                else
+                    reinterpret_cast<uint16_t*>(o.codes)[grow * (D / 8) + colq] = (uint16_t)word;
+                if ((colq % gl) == 0) {
+                    o.scale[grow * ngr + colq / gl] = sc * rsx;
+                    o.zero[grow * ngr + colq / gl] = mn * rsx;
                 }
             }
-        };
-        load_steps<D, U, RPS>(ba, xm, o, mm, rows, wr0, 0, steps, rl, colq, !first);
-        for (int s0 = 0; s0 < steps; s0 += 2 * U) {
-            load_steps<D, U, RPS>(bb, xm, o, mm, rows, wr0, s0 + U, steps, rl, colq, !first);
-            step_block(ba, s0);
-            load_steps<D, U, RPS>(ba, xm, o, mm, rows, wr0, s0 + 2 * U, steps, rl, colq, !first);
-            step_block(bb, s0 + U);
-        }
-        if (first && tid == 0) rp[rows] = (int32_t)kk;
-        if (!lowrank) break;
-
-        // ---- end of a power step: reduce W and G over the workgroup
+            if (LR) {
+                // fp16 hi + lo of R * 2^ex, row-major into the slab
+                uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int c = 0; c < RKX; ++c) W[e][c] += __shfl_xor(W[e][c], off, 64);
-        if (rl == 0) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-#pragma unroll
-                for (int c = 0; c < RKX; ++c) s_w[(wv * D + colq * 8 + e) * RKX + c] = W[e][c];
-        }
-#pragma unroll
-        for (int off = 1; off < LP; off <<= 1) gacc += __shfl_xor(gacc, off, 64);
-        if ((lane % LP) == 0 && lane / LP < NP) s_g[wv * NP + lane / LP] = gacc;
-        __syncthreads();
-        for (int i = tid; i < D * RKX; i += kThreads)
-            s_w[i] = s_w[i] + s_w[D * RKX + i] + s_w[2 * D * RKX + i] + s_w[3 * D * RKX + i];
-        if (tid == 0) {
-            int q = 0;
-            for (int c1 = 0; c1 < RKX; ++c1)
-                for (int c2 = c1; c2 < RKX; ++c2) {
-                    const double v = s_g[q] + s_g[NP + q] + s_g[2 * NP + q] + s_g[3 * NP + q];
-                    ++q;
-                    s_gt[c1 * RKX + c2] = v;
-                    s_gt[c2 * RKX + c1] = v;
+                for (int i = 0; i < 4; ++i) {
+                    const auto h2 = __builtin_amdgcn_cvt_pkrtz(R[2 * i], R[2 * i + 1]);
+                    const auto l2 = __builtin_amdgcn_cvt_pkrtz(R[2 * i] - (float)h2[0],
+                                                               R[2 * i + 1] - (float)h2[1]);
+                    hw[i] = __builtin_bit_cast(uint32_t, h2);
+                    lw[i] = __builtin_bit_cast(uint32_t, l2);
                 }
-            gram_to_m<RKX>(s_gt, s_m);
+                const int srow = 16 * wv + u * RPS + rl;
+                const int off = srow * (D * 2) + swz_chunk<D>(srow, 2 * colq) * 8;
+                *reinterpret_cast<uint4*>(slab + off) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                *reinterpret_cast<uint4*>(slab + kPlane + off) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+            }
+        }
+        if (LR) {
+            __syncthreads();
+            slab_mma<D>(slab, wv, lane, acc);
+        }
+    };
+
+    {
+        uint4 xa[SS], xb[SS];
+        load_slab(xa, 0);
+        for (int sl = 0; sl < nslab; sl += 2) {
+            load_slab(xb, sl + 1);
+            do_slab(xa, sl);
+            if (sl + 1 < nslab) {
+                load_slab(xa, sl + 2);
+                do_slab(xb, sl + 1);
+            }
+        }
+    }
+    if (tid == 0) rp[rows] = (int32_t)kk;
+    if (!LR) return;
+
+    // ---- C = R^T R (unscaled below) into LDS, both triangles
+    __syncthreads();
+    float* Cm = reinterpret_cast<float*>(s_big);
+    {
+        const int nb = blocks_of<D>(wv);
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+            if (b >= nb) break;
+            int I, J;
+            block_of<D>(wv, b, I, J);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int m = 8 * (v / 4) + 4 * (lane / 32) + (v % 4), n = lane % 32;
+                Cm[(32 * I + m) * D + 32 * J + n] = acc[b][v];
+                if (I != J) Cm[(32 * J + n) * D + 32 * I + m] = acc[b][v];
+            }
+        }
+    }
+    // B0[j][c] = top 24 bits of splitmix64 output j*r + c + 1, times 2^-23, minus 1
+    for (int i = tid; i < D * RKX; i += kThreads) {
+        const int j = i / RKX, c = i % RKX;
+        float v = 0.0f;
+        if (c < rank) {
+            const uint64_t u = splitmix64(a.seed, (uint64_t)(j * rank + c + 1)) >> 40;
+            v = (float)u * 0x1p-23f - 1.0f;
+        }
+        s_b[i] = v;
+    }
+    __syncthreads();
+
+    // ---- power steps on C (fp64)
+    const double cscale = ldexp(1.0, -2 * ex);
+    const int j = tid % D, h = tid / D;
+    for (int it = 0; it < a.iters; ++it) {
+        const bool last = it == a.iters - 1;
+        double wp[RKX];
+#pragma unroll
+        for (int c = 0; c < RKX; ++c) wp[c] = 0.0;
+        for (int c0 = h * (D / NH); c0 < (h + 1) * (D / NH); ++c0) {
+            const double cv = (double)Cm[c0 * D + j];   // C[j][c0], by symmetry
+#pragma unroll
+            for (int c = 0; c < RKX; ++c) wp[c] += cv * (double)s_b[c0 * RKX + c];
+        }
+        if (h > 0) {
+#pragma unroll
+            for (int c = 0; c < RKX; ++c) s_w[((h - 1) * D + j) * RKX + c] = wp[c];
         }
         __syncthreads();
-        // B' = W M for this lane's 8 columns
+        if (h == 0) {
+            for (int hh = 1; hh < NH; ++hh)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float wrow[RKX];
+                for (int c = 0; c < RKX; ++c) wp[c] += s_w[((hh - 1) * D + j) * RKX + c];
 #pragma unroll
-            for (int c = 0; c < RKX; ++c) wrow[c] = s_w[(colq * 8 + e) * RKX + c];
+            for (int c = 0; c < RKX; ++c) wp[c] *= cscale;
+        }
+        __syncthreads();
+        if (h == 0) {
+#pragma unroll
+            for (int c = 0; c < RKX; ++c) s_w[j * RKX + c] = wp[c];
+        }
+        __syncthreads();
+        if (tid < NP) {
+            int c1 = 0, rem = tid;
+            while (rem >= RKX - c1) {
+                rem -= RKX - c1;
+                ++c1;
+            }
+            const int c2 = c1 + rem;
+            double g = 0.0;
+            for (int jj = 0; jj < D; ++jj) g += (double)s_b[jj * RKX + c1] * s_w[jj * RKX + c2];
+            s_g[c1 * RKX + c2] = g;
+            s_g[c2 * RKX + c1] = g;
+        }
+        __syncthreads();
+        if (tid == 0) gram_to_m<RKX>(s_g, s_m);
+        __syncthreads();
+        if (h == 0) {
+            double bn[RKX], bf[RKX];
 #pragma unroll
             for (int c = 0; c < RKX; ++c) {
-                float acc = 0.0f;
+                double x1 = 0.0, x2 = 0.0;
 #pragma unroll
-                for (int c2 = 0; c2 < RKX; ++c2) acc = fmaf(wrow[c2], s_m[c2 * RKX + c], acc);
-                Bm[e][c] = acc;
-            }
-        }
-        if (last) {
-            // A = P M in place, by the lanes that stored the P rows; B out
-            if (colq == 0) {
-                for (int s = 0; s < steps; ++s) {
-                    const int row = wr0 + s * RPS + rl;
-                    if (row >= rows) break;
-                    float pr[RKX];
-#pragma unroll
-                    for (int c = 0; c < RKX; ++c) pr[c] = c < rank ? Am[(size_t)row * rank + c] : 0.0f;
-#pragma unroll
-                    for (int c = 0; c < RKX; ++c) {
-                        if (c >= rank) continue;
-                        float acc = 0.0f;
-#pragma unroll
-                        for (int c2 = 0; c2 < RKX; ++c2) acc = fmaf(pr[c2], s_m[c2 * RKX + c], acc);
-                        Am[(size_t)row * rank + c] = acc;
-                    }
+                for (int c2 = 0; c2 <= c; ++c2) {
+                    x1 += wp[c2] * s_m[c2 * RKX + c];
+                    x2 += (double)s_b[j * RKX + c2] * s_m[c2 * RKX + c];
                 }
+                bn[c] = x1;
+                bf[c] = x2;
             }
-            if (wv == 0 && rl == 0) {
-                float* Bo = o.B + (size_t)mm * D * rank;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
+            for (int c = 0; c < RKX; ++c) s_b[j * RKX + c] = (float)bn[c];
+            if (last) {
+                float* Bo = o.B + ((size_t)mm * D + j) * rank;
+                float* Bf = a.bf + ((size_t)mm * D + j) * RKX;
 #pragma unroll
-                    for (int c = 0; c < RKX; ++c)
-                        if (c < rank) Bo[(colq * 8 + e) * rank + c] = Bm[e][c];
+                for (int c = 0; c < RKX; ++c) {
+                    if (c < rank) Bo[c] = (float)bn[c];
+                    Bf[c] = (float)bf[c];
+                }
             }
         }
         __syncthreads();
     }
 }
 
+// ---------------------------------------------------------------------------
+// A = R Bf (Bf = B_prev M of the last power step), one pass over X and the
+// stored codes; independent rows, so many workgroups per matrix.  The outlier
+// mask is rebuilt from X with the selection's rule; in the row block whose
+// ties are split the taken ties are looked up in the row's CSR entries.
+template <int D, int RK>
+__global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
+    constexpr int LPR = D / 8, RPS = 64 / LPR;
+    constexpr int U = 4, STEPS = 8;
+    constexpr int ROWS_W = RPS * STEPS, ROWS_WG = 4 * ROWS_W;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int colq = lane % LPR, rl = lane / LPR;
+    const Packed& o = a.out;
+    const int rows = o.rows, rank = o.rank, bits = o.bits;
+    const uint32_t cmask = (1u << bits) - 1u;
+    const uint32_t kk = (uint32_t)o.k;
+    const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
+    const int64_t mm = blockIdx.x / nblk;
+    const int r0 = (int)(blockIdx.x % nblk) * ROWS_WG + wv * ROWS_W;
+    const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
+                                         : a.x2 + (size_t)(mm - a.m_split) * rows * D;
+    float Bm[8][RK];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int c = 0; c < RK; ++c) Bm[e][c] = a.bf[((size_t)mm * D + colq * 8 + e) * RK + c];
+
+    // per row block (wave of the compress kernel): threshold and split flag
+    float thr[4], tf = __builtin_inff();
+    bool split[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        thr[b] = __builtin_inff();
+        split[b] = false;
+    }
+    if (kk > 0) {
+        const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
+        const uint32_t tkey = sel[0];
+        tf = h2f(tkey);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t take = sel[1 + b], eq = sel[9 + b];
+            split[b] = take > 0 && take < eq;
+            thr[b] = (take > 0 && take == eq) ? (tkey > 0 ? h2f(tkey - 1) : -1.0f) : tf;
+        }
+    }
+    const int rw = wave_rows(rows);
+    const int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
+    const uint16_t* cm = o.col + (size_t)mm * kk;
+    float* Am = o.A + (size_t)mm * rows * rank;
+
+    auto step_block = [&](const StepBuf<U>& b, int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = r0 + (s0 + u) * RPS + rl;
+            const bool valid = row < rows;
+            const int blk = min(row / rw, 3);
+            const float th = blk == 0 ? thr[0] : blk == 1 ? thr[1] : blk == 2 ? thr[2] : thr[3];
+            const bool sp = blk == 0 ? split[0] : blk == 1 ? split[1] : blk == 2 ? split[2] : split[3];
+            float xf[8];
+            bool gt[8];
+            bool any_eq = false;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                xf[e] = h2f(half_of(b.x[u], e));
+                gt[e] = valid && fabsf(xf[e]) > th;
+                any_eq |= valid && sp && fabsf(xf[e]) == tf;
+            }
+            if (__ballot(any_eq) != 0ull && any_eq) {   // rare: ties of the split block
+                const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (fabsf(xf[e]) == tf) {
+                        bool f = false;
+                        for (int i = beg; i < end; ++i) f |= cm[i] == (uint16_t)(colq * 8 + e);
+                        gt[e] = f;
+                    }
+            }
+            float R[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = gt[e] ? 0.0f : xf[e];
+                const float c = (float)((b.cw[u] >> (e * bits)) & cmask);
+                R[e] = fmaf(-c, b.sc[u], v - b.zp[u]);
+            }
+            float p[RK];
+#pragma unroll
+            for (int c = 0; c < RK; ++c) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(R[e], Bm[e][c], acc);
+                p[c] = row_allreduce<LPR>(acc);
+            }
+            if (valid && colq == 0) {
+#pragma unroll
+                for (int c = 0; c < RK; ++c)
+                    if (c < rank) Am[(size_t)row * rank + c] = p[c];
+            }
+        }
+    };
+    StepBuf<U> ba, bb;
+    load_steps<D, U, RPS>(ba, xm, o, mm, rows, r0, 0, STEPS, rl, colq, true);
+#pragma unroll 1
+    for (int s0 = 0; s0 < STEPS; s0 += 2 * U) {
+        load_steps<D, U, RPS>(bb, xm, o, mm, rows, r0, s0 + U, STEPS, rl, colq, true);
+        step_block(ba, s0);
+        if (s0 + 2 * U < STEPS) load_steps<D, U, RPS>(ba, xm, o, mm, rows, r0, s0 + 2 * U, STEPS, rl, colq, true);
+        step_block(bb, s0 + U);
+    }
+}
+
+template <int D>
+constexpr int lowrank_rows_per_wg() { return 4 * (64 / (D / 8)) * 8; }
+
 template <int D, int RK>
 hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
-    if (a.out.k > 0) {
-        hipLaunchKernelGGL((select_kernel<D, 4>), dim3((unsigned)a.out.M), dim3(kSelThreads), 0, st, a);
+    const unsigned M = (unsigned)a.out.M;
+    if (a.out.k > 0 || RK > 0) {
+        Timed t(kKSelect, st);
+        hipLaunchKernelGGL((select_kernel<D, 4>), dim3(M), dim3(kSelThreads), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    constexpr int U = RK >= 8 ? 1 : 4;
-    hipLaunchKernelGGL((compress_kernel<D, RK, U>), dim3((unsigned)a.out.M), dim3(kThreads), 0, st, a);
-    return hipGetLastError();
+    hipError_t e;
+    {
+        Timed t(kKCompress, st);
+        hipLaunchKernelGGL((compress_kernel<D, RK>), dim3(M), dim3(kThreads), 0, st, a);
+        e = hipGetLastError();
+    }
+    if constexpr (RK > 0) {
+        if (e != hipSuccess) return e;
+        constexpr int RPW = lowrank_rows_per_wg<D>();
+        const int64_t blocks = a.out.M * ((a.out.rows + RPW - 1) / RPW);
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        Timed t(kKLowrankA, st);
+        hipLaunchKernelGGL((lowrank_a_kernel<D, RK>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <int D>
 hipError_t launch_d(const CompressArgs& a, hipStream_t st) {
-    const int r = a.out.rank;
-    const int rk = r == 0 ? 0 : r <= 2 ? 2 : r <= 4 ? 4 : 8;
-    switch (rk) {
+    switch (rank_slots(a.out.rank)) {
         case 0: return launch_d_rk<D, 0>(a, st);
         case 2: return launch_d_rk<D, 2>(a, st);
         case 4: return launch_d_rk<D, 4>(a, st);
@@ -890,9 +1151,16 @@ hipError_t launch_d(const CompressArgs& a, hipStream_t st) {
 
 }  // namespace
 
+size_t compress_workspace(int64_t M, int d, int rank) {
+    // never 0, which the ABI reserves for rejected settings
+    const size_t n = align_up((size_t)M * kSelStride * 4) + align_up((size_t)M * d * rank_slots(rank) * 4);
+    return n > kAlign ? n : kAlign;
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
     if (a.out.M <= 0) return hipSuccess;
     if (a.out.M > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.out.rank > 0 && (a.out.rows < 1 || a.iters < 1)) return hipErrorInvalidValue;
     if (a.out.d == 64) return launch_d<64>(a, st);
     if (a.out.d == 128) return launch_d<128>(a, st);
     return hipErrorInvalidValue;

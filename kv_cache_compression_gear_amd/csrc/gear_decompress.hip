@@ -128,8 +128,8 @@ hipError_t launch_d(const Packed& p, uint16_t* out, hipStream_t st) {
     const int64_t blocks = p.M * ((p.rows + ROWS_WG - 1) / ROWS_WG);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    const int rk = p.rank == 0 ? 0 : p.rank <= 2 ? 2 : p.rank <= 4 ? 4 : 8;
-    switch (rk) {
+    Timed t(kKDecompress, st);
+    switch (rank_slots(p.rank)) {
         case 0: hipLaunchKernelGGL((decompress_kernel<D, 0>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p, out); break;
         case 2: hipLaunchKernelGGL((decompress_kernel<D, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p, out); break;
         case 4: hipLaunchKernelGGL((decompress_kernel<D, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p, out); break;

@@ -15,6 +15,28 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
+// Opt-in per-kernel timing (gear_timing_enable): a Timed object brackets one
+// launch with HIP events on its stream while timing is on; a no-op otherwise.
+enum KernelId {
+    kKSelect, kKCompress, kKLowrankA, kKDecompress, kKAttnSplit, kKAttnCombine,
+    kKBufferAppend, kKernelCount
+};
+bool timing_on();
+hipEvent_t timing_begin(hipStream_t st);                    // nullptr on failure
+void timing_end(KernelId k, hipEvent_t start, hipStream_t st);
+struct Timed {
+    KernelId k;
+    hipStream_t st;
+    hipEvent_t start;
+    Timed(KernelId k_, hipStream_t st_)
+        : k(k_), st(st_), start(timing_on() ? timing_begin(st_) : nullptr) {}
+    ~Timed() {
+        if (start) timing_end(k, start, st);
+    }
+    Timed(const Timed&) = delete;
+    Timed& operator=(const Timed&) = delete;
+};
+
 // Resolved packed layout, with device pointers of one buffer.
 struct Packed {
     int64_t M;         // compressed matrices
@@ -38,10 +60,18 @@ struct CompressArgs {
     Packed out;
     int32_t iters;
     uint64_t seed;
-    uint32_t* err;         // device failure word (cleared by the launch)
-    uint32_t* sel;         // [M][kSelStride] outlier threshold and per-block quotas
+    uint32_t* sel;         // workspace [M][kSelStride]: outlier threshold, per-block quotas
+    float* bf;             // workspace [M][d][rank_slots(rank)]: maps R to A
 };
 constexpr int kSelStride = 16;
+// Rank rounded up to the register tile the kernels are compiled for.
+inline int rank_slots(int r) { return r == 0 ? 0 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
+// Rows of a matrix owned by each of the 4 waves of a compress workgroup (a
+// multiple of 16, so every wave contributes whole 16-row MFMA k-slices).  The
+// selection and the A-projection kernels use the same split to find which
+// wave's tie quota a row falls under.
+__host__ __device__ inline int wave_rows(int rows) { return ((rows + 3) / 4 + 15) / 16 * 16; }
+size_t compress_workspace(int64_t M, int d, int rank);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
 // ---- decompress -----------------------------------------------------------
@@ -74,9 +104,6 @@ struct AttnArgs {
     int32_t splits;
     int32_t tokens_per_split;
 };
-// Split partials start after the workspace's first 256 bytes, which hold the
-// device failure word that compress kernels of the same cache report through.
-constexpr size_t kAttnPartialOffset = 256;
 size_t attn_workspace_bytes(int B, int Hkv, int Hq, int d, int64_t tokens, int* splits,
                             int* tokens_per_split);
 hipError_t launch_decode_attn(const AttnArgs& a, hipStream_t st);

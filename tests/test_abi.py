@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     lib = gear.lib()
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(gear.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -155,3 +155,16 @@ def test_cache_without_prompt_capacity():
         assert lib.gear_decode_attn(h, fake, 16, ctypes.c_float(0.1), fake, fake, 1 << 30, None) == 2
     finally:
         lib.gear_cache_destroy(h)
+
+
+def test_timing_registry_on_the_host():
+    """Timing is opt-in; reading it with no launches recorded needs no GPU."""
+    lib = gear.lib()
+    n, ms = ctypes.c_int64(-1), ctypes.c_double(-1.0)
+    assert lib.gear_timing_read(b"no_such_kernel", ctypes.byref(n), ctypes.byref(ms)) == 1
+    assert lib.gear_timing_enable(1) == 0
+    for name in gear.KERNELS:
+        assert lib.gear_timing_read(name.encode(), ctypes.byref(n), ctypes.byref(ms)) == 0
+        assert n.value == 0 and ms.value == 0.0
+    assert lib.gear_timing_enable(0) == 0
+    assert lib.gear_timing_read(None, ctypes.byref(n), ctypes.byref(ms)) == 1

@@ -166,4 +166,3 @@ def test_streaming_full_gqa_workload_sampled():
             torch.cuda.synchronize()
             ref = oc.decode_attention(q[sel].cpu().numpy())
             _attn_check(out[sel], ref, what=f"step {s}")
-    gear.workspace_error(cache.workspace)

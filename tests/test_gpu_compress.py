@@ -33,7 +33,6 @@ def _run_case(name, B, H, n, d, p, k_ch, mult, device_gen="cpu", sample=None):
     packed = gear.compress(x, p, workspace=ws)
     xhat = gear.decompress(packed)
     torch.cuda.synchronize()
-    gear.workspace_error(ws)
     ct = p.chunk_tokens or n
     C = n // ct
     op = to_orc_params(p)
