@@ -157,8 +157,10 @@ void orc_quantize(const float *D, int64_t n, int64_t d, int bits, int group,
             }
             float diff = mx - mn;                 /* fp32, rounded */
             float s = diff / (float)qmax;         /* fp32, correctly rounded */
-            scale[t * ng + gi] = s;
-            zero[t * ng + gi] = mn;
+            /* a zero scale or zero-point is stored as +0: with -0 and +0 in
+               one group the scan order would otherwise pick the sign */
+            scale[t * ng + gi] = s + 0.0f;
+            zero[t * ng + gi] = mn + 0.0f;
             for (int j = 0; j < group; ++j) {
                 int c = 0;
                 if (s != 0.0f) {

@@ -145,6 +145,19 @@ def test_quantizer_hand_worked_examples(row):
     assert orc.dequantize(c, s, z, len(vals))[0].tolist() == deq
 
 
+def test_signed_zero_group_stores_plus_zero():
+    # A group holding only -0 and +0 (in either order) has scale +0 and
+    # zero-point +0: the stored bits do not depend on which zero comes first.
+    for vals in ([-0.0, 0.0, 0.0, -0.0], [0.0, -0.0, -0.0, 0.0], [-0.0, -0.0, -0.0, -0.0]):
+        D = np.array([vals], np.float32)
+        c, s, z = orc.quantize(D, 2, 4)
+        assert s.view(np.uint32).tolist() == [[0]] and z.view(np.uint32).tolist() == [[0]]
+        assert c.tolist() == [[0, 0, 0, 0]]
+    # a -0 maximum with a negative minimum leaves the minimum and scale as they are
+    c, s, z = orc.quantize(np.array([[-3.0, -0.0, -1.5, -0.0]], np.float32), 2, 4)
+    assert z.tolist() == [[-3.0]] and s.tolist() == [[1.0]] and c.tolist() == [[0, 3, 2, 3]]
+
+
 def test_pack_bit_order_two_bit_and_four_bit():
     code = np.array([[1, 2, 3, 0, 3, 3, 0, 1]], np.uint8)
     assert orc.pack_codes(code, 2)[0].tolist() == [0b00111001, 0b01001111]
