@@ -58,8 +58,11 @@ __device__ __forceinline__ float row_allreduce(float v) {
     return v;
 }
 
-// min and max over each aligned group of g lanes, g in {1, 2, 4, 8, 16}.
+// min and max over each aligned group of g lanes, g in {1, 2, 4, 8, 16}
+// (g = G when G > 0).
+template <int G>
 __device__ __forceinline__ void group_minmax(float& mn, float& mx, int g) {
+    if (G > 0) g = G;
     if (g >= 2) { mn = fminf(mn, dpp<0xB1>(mn)); mx = fmaxf(mx, dpp<0xB1>(mx)); }
     if (g >= 4) { mn = fminf(mn, dpp<0x4E>(mn)); mx = fmaxf(mx, dpp<0x4E>(mx)); }
     if (g >= 8) { mn = fminf(mn, dpp<0x141>(mn)); mx = fmaxf(mx, dpp<0x141>(mx)); }
@@ -144,39 +147,6 @@ constexpr int kFine = 8;        // pass-2 bins inside the chosen coarse bin
 constexpr int kFineSlot = kFine + 1;
 constexpr int kSelThreads = 1024;
 constexpr int kSelBound = 13;   // selection word holding the magnitude bound
-
-// U consecutive row steps of one wave: the X words, and (after the first
-// pass) the stored code word and the group's scale and zero of each row.
-template <int U>
-struct StepBuf {
-    uint4 x[U];
-    uint32_t cw[U];
-    float sc[U], zp[U];
-};
-
-template <int D, int U, int RPS>
-__device__ __forceinline__ void load_steps(StepBuf<U>& b, const uint16_t* xm, const Packed& o,
-                                           int64_t mm, int rows, int wr0, int s0, int steps,
-                                           int rl, int colq, bool with_codes) {
-    const int ngr = D / o.group, gl = o.group / 8;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int row = wr0 + (s0 + u) * RPS + rl;
-        const bool ok = s0 + u < steps && row < rows;
-        b.x[u] = ok ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
-                    : make_uint4(0u, 0u, 0u, 0u);
-        b.cw[u] = 0u;
-        b.sc[u] = 0.0f;
-        b.zp[u] = 0.0f;
-        if (with_codes && ok) {
-            const size_t grow = (size_t)mm * rows + row;
-            b.cw[u] = o.bits == 4 ? reinterpret_cast<const uint32_t*>(o.codes)[grow * (D / 8) + colq]
-                                  : reinterpret_cast<const uint16_t*>(o.codes)[grow * (D / 8) + colq];
-            b.sc[u] = o.scale[grow * ngr + colq / gl];
-            b.zp[u] = o.zero[grow * ngr + colq / gl];
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Outlier threshold: the k-th largest |x| of a matrix, with ties broken by
@@ -680,7 +650,9 @@ __device__ __forceinline__ int residual_exponent(float bound) {
     return 14 - E;
 }
 
-template <int D, int RK>
+// GL: lanes per quantization group when fixed at compile time (D/8: a group
+// is a whole token row), 0 for the group size of the call.
+template <int D, int RK, int GL>
 __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPS = 64 / LPR;           // rows per wave per step
@@ -702,16 +674,24 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     const Packed& o = a.out;
     const int64_t mm = blockIdx.x;
     const int rows = o.rows;
-    const int bits = o.bits, gl = o.group / 8, ngr = D / o.group;
+    const int bits = o.bits;
+    const int gl = GL > 0 ? GL : o.group / 8, ngr = D / (8 * gl);
     const uint32_t kk = (uint32_t)o.k;
-    const uint32_t cmask = (1u << bits) - 1u;
-    const float qmax = (float)cmask;
+    const float qmax = (float)((1 << bits) - 1);
+    // 1/qmax rounded to nearest: with one fma correction the quotient
+    // y / qmax is correctly rounded for every fp32 y (checked exhaustively
+    // over all significands for qmax = 3 and 15)
+    const float rq = bits == 4 ? 0x1.111112p-4f : 0x1.555556p-2f;
     const int rank = o.rank;
     const int rw = wave_rows(rows);
     const int nslab = rw / 16;
     const int wr0 = wv * rw;
-    const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
-                                         : a.x2 + (size_t)(mm - a.m_split) * rows * D;
+    // per-matrix bases; 32-bit offsets below (rows * D * 2 < 2^32)
+    const unsigned char* xb = reinterpret_cast<const unsigned char*>(
+        mm < a.m_split ? a.x + (size_t)mm * rows * D : a.x2 + (size_t)(mm - a.m_split) * rows * D);
+    unsigned char* codes_m = o.codes + (size_t)mm * rows * (D * bits / 8);
+    float* scale_m = o.scale + (size_t)mm * rows * ngr;
+    float* zero_m = o.zero + (size_t)mm * rows * ngr;
 
     // ---- outlier rule from the selection: |x| > thr, plus (in the one row
     // block whose quota splits the ties at key T) ties ranked in flat order
@@ -749,7 +729,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         for (int u = 0; u < SS; ++u) {
             const int row = wr0 + sl * 16 + u * RPS + rl;
             const bool ok = sl < nslab && row < rows;
-            xr[u] = ok ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
+            xr[u] = ok ? *reinterpret_cast<const uint4*>(xb + ((uint32_t)row * D + colq * 8) * 2)
                        : make_uint4(0u, 0u, 0u, 0u);
         }
     };
@@ -760,50 +740,51 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         for (int u = 0; u < SS; ++u) {
             const int row = wr0 + sl * 16 + u * RPS + rl;
             const bool valid = row < rows;
-            const size_t grow = (size_t)mm * rows + (valid ? row : 0);
-            float xf[8];
-            bool gt[8];
+            const uint32_t urow = valid ? (uint32_t)row : 0u;
+            float xf[8], v[8];
+            uint32_t om = 0u;   // this lane's outliers (bit e: column 8 colq + e)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 xf[e] = h2f(half_of(xr[u], e)) * sx;
-                gt[e] = valid && fabsf(xf[e]) > thr_s;
+                const bool gt = valid && fabsf(xf[e]) > thr_s;
+                v[e] = gt ? 0.0f : xf[e];
+                if (kk > 0) om |= gt ? (1u << e) : 0u;
             }
-            if (split) {   // wave-uniform
-                bool any_eq = false;
+            if (split) {   // wave-uniform: the one block whose ties are split
+                uint32_t eqm = 0u;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) any_eq |= valid && fabsf(xf[e]) == tf_s;
-                if (__ballot(any_eq) != 0ull && ties_seen < take_w) {
-                    uint32_t eqm = 0u;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        eqm |= (valid && fabsf(xf[e]) == tf_s) ? (1u << e) : 0u;
+                for (int e = 0; e < 8; ++e)
+                    eqm |= (valid && fabsf(xf[e]) == tf_s) ? (1u << e) : 0u;
+                if (__ballot(eqm != 0u) != 0ull && ties_seen < take_w) {
                     uint32_t tot;
-                    uint32_t rank0 = ties_seen + wave_excl_scan(__builtin_popcount(eqm), lane, &tot);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if ((eqm >> e) & 1u) {
-                            gt[e] = rank0 < take_w;
-                            ++rank0;
-                        }
+                    uint32_t r = ties_seen + wave_excl_scan(__builtin_popcount(eqm), lane, &tot);
+                    uint32_t tm = 0u, m = eqm;   // ties of this lane taken, column order
+                    while (m != 0u && r < take_w) {
+                        tm |= m & (0u - m);
+                        m &= m - 1u;
+                        ++r;
+                    }
                     ties_seen += tot;
+                    om |= tm;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) v[e] = ((tm >> e) & 1u) ? 0.0f : v[e];
                 }
             }
             // ---- CSR: row pointer, then this lane's outliers in column order
             if (kk > 0) {
-                uint32_t om = 0u;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) om |= gt[e] ? (1u << e) : 0u;
                 const uint32_t cnt = __builtin_popcount(om);
                 const uint32_t inc = wave_incl_scan_dpp(cnt);
                 const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
                 uint32_t pos = csr + inc - cnt;
                 if (valid && colq == 0) rp[row] = (int32_t)pos;
-                while (om) {
-                    const int e = __builtin_ctz(om);
+                while (om != 0u) {
+                    const uint32_t e = (uint32_t)__builtin_ctz(om);
                     om &= om - 1u;
+                    const uint32_t w = (e & 4u) ? ((e & 2u) ? xr[u].w : xr[u].z)
+                                                : ((e & 2u) ? xr[u].y : xr[u].x);
                     if (pos < kk) {
                         cm[pos] = (uint16_t)(colq * 8 + e);
-                        vm[pos] = (uint16_t)half_of(xr[u], e);
+                        vm[pos] = (uint16_t)((e & 1u) ? (w >> 16) : w);
                     }
                     ++pos;
                 }
@@ -813,15 +794,14 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
             }
             // ---- D = X - S, group quantization (in units scaled by 2^ex: every
             // step below is exact under the scaling), R = D - deq
-            float v[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = gt[e] ? 0.0f : xf[e];
             float mn = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])),
                              fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
             float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
                              fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-            group_minmax(mn, mx, gl);
-            const float sc = (mx - mn) / qmax;
+            group_minmax<GL>(mn, mx, gl);
+            const float y = mx - mn;
+            const float q0 = y * rq;
+            const float sc = fmaf(fmaf(-q0, qmax, y), rq, q0) + 0.0f;   // RN(y / qmax), +0 for 0
             const float inv = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
             float t[8], cf[8];
             bool near_tie = false;
@@ -837,22 +817,30 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cf[e] = rintf(t[e] / sc);
             }
+            // 0 <= t <= mx - mn, so rint(t / sc) already lies in [0, 2^b - 1]
             uint32_t word = 0;
+            if (bits == 4) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    word = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(cf[2 * i + 1], 16.0f, cf[2 * i]), i, word);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    word = __builtin_amdgcn_cvt_pk_u8_f32(
+                        fmaf(cf[4 * i + 3], 64.0f, fmaf(cf[4 * i + 2], 16.0f, fmaf(cf[4 * i + 1], 4.0f, cf[4 * i]))),
+                        i, word);
+            }
             float R[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                cf[e] = __builtin_amdgcn_fmed3f(cf[e], 0.0f, qmax);
-                word |= (uint32_t)cf[e] << (e * bits);
-                R[e] = fmaf(-cf[e], sc, t[e]);
-            }
+            for (int e = 0; e < 8; ++e) R[e] = fmaf(-cf[e], sc, t[e]);
             if (valid) {
                 if (bits == 4)
-                    reinterpret_cast<uint32_t*>(o.codes)[grow * (D / 8) + colq] = word;
+                    *reinterpret_cast<uint32_t*>(codes_m + urow * (D / 2) + colq * 4) = word;
                 else
-                    reinterpret_cast<uint16_t*>(o.codes)[grow * (D / 8) + colq] = (uint16_t)word;
+                    *reinterpret_cast<uint16_t*>(codes_m + urow * (D / 4) + colq * 2) = (uint16_t)word;
                 if ((colq % gl) == 0) {
-                    o.scale[grow * ngr + colq / gl] = sc * rsx;
-                    o.zero[grow * ngr + colq / gl] = mn * rsx;
+                    scale_m[urow * ngr + colq / gl] = sc * rsx;
+                    zero_m[urow * ngr + colq / gl] = (mn + 0.0f) * rsx;
                 }
             }
             if (LR) {
@@ -1001,116 +989,160 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
 // ---------------------------------------------------------------------------
 // A = R Bf (Bf = B_prev M of the last power step), one pass over X and the
 // stored codes; independent rows, so many workgroups per matrix.  The outlier
-// mask is rebuilt from X with the selection's rule; in the row block whose
-// ties are split the taken ties are looked up in the row's CSR entries.
+// mask is rebuilt from X with the selection's rule: ties at key T are taken in
+// flat order, so rows below r_all take all of them, rows at or above r_none
+// none, and only rows in [r_all, r_none) (the one row block whose quota splits
+// the ties) look the taken ties up in their CSR entries.
+constexpr int kLrSteps = 16;   // token-row steps per wave
+
+// Ties taken, by flat order: rows [0, r_all) take all, [r_all, r_none) some.
+__device__ __forceinline__ void tie_rows(const uint32_t* sel, int rows, int& r_all, int& r_none) {
+    const int rw = wave_rows(rows);
+    r_all = rows;
+    r_none = rows;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t take = sel[1 + b], eq = sel[9 + b];
+        if (take < eq && r_all == rows) {
+            r_all = min(b * rw, rows);
+            r_none = take > 0 ? min((b + 1) * rw, rows) : r_all;
+        }
+    }
+}
+
 template <int D, int RK>
 __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR;
-    constexpr int U = 4, STEPS = 8;
-    constexpr int ROWS_W = RPS * STEPS, ROWS_WG = 4 * ROWS_W;
+    constexpr int U = 4;
+    constexpr int ROWS_W = RPS * kLrSteps, ROWS_WG = 4 * ROWS_W;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
     const int rows = o.rows, rank = o.rank, bits = o.bits;
+    const int ngr = D / o.group, gl = o.group / 8;
     const uint32_t cmask = (1u << bits) - 1u;
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
     const int64_t mm = blockIdx.x / nblk;
     const int r0 = (int)(blockIdx.x % nblk) * ROWS_WG + wv * ROWS_W;
-    const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
-                                         : a.x2 + (size_t)(mm - a.m_split) * rows * D;
+    // per-matrix bases; 32-bit byte offsets below (rows * D * 2 < 2^32)
+    const unsigned char* xb = reinterpret_cast<const unsigned char*>(
+        mm < a.m_split ? a.x + (size_t)mm * rows * D : a.x2 + (size_t)(mm - a.m_split) * rows * D);
+    const unsigned char* cb = o.codes + (size_t)mm * rows * (D * bits / 8);
+    const float* scb = o.scale + (size_t)mm * rows * ngr;
+    const float* zpb = o.zero + (size_t)mm * rows * ngr;
     float Bm[8][RK];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
         for (int c = 0; c < RK; ++c) Bm[e][c] = a.bf[((size_t)mm * D + colq * 8 + e) * RK + c];
 
-    // per row block (wave of the compress kernel): threshold and split flag
-    float thr[4], tf = __builtin_inff();
-    bool split[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        thr[b] = __builtin_inff();
-        split[b] = false;
-    }
+    float tf = __builtin_inff(), tf_lo = __builtin_inff();
+    int r_all = rows, r_none = rows;
     if (kk > 0) {
         const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
         const uint32_t tkey = sel[0];
         tf = h2f(tkey);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t take = sel[1 + b], eq = sel[9 + b];
-            split[b] = take > 0 && take < eq;
-            thr[b] = (take > 0 && take == eq) ? (tkey > 0 ? h2f(tkey - 1) : -1.0f) : tf;
-        }
+        tf_lo = tkey > 0 ? h2f(tkey - 1) : -1.0f;
+        tie_rows(sel, rows, r_all, r_none);
     }
-    const int rw = wave_rows(rows);
+    const bool wave_split = r0 < r_none && r0 + ROWS_W > r_all;   // wave-uniform
     const int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     const uint16_t* cm = o.col + (size_t)mm * kk;
     float* Am = o.A + (size_t)mm * rows * rank;
 
-    auto step_block = [&](const StepBuf<U>& b, int s0) {
+    uint4 xr[2][U];
+    uint32_t cw[2][U];
+    float sc[2][U], zp[2][U];
+    auto load = [&](int buf, int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int row = r0 + (s0 + u) * RPS + rl;
+            const bool ok = s0 + u < kLrSteps && row < rows;
+            const uint32_t rr = ok ? (uint32_t)row : 0u;
+            xr[buf][u] = ok ? *reinterpret_cast<const uint4*>(xb + (rr * D + colq * 8) * 2)
+                            : make_uint4(0u, 0u, 0u, 0u);
+            cw[buf][u] = !ok ? 0u
+                       : bits == 4 ? *reinterpret_cast<const uint32_t*>(cb + rr * (D / 2) + colq * 4)
+                                   : *reinterpret_cast<const uint16_t*>(cb + rr * (D / 4) + colq * 2);
+            const uint32_t gi = rr * ngr + colq / gl;
+            sc[buf][u] = ok ? scb[gi] : 0.0f;
+            zp[buf][u] = ok ? zpb[gi] : 0.0f;
+        }
+    };
+    auto compute = [&](int buf, int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = r0 + (s0 + u) * RPS + rl;
             const bool valid = row < rows;
-            const int blk = min(row / rw, 3);
-            const float th = blk == 0 ? thr[0] : blk == 1 ? thr[1] : blk == 2 ? thr[2] : thr[3];
-            const bool sp = blk == 0 ? split[0] : blk == 1 ? split[1] : blk == 2 ? split[2] : split[3];
-            float xf[8];
-            bool gt[8];
-            bool any_eq = false;
+            const float th = row < r_all ? tf_lo : tf;
+            float v[8];
+            bool eqa = false;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                xf[e] = h2f(half_of(b.x[u], e));
-                gt[e] = valid && fabsf(xf[e]) > th;
-                any_eq |= valid && sp && fabsf(xf[e]) == tf;
+                const float xf = h2f(half_of(xr[buf][u], e));
+                v[e] = fabsf(xf) > th ? 0.0f : xf;
+                if (wave_split) eqa |= fabsf(xf) == tf;
             }
-            if (__ballot(any_eq) != 0ull && any_eq) {   // rare: ties of the split block
-                const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (fabsf(xf[e]) == tf) {
-                        bool f = false;
-                        for (int i = beg; i < end; ++i) f |= cm[i] == (uint16_t)(colq * 8 + e);
-                        gt[e] = f;
+            if (wave_split) {
+                eqa = eqa && valid && row >= r_all && row < r_none;
+                if (__ballot(eqa) != 0ull && eqa) {
+                    // taken ties of this lane: those listed in the row's CSR
+                    uint32_t tm = 0u;
+                    const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
+#pragma unroll 1
+                    for (int i = beg; i < end; ++i) {
+                        const int cj = cm[i];
+                        if ((cj >> 3) == colq) tm |= 1u << (cj & 7);
                     }
-            }
-            float R[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float v = gt[e] ? 0.0f : xf[e];
-                const float c = (float)((b.cw[u] >> (e * bits)) & cmask);
-                R[e] = fmaf(-c, b.sc[u], v - b.zp[u]);
+                    for (int e = 0; e < 8; ++e)
+                        if (((tm >> e) & 1u) && fabsf(v[e]) == tf) v[e] = 0.0f;
+                }
             }
             float p[RK];
 #pragma unroll
-            for (int c = 0; c < RK; ++c) {
-                float acc = 0.0f;
+            for (int c = 0; c < RK; ++c) p[c] = 0.0f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc = fmaf(R[e], Bm[e][c], acc);
-                p[c] = row_allreduce<LPR>(acc);
+            for (int e = 0; e < 8; ++e) {
+                const float code = (float)((cw[buf][u] >> (e * bits)) & cmask);
+                const float R = fmaf(-code, sc[buf][u], v[e] - zp[buf][u]);
+#pragma unroll
+                for (int c = 0; c < RK; ++c) p[c] = fmaf(R, Bm[e][c], p[c]);
             }
-            if (valid && colq == 0) {
 #pragma unroll
-                for (int c = 0; c < RK; ++c)
-                    if (c < rank) Am[(size_t)row * rank + c] = p[c];
+            for (int c = 0; c < RK; ++c) p[c] = row_allreduce<LPR>(p[c]);
+            if (valid && colq == 0) {
+                if (rank == RK) {
+                    float* dst = Am + (size_t)row * RK;
+                    if (RK == 8) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(p[0], p[1 % RK], p[2 % RK], p[3 % RK]);
+                        *reinterpret_cast<float4*>(dst + 4) = make_float4(p[4 % RK], p[5 % RK], p[6 % RK], p[7 % RK]);
+                    } else if (RK == 4) {
+                        *reinterpret_cast<float4*>(dst) = make_float4(p[0], p[1 % RK], p[2 % RK], p[3 % RK]);
+                    } else {
+                        *reinterpret_cast<float2*>(dst) = make_float2(p[0], p[1 % RK]);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < RK; ++c)
+                        if (c < rank) Am[(size_t)row * rank + c] = p[c];
+                }
             }
         }
     };
-    StepBuf<U> ba, bb;
-    load_steps<D, U, RPS>(ba, xm, o, mm, rows, r0, 0, STEPS, rl, colq, true);
+    load(0, 0);
 #pragma unroll 1
-    for (int s0 = 0; s0 < STEPS; s0 += 2 * U) {
-        load_steps<D, U, RPS>(bb, xm, o, mm, rows, r0, s0 + U, STEPS, rl, colq, true);
-        step_block(ba, s0);
-        if (s0 + 2 * U < STEPS) load_steps<D, U, RPS>(ba, xm, o, mm, rows, r0, s0 + 2 * U, STEPS, rl, colq, true);
-        step_block(bb, s0 + U);
+    for (int s0 = 0; s0 < kLrSteps; s0 += 2 * U) {
+        load(1, s0 + U);
+        compute(0, s0);
+        if (s0 + 2 * U < kLrSteps) load(0, s0 + 2 * U);
+        compute(1, s0 + U);
     }
 }
 
 template <int D>
-constexpr int lowrank_rows_per_wg() { return 4 * (64 / (D / 8)) * 8; }
+constexpr int lowrank_rows_per_wg() { return 4 * (64 / (D / 8)) * kLrSteps; }
 
 template <int D, int RK>
 hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
@@ -1124,7 +1156,10 @@ hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
     hipError_t e;
     {
         Timed t(kKCompress, st);
-        hipLaunchKernelGGL((compress_kernel<D, RK>), dim3(M), dim3(kThreads), 0, st, a);
+        if (a.out.group == D)
+            hipLaunchKernelGGL((compress_kernel<D, RK, D / 8>), dim3(M), dim3(kThreads), 0, st, a);
+        else
+            hipLaunchKernelGGL((compress_kernel<D, RK, 0>), dim3(M), dim3(kThreads), 0, st, a);
         e = hipGetLastError();
     }
     if constexpr (RK > 0) {
