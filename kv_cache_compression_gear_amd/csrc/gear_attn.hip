@@ -79,13 +79,33 @@ __device__ Piece find_piece(const AttnArgs& a, int b, int hk, int t, int t_end) 
     return pc;
 }
 
-template <int LPR>
-__device__ __forceinline__ float row_sum(float v) {
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) v += __shfl_xor(v, off, 64);
+// Sum over each aligned group of N lanes (N = 8 or 16) with DPP: pairs,
+// quads, the mirrored quad, the mirrored half-row.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float row_allreduce(float v) {
+    v += dpp<0xB1>(v);
+    v += dpp<0x4E>(v);
+    v += dpp<0x141>(v);
+    if (N >= 16) v += dpp<0x140>(v);
     return v;
 }
 
+constexpr int kAttnCsrCap = 2048;   // outliers of one piece staged in LDS
+constexpr int kAU = 4;              // token steps per batch of loads
+
+// One workgroup per (batch, kv-head, split of kTPS tokens).  Each token of a
+// compressed piece is read once per phase: 8 codes per lane (D/8 lanes per
+// token), the group's scale and zero, the token's A row; the piece's CSR rows
+// are staged in LDS first so that the sparse terms need no dependent global
+// loads.  Phase 1 writes raw scores to LDS and adds the sparse term per row
+// (one thread per token, entries in CSR order); phase 2 folds each token's
+// sparse V entries into its dequantised values through a small per-wave LDS
+// tile that is scattered, read and cleared again.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TILE = 4 * RPS;
@@ -94,6 +114,10 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     __shared__ float s_qb[G * kMaxRank];
     __shared__ float s_red[4 * G * D];
     __shared__ float s_stat[2 * G];
+    __shared__ int32_t s_rp[kTPS + 1];
+    __shared__ uint32_t s_cv[kAttnCsrCap];
+    __shared__ __attribute__((aligned(16))) float s_tile[4 * RPS * D];
+    __shared__ float s_pa[4 * G * kMaxRank];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
@@ -108,6 +132,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         const int h = i / D, j = i % D;
         s_q[i] = h2f(a.q[((size_t)b * a.Hq + hk * G + h) * D + j]);
     }
+    for (int i = tid; i < 4 * RPS * D; i += kThreads) s_tile[i] = 0.0f;
     __syncthreads();
     float q[G][8], qs[G];
 #pragma unroll
@@ -120,89 +145,142 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         }
     }
 
-    // ---------------- phase 1: scores of the split's tokens
+    // CSR rows [row0, row0 + len) of matrix m of p into s_rp / s_cv; an entry
+    // is packed as column (bits 0-6) | row in the piece (bits 7-15) | fp16
+    // value (bits 16-31).
+    int csr_beg = 0, csr_cnt = 0;
+    bool csr_staged = true;
+    auto stage_csr = [&](const Packed& p, int64_t m, int row0, int len) {
+        __syncthreads();
+        const int32_t* rp = p.row_ptr + (size_t)m * (p.rows + 1) + row0;
+        for (int i = tid; i <= len; i += kThreads) s_rp[i] = min(max(rp[i], 0), p.k);
+        __syncthreads();
+        csr_beg = __builtin_amdgcn_readfirstlane(s_rp[0]);
+        csr_cnt = max(__builtin_amdgcn_readfirstlane(s_rp[len]) - csr_beg, 0);
+        csr_staged = csr_cnt <= kAttnCsrCap;
+        if (csr_staged) {
+            const uint16_t* cm = p.col + (size_t)m * p.k;
+            const uint16_t* vm = p.val + (size_t)m * p.k;
+            for (int i = tid; i < len; i += kThreads)
+                for (int k = s_rp[i]; k < s_rp[i + 1]; ++k)
+                    s_cv[k - csr_beg] = ((uint32_t)cm[k] & (D - 1)) | ((uint32_t)i << 7) |
+                                        ((uint32_t)vm[k] << 16);
+        }
+    };
+    // entry k (absolute index) of row `row` of the piece
+    auto csr_entry = [&](const Packed& p, int64_t m, int k, int row) -> uint32_t {
+        if (csr_staged) return s_cv[k - csr_beg];
+        return ((uint32_t)p.col[(size_t)m * p.k + k] & (D - 1)) | ((uint32_t)row << 7) |
+               ((uint32_t)p.val[(size_t)m * p.k + k] << 16);
+    };
+
+    // ---------------- phase 1: raw scores q . K^_t of the split's tokens
     for (int t = t0; t < t1;) {
         const Piece pc = find_piece(a, b, hk, t, t1);
+        const int base = t - t0;
         if (pc.kind == 0) {
             const Packed& p = pc.p;
             const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
             const uint32_t cmask = (1u << bits) - 1u;
-            // B^T q for this matrix: one row group of wave 0 spans all D columns
-            if (r > 0) {
-                __syncthreads();
-                if (wv == 0) {
-                    for (int c = 0; c < r; ++c) {
-                        float part[G];
+            stage_csr(p, pc.mk, pc.row0, pc.len);
+            if (r > 0 && wv == 0) {
+                // B^T q: one token row of lanes spans all D columns
+                for (int c = 0; c < r; ++c) {
+                    float part[G];
 #pragma unroll
-                        for (int h = 0; h < G; ++h) part[h] = 0.0f;
-                        if (rl == 0) {
+                    for (int h = 0; h < G; ++h) part[h] = 0.0f;
+                    if (rl == 0) {
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float bv = p.B[((size_t)pc.mk * D + colq * 8 + e) * r + c];
+                        for (int e = 0; e < 8; ++e) {
+                            const float bv = p.B[((size_t)pc.mk * D + colq * 8 + e) * r + c];
 #pragma unroll
-                                for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], bv, part[h]);
-                            }
-                        }
-#pragma unroll
-                        for (int h = 0; h < G; ++h) {
-                            const float v = row_sum<LPR>(part[h]);
-                            if (lane == 0) s_qb[h * kMaxRank + c] = v;
+                            for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], bv, part[h]);
                         }
                     }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const float v = row_allreduce<LPR>(part[h]);
+                        if (lane == 0) s_qb[h * kMaxRank + c] = v;
+                    }
                 }
-                __syncthreads();
             }
-            const int32_t* rp = p.row_ptr + (size_t)pc.mk * (p.rows + 1);
-            const uint16_t* cm = p.col + (size_t)pc.mk * p.k;
-            const uint16_t* vm = p.val + (size_t)pc.mk * p.k;
-            for (int tt = 0; tt < pc.len; tt += TILE) {
-                const int tok = tt + wv * RPS + rl;
-                const bool valid = tok < pc.len;
-                float part[G];
+            __syncthreads();
+            float qbl[G];   // (B^T q)[colq] for colq < r
 #pragma unroll
-                for (int h = 0; h < G; ++h) part[h] = 0.0f;
-                const int row = pc.row0 + (valid ? tok : 0);
-                const size_t grow = (size_t)pc.mk * p.rows + row;
-                if (valid) {
-                    uint32_t word;
-                    if (bits == 4)
-                        word = reinterpret_cast<const uint32_t*>(p.codes)[grow * (D / 8) + colq];
-                    else
-                        word = reinterpret_cast<const uint16_t*>(p.codes)[grow * (D / 8) + colq];
-                    const float sc = p.scale[grow * ngr + colq / gl];
-                    const float zp = p.zero[grow * ngr + colq / gl];
-                    float dot[G];
+            for (int h = 0; h < G; ++h) qbl[h] = colq < r ? s_qb[h * kMaxRank + colq] : 0.0f;
+            const size_t mrow = (size_t)pc.mk * p.rows + pc.row0;
+            const int steps = (pc.len + TILE - 1) / TILE;
+            uint32_t word[1][kAU];
+            float sc[1][kAU], zp[1][kAU], av[1][kAU];   // av: A[t][colq] for colq < r
+            // per-piece bases (uniform); lanes use 32-bit offsets and a clamped
+            // token (always a valid address), then zero what lies past the piece
+            const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
+            const float* sbase = p.scale + mrow * ngr;
+            const float* zbase = p.zero + mrow * ngr;
+            const float* abase = p.A + mrow * r;
+            const int acol = min(colq, max(r - 1, 0));
+            auto load = [&](int bf, int s0) {
 #pragma unroll
-                    for (int h = 0; h < G; ++h) dot[h] = 0.0f;
+                for (int u = 0; u < kAU; ++u) {
+                    const int tok = (s0 + u) * TILE + wv * RPS + rl;
+                    const bool ok = tok < pc.len;
+                    const uint32_t tk = (uint32_t)min(tok, pc.len - 1);
+                    const uint32_t w = bits == 4
+                        ? ld_at<uint32_t>(cbase, tk * (D / 2) + colq * 4)
+                        : (uint32_t)ld_at<uint16_t>(cbase, tk * (D / 4) + colq * 2);
+                    const uint32_t go = (tk * ngr + colq / gl) * 4;
+                    const float scv = ld_at<float>(sbase, go);
+                    const float zpv = ld_at<float>(zbase, go);
+                    const float a1 = r > 0 ? ld_at<float>(abase, (tk * r + acol) * 4) : 0.0f;
+                    word[bf][u] = ok ? w : 0u;
+                    sc[bf][u] = ok ? scv : 0.0f;
+                    zp[bf][u] = ok ? zpv : 0.0f;
+                    av[bf][u] = (ok && colq < r) ? a1 : 0.0f;
+                }
+            };
+            auto compute = [&](int bf, int s0) {
+#pragma unroll
+                for (int u = 0; u < kAU; ++u) {
+                    const int tok = (s0 + u) * TILE + wv * RPS + rl;
+                    float part[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) part[h] = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float cf = (float)((word >> (e * bits)) & cmask);
+                        const float cf = (float)((word[bf][u] >> (e * bits)) & cmask);
 #pragma unroll
-                        for (int h = 0; h < G; ++h) dot[h] = fmaf(q[h][e], cf, dot[h]);
+                        for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], cf, part[h]);
                     }
+                    // + A[t][colq] (B^T q)[colq] in the lanes colq < r, then the row sum
 #pragma unroll
-                    for (int h = 0; h < G; ++h) part[h] = fmaf(sc, dot[h], zp * qs[h]);
-                    const int beg = max(rp[row], 0), end = min(rp[row + 1], p.k);
-                    for (int i = beg; i < end; ++i) {
-                        const int cj = cm[i];
-                        if ((cj >> 3) == colq) {
-                            const float v = h2f(vm[i]);
+                    for (int h = 0; h < G; ++h)
+                        part[h] = row_allreduce<LPR>(
+                            fmaf(av[bf][u], qbl[h], fmaf(sc[bf][u], part[h], zp[bf][u] * qs[h])));
+                    if (tok < pc.len && colq == 0) {
 #pragma unroll
-                            for (int h = 0; h < G; ++h) part[h] = fmaf(s_q[h * D + cj], v, part[h]);
-                        }
+                        for (int h = 0; h < G; ++h) s_sc[(base + tok) * G + h] = part[h];
                     }
                 }
+            };
+            for (int s0 = 0; s0 < steps; s0 += kAU) {
+                load(0, s0);
+                compute(0, s0);
+            }
+            __syncthreads();
+            // sparse term, one thread per token, entries in CSR order
+            for (int i = tid; i < pc.len; i += kThreads) {
+                float add[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h) part[h] = row_sum<LPR>(part[h]);
-                if (valid && colq == 0) {
-                    for (int c = 0; c < r; ++c) {
-                        const float av = p.A[grow * r + c];
+                for (int h = 0; h < G; ++h) add[h] = 0.0f;
+                for (int k = s_rp[i]; k < s_rp[i + 1]; ++k) {
+                    const uint32_t cv = csr_entry(p, pc.mk, k, i);
+                    const int cj = (int)(cv & (D - 1));
+                    const float v = h2f(cv >> 16);
 #pragma unroll
-                        for (int h = 0; h < G; ++h) part[h] = fmaf(av, s_qb[h * kMaxRank + c], part[h]);
-                    }
-#pragma unroll
-                    for (int h = 0; h < G; ++h) s_sc[(t - t0 + tok) * G + h] = a.sm_scale * part[h];
+                    for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
                 }
+#pragma unroll
+                for (int h = 0; h < G; ++h) s_sc[(base + i) * G + h] += add[h];
             }
         } else {
             const uint16_t* kb = a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
@@ -223,10 +301,10 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     }
                 }
 #pragma unroll
-                for (int h = 0; h < G; ++h) part[h] = row_sum<LPR>(part[h]);
+                for (int h = 0; h < G; ++h) part[h] = row_allreduce<LPR>(part[h]);
                 if (valid && colq == 0) {
 #pragma unroll
-                    for (int h = 0; h < G; ++h) s_sc[(t - t0 + tok) * G + h] = a.sm_scale * part[h];
+                    for (int h = 0; h < G; ++h) s_sc[(base + tok) * G + h] = part[h];
                 }
             }
         }
@@ -234,7 +312,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // ---------------- softmax inside the split
+    // ---------------- softmax inside the split (scores scaled here)
     const int n = max(t1 - t0, 0);
     {
         float mx[G];
@@ -242,7 +320,11 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
         for (int i = tid; i < n; i += kThreads)
 #pragma unroll
-            for (int h = 0; h < G; ++h) mx[h] = fmaxf(mx[h], s_sc[i * G + h]);
+            for (int h = 0; h < G; ++h) {
+                const float v = a.sm_scale * s_sc[i * G + h];
+                s_sc[i * G + h] = v;
+                mx[h] = fmaxf(mx[h], v);
+            }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -284,73 +366,120 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    float* tile = s_tile + wv * RPS * D;
     for (int t = t0; t < t1;) {
         const Piece pc = find_piece(a, b, hk, t, t1);
+        const int base = t - t0;
         if (pc.kind == 0) {
             const Packed& p = pc.p;
             const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
             const uint32_t cmask = (1u << bits) - 1u;
-            const int32_t* rp = p.row_ptr + (size_t)pc.mv * (p.rows + 1);
-            const uint16_t* cm = p.col + (size_t)pc.mv * p.k;
-            const uint16_t* vm = p.val + (size_t)pc.mv * p.k;
-            float pa[G][kMaxRank];
+            stage_csr(p, pc.mv, pc.row0, pc.len);
+            __syncthreads();
+            float pa[G];   // sum_t p_t A[t][colq] in the lanes colq < r
 #pragma unroll
-            for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h) pa[h] = 0.0f;
+            const size_t mrow = (size_t)pc.mv * p.rows + pc.row0;
+            const int steps = (pc.len + TILE - 1) / TILE;
+            uint32_t word[1][kAU];
+            float sc[1][kAU], zp[1][kAU], av[1][kAU];
+            // per-piece bases (uniform); lanes use 32-bit offsets and a clamped
+            // token (always a valid address), then zero what lies past the piece
+            const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
+            const float* sbase = p.scale + mrow * ngr;
+            const float* zbase = p.zero + mrow * ngr;
+            const float* abase = p.A + mrow * r;
+            const int acol = min(colq, max(r - 1, 0));
+            auto load = [&](int bf, int s0) {
 #pragma unroll
-                for (int c = 0; c < kMaxRank; ++c) pa[h][c] = 0.0f;
-            for (int tt = 0; tt < pc.len; tt += TILE) {
-                const int tok = tt + wv * RPS + rl;
-                if (tok >= pc.len) continue;
-                const int row = pc.row0 + tok;
-                const size_t grow = (size_t)pc.mv * p.rows + row;
-                float pr[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h) pr[h] = s_sc[(t - t0 + tok) * G + h];
-                uint32_t word;
-                if (bits == 4)
-                    word = reinterpret_cast<const uint32_t*>(p.codes)[grow * (D / 8) + colq];
-                else
-                    word = reinterpret_cast<const uint16_t*>(p.codes)[grow * (D / 8) + colq];
-                const float sc = p.scale[grow * ngr + colq / gl];
-                const float zp = p.zero[grow * ngr + colq / gl];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float dv = fmaf((float)((word >> (e * bits)) & cmask), sc, zp);
-#pragma unroll
-                    for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pr[h], dv, acc[h][e]);
+                for (int u = 0; u < kAU; ++u) {
+                    const int tok = (s0 + u) * TILE + wv * RPS + rl;
+                    const bool ok = tok < pc.len;
+                    const uint32_t tk = (uint32_t)min(tok, pc.len - 1);
+                    const uint32_t w = bits == 4
+                        ? ld_at<uint32_t>(cbase, tk * (D / 2) + colq * 4)
+                        : (uint32_t)ld_at<uint16_t>(cbase, tk * (D / 4) + colq * 2);
+                    const uint32_t go = (tk * ngr + colq / gl) * 4;
+                    const float scv = ld_at<float>(sbase, go);
+                    const float zpv = ld_at<float>(zbase, go);
+                    const float a1 = r > 0 ? ld_at<float>(abase, (tk * r + acol) * 4) : 0.0f;
+                    word[bf][u] = ok ? w : 0u;
+                    sc[bf][u] = ok ? scv : 0.0f;
+                    zp[bf][u] = ok ? zpv : 0.0f;
+                    av[bf][u] = (ok && colq < r) ? a1 : 0.0f;
                 }
+            };
+            auto compute = [&](int bf, int s0) {
 #pragma unroll
-                for (int c = 0; c < kMaxRank; ++c) {
-                    if (c < r) {
-                        const float av = p.A[grow * r + c];
-#pragma unroll
-                        for (int h = 0; h < G; ++h) pa[h][c] = fmaf(pr[h], av, pa[h][c]);
+                for (int u = 0; u < kAU; ++u) {
+                    const int first = (s0 + u) * TILE + wv * RPS;   // this wave's first token
+                    const int tok = first + rl;
+                    const bool ok = tok < pc.len;
+                    // scatter the sparse entries of the wave's RPS tokens into its
+                    // tile, read this lane's 8 values, clear the cells again (LDS
+                    // operations of one wave execute in order)
+                    const int last = min(first + RPS, pc.len);
+                    const int e0 = first < pc.len ? s_rp[first] : 0;
+                    const int e1 = first < pc.len ? s_rp[last] : 0;
+                    for (int k = e0 + lane; k < e1; k += 64) {
+                        int rr = 0;
+                        if (!csr_staged)
+                            while (rr + 1 < RPS && first + rr + 1 <= last && k >= s_rp[first + rr + 1]) ++rr;
+                        const uint32_t cv = csr_entry(p, pc.mv, k, first + rr);
+                        tile[(((cv >> 7) & 0x1ffu) - first) * D + (cv & (D - 1))] = h2f(cv >> 16);
                     }
-                }
-                const int beg = max(rp[row], 0), end = min(rp[row + 1], p.k);
-                for (int i = beg; i < end; ++i) {
-                    const int cj = cm[i];
-                    if ((cj >> 3) == colq) {
-                        const float v = h2f(vm[i]);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if ((cj & 7) == e) {
-#pragma unroll
-                                for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pr[h], v, acc[h][e]);
-                            }
+                    __builtin_amdgcn_wave_barrier();
+                    const float4 s0v = *reinterpret_cast<const float4*>(tile + rl * D + colq * 8);
+                    const float4 s1v = *reinterpret_cast<const float4*>(tile + rl * D + colq * 8 + 4);
+                    const float sv[8] = {s0v.x, s0v.y, s0v.z, s0v.w, s1v.x, s1v.y, s1v.z, s1v.w};
+                    __builtin_amdgcn_wave_barrier();
+                    for (int k = e0 + lane; k < e1; k += 64) {
+                        int rr = 0;
+                        if (!csr_staged)
+                            while (rr + 1 < RPS && first + rr + 1 <= last && k >= s_rp[first + rr + 1]) ++rr;
+                        const uint32_t cv = csr_entry(p, pc.mv, k, first + rr);
+                        tile[(((cv >> 7) & 0x1ffu) - first) * D + (cv & (D - 1))] = 0.0f;
                     }
-                }
-            }
-            // low-rank part of this matrix: acc += B (sum_t p_t A_t)
+                    float pr[G];
 #pragma unroll
-            for (int c = 0; c < kMaxRank; ++c) {
-                if (c < r) {
+                    for (int h = 0; h < G; ++h) pr[h] = ok ? s_sc[(base + tok) * G + h] : 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float bv = p.B[((size_t)pc.mv * D + colq * 8 + e) * r + c];
+                        const float dv = fmaf((float)((word[bf][u] >> (e * bits)) & cmask), sc[bf][u], zp[bf][u]) + sv[e];
 #pragma unroll
-                        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pa[h][c], bv, acc[h][e]);
+                        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pr[h], dv, acc[h][e]);
                     }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) pa[h] = fmaf(pr[h], av[bf][u], pa[h]);
+                }
+            };
+            for (int s0 = 0; s0 < steps; s0 += kAU) {
+                load(0, s0);
+                compute(0, s0);
+            }
+            // low-rank part of this matrix: acc += B (sum_t p_t A_t), with the
+            // sums over the piece's tokens gathered per rank column c = colq
+#pragma unroll
+            for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+                for (int h = 0; h < G; ++h) pa[h] += __shfl_xor(pa[h], off, 64);
+            if (rl == 0 && colq < r) {
+#pragma unroll
+                for (int h = 0; h < G; ++h) s_pa[(wv * G + h) * kMaxRank + colq] = pa[h];
+            }
+            __syncthreads();
+            // the totals are workgroup-wide: one row group adds them
+            for (int c = 0; c < (wv == 0 && rl == 0 ? r : 0); ++c) {
+                float tot[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    tot[h] = s_pa[(0 * G + h) * kMaxRank + c] + s_pa[(1 * G + h) * kMaxRank + c] +
+                             s_pa[(2 * G + h) * kMaxRank + c] + s_pa[(3 * G + h) * kMaxRank + c];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float bv = p.B[((size_t)pc.mv * D + colq * 8 + e) * r + c];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) acc[h][e] = fmaf(tot[h], bv, acc[h][e]);
                 }
             }
         } else {
@@ -360,7 +489,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 if (tok >= pc.len) continue;
                 float pr[G];
 #pragma unroll
-                for (int h = 0; h < G; ++h) pr[h] = s_sc[(t - t0 + tok) * G + h];
+                for (int h = 0; h < G; ++h) pr[h] = s_sc[(base + tok) * G + h];
                 const uint4 w = *reinterpret_cast<const uint4*>(vb + (size_t)(pc.row0 + tok) * D + colq * 8);
                 const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -400,29 +529,54 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     }
 }
 
-// out[b][hq][:] = merge over splits of (acc, max, sum).
+// out[b][hq][:] = merge over splits of (acc, max, sum): 256 threads per
+// (b, hq); the splits are shared out over 256 / D lanes per column.
 template <int D, int G>
-__global__ void attn_combine_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
+    constexpr int NQ = kThreads / D;
+    __shared__ float s_m[kThreads / 64];
+    __shared__ float s_num[kThreads];
+    __shared__ float s_den[kThreads];
     const int bh = blockIdx.x;                 // b * Hq + hq
     const int b = bh / a.Hq, hq = bh % a.Hq;
     const int hk = hq / G, h = hq % G;
     const int pair = b * a.Hkv + hk;
-    const int j = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const float* base = a.partial + ((size_t)pair * a.splits * G + h) * (D + 2);
+    const size_t stride = (size_t)G * (D + 2);   // between splits
     float m = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) {
-        const float* part = a.partial + ((size_t)(pair * a.splits + s) * G + h) * (D + 2);
+    for (int s = tid; s < a.splits; s += kThreads) {
+        const float* part = base + s * stride;
         if (part[D + 1] > 0.0f) m = fmaxf(m, part[D]);
     }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) s_m[wv] = m;
+    __syncthreads();
+    m = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, s_m[w]);
+    const int j = tid % D, q = tid / D;
     float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < a.splits; ++s) {
-        const float* part = a.partial + ((size_t)(pair * a.splits + s) * G + h) * (D + 2);
-        if (part[D + 1] > 0.0f) {
+    for (int s = q; s < a.splits; s += NQ) {
+        const float* part = base + s * stride;
+        const float l = part[D + 1];
+        if (l > 0.0f) {
             const float w = expf(part[D] - m);
             num = fmaf(w, part[j], num);
-            den = fmaf(w, part[D + 1], den);
+            den = fmaf(w, l, den);
         }
     }
-    a.out[(size_t)bh * D + j] = den > 0.0f ? num / den : 0.0f;
+    s_num[tid] = num;
+    s_den[tid] = den;
+    __syncthreads();
+    if (q == 0) {
+        for (int qq = 1; qq < NQ; ++qq) {
+            num += s_num[qq * D + j];
+            den += s_den[qq * D + j];
+        }
+        a.out[(size_t)bh * D + j] = den > 0.0f ? num / den : 0.0f;
+    }
 }
 
 template <int D, int G>
@@ -437,7 +591,7 @@ hipError_t launch_dg(const AttnArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     {
         Timed t(kKAttnCombine, st);
-        hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((unsigned)(a.B * a.Hq)), dim3(D), 0, st, a);
+        hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((unsigned)(a.B * a.Hq)), dim3(kThreads), 0, st, a);
         e = hipGetLastError();
     }
     return e;

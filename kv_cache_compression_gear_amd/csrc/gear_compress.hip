@@ -729,8 +729,9 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         for (int u = 0; u < SS; ++u) {
             const int row = wr0 + sl * 16 + u * RPS + rl;
             const bool ok = sl < nslab && row < rows;
-            xr[u] = ok ? *reinterpret_cast<const uint4*>(xb + ((uint32_t)row * D + colq * 8) * 2)
-                       : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t rc = (uint32_t)min(row, rows - 1);   // always a valid address
+            const uint4 xv = ld_at<uint4>(xb, (rc * D + colq * 8) * 2);
+            xr[u] = ok ? xv : make_uint4(0u, 0u, 0u, 0u);
         }
     };
 
@@ -776,21 +777,21 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                 const uint32_t inc = wave_incl_scan_dpp(cnt);
                 const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
                 uint32_t pos = csr + inc - cnt;
-                if (valid && colq == 0) rp[row] = (int32_t)pos;
+                if (valid && colq == 0) st_at<int32_t>(rp, urow * 4, (int32_t)pos);
                 while (om != 0u) {
                     const uint32_t e = (uint32_t)__builtin_ctz(om);
                     om &= om - 1u;
                     const uint32_t w = (e & 4u) ? ((e & 2u) ? xr[u].w : xr[u].z)
                                                 : ((e & 2u) ? xr[u].y : xr[u].x);
                     if (pos < kk) {
-                        cm[pos] = (uint16_t)(colq * 8 + e);
-                        vm[pos] = (uint16_t)((e & 1u) ? (w >> 16) : w);
+                        st_at<uint16_t>(cm, pos * 2, (uint16_t)(colq * 8 + e));
+                        st_at<uint16_t>(vm, pos * 2, (uint16_t)((e & 1u) ? (w >> 16) : w));
                     }
                     ++pos;
                 }
                 csr += tot;
             } else if (valid && colq == 0) {
-                rp[row] = 0;
+                st_at<int32_t>(rp, urow * 4, 0);
             }
             // ---- D = X - S, group quantization (in units scaled by 2^ex: every
             // step below is exact under the scaling), R = D - deq
@@ -835,12 +836,13 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
             for (int e = 0; e < 8; ++e) R[e] = fmaf(-cf[e], sc, t[e]);
             if (valid) {
                 if (bits == 4)
-                    *reinterpret_cast<uint32_t*>(codes_m + urow * (D / 2) + colq * 4) = word;
+                    st_at<uint32_t>(codes_m, urow * (D / 2) + colq * 4, word);
                 else
-                    *reinterpret_cast<uint16_t*>(codes_m + urow * (D / 4) + colq * 2) = (uint16_t)word;
+                    st_at<uint16_t>(codes_m, urow * (D / 4) + colq * 2, (uint16_t)word);
                 if ((colq % gl) == 0) {
-                    scale_m[urow * ngr + colq / gl] = sc * rsx;
-                    zero_m[urow * ngr + colq / gl] = (mn + 0.0f) * rsx;
+                    const uint32_t go = (urow * ngr + colq / gl) * 4;
+                    st_at<float>(scale_m, go, sc * rsx);
+                    st_at<float>(zero_m, go, (mn + 0.0f) * rsx);
                 }
             }
             if (LR) {
@@ -1060,14 +1062,15 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
             const int row = r0 + (s0 + u) * RPS + rl;
             const bool ok = s0 + u < kLrSteps && row < rows;
             const uint32_t rr = ok ? (uint32_t)row : 0u;
-            xr[buf][u] = ok ? *reinterpret_cast<const uint4*>(xb + (rr * D + colq * 8) * 2)
-                            : make_uint4(0u, 0u, 0u, 0u);
-            cw[buf][u] = !ok ? 0u
-                       : bits == 4 ? *reinterpret_cast<const uint32_t*>(cb + rr * (D / 2) + colq * 4)
-                                   : *reinterpret_cast<const uint16_t*>(cb + rr * (D / 4) + colq * 2);
-            const uint32_t gi = rr * ngr + colq / gl;
-            sc[buf][u] = ok ? scb[gi] : 0.0f;
-            zp[buf][u] = ok ? zpb[gi] : 0.0f;
+            const uint4 xv = ld_at<uint4>(xb, (rr * D + colq * 8) * 2);
+            const uint32_t cv = bits == 4 ? ld_at<uint32_t>(cb, rr * (D / 2) + colq * 4)
+                                          : (uint32_t)ld_at<uint16_t>(cb, rr * (D / 4) + colq * 2);
+            const uint32_t go = (rr * ngr + colq / gl) * 4;
+            const float scv = ld_at<float>(scb, go), zpv = ld_at<float>(zpb, go);
+            xr[buf][u] = ok ? xv : make_uint4(0u, 0u, 0u, 0u);
+            cw[buf][u] = ok ? cv : 0u;
+            sc[buf][u] = ok ? scv : 0.0f;
+            zp[buf][u] = ok ? zpv : 0.0f;
         }
     };
     auto compute = [&](int buf, int s0) {

@@ -15,6 +15,18 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
+// Loads and stores at a 32-bit byte offset from a (workgroup-uniform) base, so
+// that the address is formed as base + zero-extended offset in one step (the
+// scalar-base addressing form), not with 64-bit vector arithmetic.
+template <typename T>
+__device__ __forceinline__ T ld_at(const void* base, uint32_t byte_off) {
+    return *reinterpret_cast<const T*>(static_cast<const unsigned char*>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ void st_at(void* base, uint32_t byte_off, T v) {
+    *reinterpret_cast<T*>(static_cast<unsigned char*>(base) + byte_off) = v;
+}
+
 // Opt-in per-kernel timing (gear_timing_enable): a Timed object brackets one
 // launch with HIP events on its stream while timing is on; a no-op otherwise.
 enum KernelId {
