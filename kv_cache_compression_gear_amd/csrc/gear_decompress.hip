@@ -5,12 +5,13 @@
 // coherent error, sparse for the outliers).
 //
 // HBM-bound streaming kernel.  A workgroup reconstructs a block of tokens of
-// one matrix: it first stages the block's slice of row_ptr and its outliers
-// (contiguous in the CSR arrays) in LDS with coalesced loads, then every lane
+// one matrix: every lane
 // -- owning 8 consecutive columns of a token, D/8 lanes per token -- issues the
 // loads of all its tokens (one 32- or 16-bit code word, the group's scale and
-// zero, the token's A row) before computing, adds its outliers from LDS, and
-// writes 8 fp16 values as one 16-byte store.
+// zero, the token's A row) before computing.  The block's outliers are
+// written into a dense fp16 LDS tile (one thread per row, in CSR order), read
+// back as 8 values per lane; each lane writes 8 fp16 values as one 16-byte
+// store.
 #include "gear_internal.h"
 
 namespace gear {
@@ -18,7 +19,6 @@ namespace {
 
 constexpr int kSteps = 8;        // token rows per lane
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kCsrCap = 4096;    // outliers a block stages in LDS
 
 __device__ __forceinline__ float h2f(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
@@ -33,9 +33,9 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     constexpr int ROWS_STEP = 4 * RPS;
     constexpr int ROWS_WG = kSteps * ROWS_STEP;
     constexpr int RKX = RK > 0 ? RK : 1;
-    __shared__ int32_t s_rp[ROWS_WG + 1];
-    __shared__ uint32_t s_cv[kCsrCap];       // col | (fp16 value << 16)
     __shared__ float s_b[D * RKX];
+    // S of the block's rows as a dense fp16 tile (the outliers are fp16 values)
+    __shared__ __attribute__((aligned(16))) uint16_t s_s[ROWS_WG * D];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
@@ -47,40 +47,64 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
     const uint32_t cmask = (1u << bits) - 1u;
 
-    const int32_t* rp = p.row_ptr + (size_t)mm * (rows + 1) + row0;
-    const uint16_t* cm = p.col + (size_t)mm * p.k;
-    const uint16_t* vm = p.val + (size_t)mm * p.k;
-    for (int i = tid; i <= nrows; i += kThreads) s_rp[i] = min(max(rp[i], 0), p.k);
+    // issue the loads of all the lane's tokens first (clamped rows: always
+    // valid addresses)
+    const size_t mrow = (size_t)mm * rows + row0;
+    const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
+    const float* sbase = p.scale + mrow * ngr;
+    const float* zbase = p.zero + mrow * ngr;
+    const float* abase = p.A + mrow * r;
+    uint32_t word[kSteps];
+    float sc[kSteps], zp[kSteps], ar[kSteps][RKX];
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int lr = s * ROWS_STEP + wv * RPS + rl;
+        const uint32_t tk = (uint32_t)min(lr, nrows - 1);
+        word[s] = bits == 4 ? ld_at<uint32_t>(cbase, tk * (D / 2) + colq * 4)
+                            : (uint32_t)ld_at<uint16_t>(cbase, tk * (D / 4) + colq * 2);
+        const uint32_t go = (tk * ngr + colq / gl) * 4;
+        sc[s] = ld_at<float>(sbase, go);
+        zp[s] = ld_at<float>(zbase, go);
+        if (RK > 0 && r == RK) {            // the A row as one or two vector loads
+            if (RK >= 4) {
+#pragma unroll
+                for (int c4 = 0; c4 < RKX / 4; ++c4) {
+                    const float4 a4 = ld_at<float4>(abase, (tk * RK + 4 * c4) * 4);
+                    ar[s][(4 * c4) % RKX] = a4.x;
+                    ar[s][(4 * c4 + 1) % RKX] = a4.y;
+                    ar[s][(4 * c4 + 2) % RKX] = a4.z;
+                    ar[s][(4 * c4 + 3) % RKX] = a4.w;
+                }
+            } else {
+                const float2 a2 = ld_at<float2>(abase, tk * RK * 4);
+                ar[s][0] = a2.x;
+                ar[s][1 % RKX] = a2.y;
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < RKX; ++c) ar[s][c] = (RK > 0 && c < r) ? ld_at<float>(abase, (tk * r + c) * 4) : 0.0f;
+        }
+    }
+
+    // S tile: clear, then one thread per row writes the row's outliers
+    {
+        uint4* t4 = reinterpret_cast<uint4*>(s_s);
+        for (int i = tid; i < ROWS_WG * D / 8; i += kThreads) t4[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     if (RK > 0)
         for (int i = tid; i < D * RKX; i += kThreads) {
             const int j = i / RKX, c = i % RKX;
             s_b[i] = c < r ? p.B[((size_t)mm * D + j) * r + c] : 0.0f;
         }
     __syncthreads();
-    const int beg = s_rp[0], cnt = max(s_rp[nrows] - beg, 0);
-    const bool staged = cnt <= kCsrCap;
-    if (staged)
-        for (int i = tid; i < cnt; i += kThreads)
-            s_cv[i] = (uint32_t)cm[beg + i] | ((uint32_t)vm[beg + i] << 16);
-
-    // all loads of the lane's tokens first
-    uint32_t word[kSteps];
-    float sc[kSteps], zp[kSteps], ar[kSteps][RKX];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int lr = s * ROWS_STEP + wv * RPS + rl;
-        const bool ok = lr < nrows;
-        const size_t grow = (size_t)mm * rows + row0 + (ok ? lr : 0);
-        word[s] = 0u;
-        sc[s] = zp[s] = 0.0f;
-        if (ok) {
-            word[s] = bits == 4 ? reinterpret_cast<const uint32_t*>(p.codes)[grow * (D / 8) + colq]
-                                : reinterpret_cast<const uint16_t*>(p.codes)[grow * (D / 8) + colq];
-            sc[s] = p.scale[grow * ngr + colq / gl];
-            zp[s] = p.zero[grow * ngr + colq / gl];
+    {
+        const int32_t* rp = p.row_ptr + (size_t)mm * (rows + 1) + row0;
+        const uint16_t* cm = p.col + (size_t)mm * p.k;
+        const uint16_t* vm = p.val + (size_t)mm * p.k;
+        for (int i = tid; i < nrows; i += kThreads) {
+            const int k0 = min(max(rp[i], 0), p.k), k1 = min(max(rp[i + 1], 0), p.k);
+            for (int k = k0; k < k1; ++k) s_s[i * D + (cm[k] & (D - 1))] = vm[k];
         }
-#pragma unroll
-        for (int c = 0; c < RKX; ++c) ar[s][c] = (RK > 0 && ok && c < r) ? p.A[grow * r + c] : 0.0f;
     }
     float Bm[8][RKX];
     __syncthreads();
@@ -92,33 +116,25 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         const int lr = s * ROWS_STEP + wv * RPS + rl;
-        if (lr >= nrows) continue;
-        const size_t grow = (size_t)mm * rows + row0 + lr;
+        if (s * ROWS_STEP + wv * RPS >= nrows) break;    // wave-uniform
+        const uint4 sv = *reinterpret_cast<const uint4*>(s_s + min(lr, ROWS_WG - 1) * D + colq * 8);
+        const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
         float x[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float v = fmaf((float)((word[s] >> (e * bits)) & cmask), sc[s], zp[s]);
 #pragma unroll
             for (int c = 0; c < RKX; ++c) v = fmaf(ar[s][c], Bm[e][c], v);
-            x[e] = v;
+            x[e] = v + h2f(sw[e >> 1] >> (16 * (e & 1)));
         }
-        const int lo = max(s_rp[lr] - beg, 0), hi = min(s_rp[lr + 1] - beg, cnt);
-        for (int i = lo; i < hi; ++i) {
-            const uint32_t cv = staged ? s_cv[i]
-                                       : ((uint32_t)cm[beg + i] | ((uint32_t)vm[beg + i] << 16));
-            const int cj = (int)(cv & 0xffffu);
-            if ((cj >> 3) == colq) {
-                const float v = h2f(cv >> 16);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] += ((cj & 7) == e) ? v : 0.0f;
-            }
+        if (lr < nrows) {
+            u32x4 o;
+            o.x = f2h(x[0]) | (f2h(x[1]) << 16);
+            o.y = f2h(x[2]) | (f2h(x[3]) << 16);
+            o.z = f2h(x[4]) | (f2h(x[5]) << 16);
+            o.w = f2h(x[6]) | (f2h(x[7]) << 16);
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + (mrow + lr) * D + colq * 8));
         }
-        u32x4 o;
-        o.x = f2h(x[0]) | (f2h(x[1]) << 16);
-        o.y = f2h(x[2]) | (f2h(x[3]) << 16);
-        o.z = f2h(x[4]) | (f2h(x[5]) << 16);
-        o.w = f2h(x[6]) | (f2h(x[7]) << 16);
-        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(out + grow * D + colq * 8));
     }
 }
 
