@@ -14,7 +14,7 @@
 //     largest |x|, each row block's share of the ties at T and its first CSR
 //     position.  A 1/16 row sample places a 4096-key window that one exact
 //     counting pass resolves; a two-pass radix select is the fallback.
-//   * compress_kernel (4 waves per matrix, one pass over X): outlier mask, CSR
+//   * compress_kernel (8 waves per matrix, one pass over X): outlier mask, CSR
 //     emit (DPP prefix sums), bit-exact fp32 group quantization (rint of the
 //     correctly rounded quotient, taken from a reciprocal product away from
 //     rounding ties), codes packed in registers, and C = R^T R on the matrix
@@ -146,18 +146,16 @@ constexpr int kCoarse = 4096;   // pass-1 bins: |x| bit pattern >> 3
 constexpr int kFine = 8;        // pass-2 bins inside the chosen coarse bin
 constexpr int kFineSlot = kFine + 1;
 constexpr int kSelThreads = 1024;
-constexpr int kSelBound = 13;   // selection word holding the magnitude bound
 
 // ---------------------------------------------------------------------------
 // Outlier threshold: the k-th largest |x| of a matrix, with ties broken by
 // the lower flat index.  One 16-wave workgroup per matrix.  The rows are split
-// exactly as the compress kernel splits them over its 4 waves (wave_rows);
-// each of those row blocks is read here by 4 consecutive waves.  Output per
-// matrix (kSelStride words): [0] threshold key T (|x| bits); [1..4] per row
-// block, the number of entries with key T it takes; [5..8] its first CSR
-// position; [9..12] the number of entries with key T it holds; [13] a key
-// bounding |x| over the entries that are not outliers (T, or the largest key
-// when k = 0, which only the low-rank fit needs).
+// exactly as the compress kernel splits them over its 8 waves (wave_rows);
+// each of those row blocks is read here by 2 consecutive waves.  Output per
+// matrix (kSelStride words, layout in gear_internal.h): the threshold key T,
+// per row block the ties at T it takes, its first CSR position and the ties it
+// holds, and a key bounding |x| over the entries that are not outliers (T, or
+// the largest key when k = 0, which only the low-rank fit needs).
 //
 // Common path (one pass over X plus a 1/16 sample): a histogram of a sample
 // of rows gives a key L0 that at least ~1.25 k entries reach; one pass then
@@ -169,14 +167,16 @@ template <int D, int U>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR;
     constexpr int NW = kSelThreads / 64;       // 16 waves
+    constexpr int NB = kCompressWaves;         // row blocks
+    constexpr int WPB = NW / NB;               // waves per row block
     constexpr int kWin = 4096;                 // exact window of keys
     constexpr int kSampleEvery = 16;           // sample = every 16th step
     __shared__ uint32_t s_hist[kCoarse];
-    __shared__ uint32_t s_win[4 * kWin];
+    __shared__ uint32_t s_win[NB * kWin];
     __shared__ uint32_t s_cnt[2 * NW];
     __shared__ uint32_t s_fine[NW * kFineSlot];
     __shared__ uint32_t s_tmp[NW];
-    __shared__ uint32_t s_res[12];
+    __shared__ uint32_t s_res[4 + kCompressWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
@@ -187,8 +187,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     uint32_t* sel = a.sel + (size_t)mm * kSelStride;
     const int rw = wave_rows(rows);
     const int steps = rw / RPS;
-    const int mb = wv / 4, sub = wv % 4;
-    const int per = (steps + 3) / 4;
+    const int mb = wv / WPB, sub = wv % WPB;
+    const int per = (steps + WPB - 1) / WPB;
     const int sb = min(steps, sub * per), se = min(steps, sb + per);
     const int wr0 = mb * rw;
     const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * rows * D
@@ -218,9 +218,9 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         return;
     }
     for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
-    for (int i = tid; i < 4 * kWin; i += kSelThreads) s_win[i] = 0u;
+    for (int i = tid; i < NB * kWin; i += kSelThreads) s_win[i] = 0u;
     if (tid < NW * kFineSlot) s_fine[tid] = 0u;
-    if (tid < 12) s_res[tid] = 0u;
+    if (tid < 4 + NB) s_res[tid] = 0u;
     __syncthreads();
 
     auto load = [&](uint4 (&xr)[U], bool (&ok)[U], int s0) {
@@ -258,11 +258,21 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
 
     // ---- sample: every 16th step of each wave's range
     uint32_t nsamp = 0;
-    for (int s0 = sb; s0 < se; s0 += kSampleEvery) {
-        const int row = wr0 + s0 * RPS + rl;
-        if (row < rows) {
-            const uint4 xr = *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8);
-            const uint32_t w4[4] = {xr.x, xr.y, xr.z, xr.w};
+    for (int s0 = sb; s0 < se; s0 += 4 * kSampleEvery) {   // 4 sampled rows in flight
+        uint4 xr[4];
+        bool ok[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int s = s0 + q * kSampleEvery;
+            const int row = wr0 + s * RPS + rl;
+            ok[q] = s < se && row < rows;
+            xr[q] = ok[q] ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
+                          : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (!ok[q]) continue;
+            const uint32_t w4[4] = {xr[q].x, xr[q].y, xr[q].z, xr[q].w};
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 atomicAdd(&s_hist[__builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 19u : 3u, 12u)], 1u);
@@ -329,18 +339,17 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     for (int off = 1; off < 64; off <<= 1) above += __shfl_xor(above, off, 64);
     if (lane == 0) s_cnt[NW + wv] = above;
     __syncthreads();
-    uint32_t above_b[4], above_tot = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        above_b[b] = s_cnt[NW + 4 * b] + s_cnt[NW + 4 * b + 1] + s_cnt[NW + 4 * b + 2] + s_cnt[NW + 4 * b + 3];
-        above_tot += above_b[b];
-    }
+    uint32_t above_tot = 0;
+    for (int w = 0; w < NW; ++w) above_tot += s_cnt[NW + w];
     {
         uint32_t h[4];
         const int b0 = (kSelThreads - 1 - tid) * 4;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            h[q] = s_win[b0 + q] + s_win[kWin + b0 + q] + s_win[2 * kWin + b0 + q] + s_win[3 * kWin + b0 + q];
+        for (int q = 0; q < 4; ++q) {
+            h[q] = 0u;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) h[q] += s_win[b * kWin + b0 + q];
+        }
         s_res[1] = 0xffffffffu;
         __syncthreads();
         if (above_tot < kk) find_bin(h, above_tot, kk, &s_res[1]);
@@ -350,25 +359,29 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     if (jstar != 0xffffffffu) {
         // exact threshold T = L0 + j*; per block: ties at T, count above T
         const int b0 = (kSelThreads - 1 - tid) * 4;
-        uint32_t gtp[4] = {0u, 0u, 0u, 0u};
+        uint32_t gtp[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) gtp[b] = 0u;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if ((uint32_t)(b0 + q) > jstar) {
 #pragma unroll
-                for (int b = 0; b < 4; ++b) gtp[b] += s_win[b * kWin + b0 + q];
+                for (int b = 0; b < NB; ++b) gtp[b] += s_win[b * kWin + b0 + q];
             }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < NB; ++b) {
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) gtp[b] += __shfl_xor(gtp[b], off, 64);
             if (lane == 0 && gtp[b]) atomicAdd(&s_res[4 + b], gtp[b]);
         }
         __syncthreads();
         if (wv == 0) {
-            const uint32_t eq = lane < 4 ? s_win[lane * kWin + jstar] : 0u;
+            const uint32_t eq = lane < NB ? s_win[lane * kWin + jstar] : 0u;
             uint32_t gt = 0;
-            if (lane < 4) gt = s_res[4 + lane] + (lane == 0 ? above_b[0] : lane == 1 ? above_b[1]
-                                                 : lane == 2 ? above_b[2] : above_b[3]);
+            if (lane < NB) {
+                gt = s_res[4 + lane];
+                for (int j = 0; j < WPB; ++j) gt += s_cnt[NW + lane * WPB + j];
+            }
             uint32_t tot_gt = gt;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) tot_gt += __shfl_xor(tot_gt, off, 64);
@@ -381,10 +394,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
                 sel[0] = L0 + jstar;
                 sel[kSelBound] = L0 + jstar;
             }
-            if (lane < 4) {
-                sel[1 + lane] = take;
-                sel[5 + lane] = before;
-                sel[9 + lane] = eq;
+            if (lane < NB) {
+                sel[kSelTake + lane] = take;
+                sel[kSelCsr + lane] = before;
+                sel[kSelEq + lane] = eq;
             }
         }
         return;
@@ -478,9 +491,9 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         const int fstar = bal ? (int)__builtin_ctzll(bal) : 0;
         const uint32_t need = needk - __shfl(strictly_above, fstar, 64);   // ties to take
         uint32_t eq = 0, gt = 0;
-        if (lane < 4) {
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t* f = s_fine + (lane * 4 + j) * kFineSlot;
+        if (lane < NB) {
+            for (int j = 0; j < WPB; ++j) {
+                const uint32_t* f = s_fine + (lane * WPB + j) * kFineSlot;
                 eq += f[fstar];
                 gt += f[kFine];
                 for (int q = fstar + 1; q < kFine; ++q) gt += f[q];
@@ -494,20 +507,20 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
             sel[0] = (bstar << 3) | (uint32_t)fstar;
             sel[kSelBound] = (bstar << 3) | (uint32_t)fstar;
         }
-        if (lane < 4) {
-            sel[1 + lane] = take;
-            sel[5 + lane] = before;
-            sel[9 + lane] = eq;
+        if (lane < NB) {
+            sel[kSelTake + lane] = take;
+            sel[kSelCsr + lane] = before;
+            sel[kSelEq + lane] = eq;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// Compress: one workgroup (4 waves) per matrix, one pass over its rows.
+// Compress: one workgroup (8 waves) per matrix, one pass over its rows.
 //
 // Wave w owns rows [w * wave_rows(n), (w + 1) * wave_rows(n)); a lane holds 8
 // consecutive columns of a token row, D/8 lanes per row.  The rows are taken
-// in slabs of 16 rows per wave (64 per workgroup).  For each row the wave
+// in slabs of 8 rows per wave (64 per workgroup).  For each row the wave
 // applies the outlier mask, emits the row's CSR entries, quantizes the groups
 // and forms the residual R = D - deq(Q).  With a low-rank term, R (scaled by
 // 2^ex so that fp16 covers it) is split into fp16 hi + lo parts and written
@@ -533,7 +546,9 @@ typedef short s4v __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) s4v lds_s4v;
 
-constexpr int kSlabRows = 64;     // 16 rows from each of the 4 waves
+constexpr int kSlabRows = 64;     // 8 rows from each of the 8 waves
+constexpr int kWaveSlab = kSlabRows / kCompressWaves;
+constexpr int kCompressThreads = kCompressWaves * 64;
 
 // 8-byte chunk c8 of slab row `row`, XOR-swizzled: the 4 rows a half-wave
 // reads in one transposing load land in 4 disjoint groups of 16 banks.
@@ -568,62 +583,50 @@ __device__ __forceinline__ f16v mma3(const h8v& hi_i, const h8v& lo_i, const h8v
     return acc;
 }
 
-// This wave's 32x32 blocks (I, J), I <= J, of C = R^T R, in column units of 32.
-// D = 128: waves 0, 1 take (a,a) (a,a+1) (a+1,a+1) for a = 0, 2; waves 2, 3
-// take (c,2) (c,3) for c = 0, 1.  D = 64: waves 0..2 take (0,0) (0,1) (1,1).
+// This wave's 32x32 blocks (I, J), I <= J, of C = R^T R, in column units of
+// 32.  D = 128 (10 blocks): waves 0..3 take (w,w) and (w,w+1) (wave 3:
+// (3,3) and (0,3)), wave 4 takes (0,2), wave 5 (1,3).  D = 64 (3 blocks):
+// waves 0..2 take (0,0), (0,1), (1,1).
+template <int D>
+__device__ __forceinline__ int blocks_of(int wv) {
+    return D == 128 ? (wv < 4 ? 2 : wv < 6 ? 1 : 0) : (wv < 3 ? 1 : 0);
+}
 template <int D>
 __device__ __forceinline__ void block_of(int wv, int b, int& I, int& J) {
     if (D == 128) {
-        if (wv < 2) {
-            I = 2 * wv + (b == 2 ? 1 : 0);
-            J = 2 * wv + (b == 0 ? 0 : 1);
+        if (wv < 4) {
+            I = b == 0 ? wv : (wv == 3 ? 0 : wv);
+            J = b == 0 ? wv : (wv == 3 ? 3 : wv + 1);
         } else {
-            I = wv - 2;
-            J = 2 + b;
+            I = wv - 4;
+            J = wv - 2;
         }
     } else {
         I = wv == 2 ? 1 : 0;
         J = wv == 0 ? 0 : 1;
     }
 }
-template <int D>
-__device__ __forceinline__ int blocks_of(int wv) {
-    return D == 128 ? (wv < 2 ? 3 : 2) : (wv < 3 ? 1 : 0);
-}
 
 template <int D>
-__device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane, f16v (&acc)[3]) {
+__device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane, f16v (&acc)[2]) {
     constexpr int kPlane = kSlabRows * D * 2;
     const unsigned char* hi = slab;
     const unsigned char* lo = slab + kPlane;
+    const int nb = blocks_of<D>(wv);
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-        const int kb = 16 * kc;
-        if (D == 128) {
-            if (wv < 2) {
-                const int c0 = 64 * wv, c1 = c0 + 32;
-                const h8v h0 = read_operand<D>(hi, kb, c0, lane), l0 = read_operand<D>(lo, kb, c0, lane);
-                const h8v h1 = read_operand<D>(hi, kb, c1, lane), l1 = read_operand<D>(lo, kb, c1, lane);
-                acc[0] = mma3(h0, l0, h0, l0, acc[0]);
-                acc[1] = mma3(h0, l0, h1, l1, acc[1]);
-                acc[2] = mma3(h1, l1, h1, l1, acc[2]);
+    for (int b = 0; b < 2; ++b) {
+        if (b >= nb) break;   // wave-uniform
+        int I, J;
+        block_of<D>(wv, b, I, J);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+            const int kb = 16 * kc;
+            const h8v hi_i = read_operand<D>(hi, kb, 32 * I, lane), lo_i = read_operand<D>(lo, kb, 32 * I, lane);
+            if (I == J) {
+                acc[b] = mma3(hi_i, lo_i, hi_i, lo_i, acc[b]);
             } else {
-                const int c0 = 32 * (wv - 2);
-                const h8v h0 = read_operand<D>(hi, kb, c0, lane), l0 = read_operand<D>(lo, kb, c0, lane);
-                const h8v h2 = read_operand<D>(hi, kb, 64, lane), l2 = read_operand<D>(lo, kb, 64, lane);
-                const h8v h3 = read_operand<D>(hi, kb, 96, lane), l3 = read_operand<D>(lo, kb, 96, lane);
-                acc[0] = mma3(h0, l0, h2, l2, acc[0]);
-                acc[1] = mma3(h0, l0, h3, l3, acc[1]);
-            }
-        } else {
-            if (wv == 1) {
-                const h8v h0 = read_operand<D>(hi, kb, 0, lane), l0 = read_operand<D>(lo, kb, 0, lane);
-                const h8v h1 = read_operand<D>(hi, kb, 32, lane), l1 = read_operand<D>(lo, kb, 32, lane);
-                acc[0] = mma3(h0, l0, h1, l1, acc[0]);
-            } else if (wv != 3) {
-                const int c = wv == 0 ? 0 : 32;
-                const h8v h0 = read_operand<D>(hi, kb, c, lane), l0 = read_operand<D>(lo, kb, c, lane);
-                acc[0] = mma3(h0, l0, h0, l0, acc[0]);
+                const h8v hi_j = read_operand<D>(hi, kb, 32 * J, lane), lo_j = read_operand<D>(lo, kb, 32 * J, lane);
+                acc[b] = mma3(hi_i, lo_i, hi_j, lo_j, acc[b]);
             }
         }
     }
@@ -653,14 +656,15 @@ __device__ __forceinline__ int residual_exponent(float bound) {
 // GL: lanes per quantization group when fixed at compile time (D/8: a group
 // is a whole token row), 0 for the group size of the call.
 template <int D, int RK, int GL>
-__global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
+__global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPS = 64 / LPR;           // rows per wave per step
-    constexpr int SS = 16 / RPS;            // steps per 16-row slab slice
+    constexpr int SS = kWaveSlab / RPS;     // steps per slab slice of a wave
     constexpr bool LR = RK > 0;
     constexpr int RKX = LR ? RK : 1;
     constexpr int NP = RKX * (RKX + 1) / 2;
-    constexpr int NH = kThreads / D;        // threads per row of C in the power steps
+    constexpr int PT = 256;                 // threads taking part in the power steps
+    constexpr int NH = PT / D;              // threads per row of C in the power steps
     constexpr int kPlane = kSlabRows * D * 2;
     constexpr int kBig = LR ? (4 * kPlane > D * D * 4 ? 4 * kPlane : D * D * 4) : 16;
     __shared__ __attribute__((aligned(16))) unsigned char s_big[kBig];  // 2 slabs, then C
@@ -684,7 +688,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     const float rq = bits == 4 ? 0x1.111112p-4f : 0x1.555556p-2f;
     const int rank = o.rank;
     const int rw = wave_rows(rows);
-    const int nslab = rw / 16;
+    const int nslab = rw / kWaveSlab;
     const int wr0 = wv * rw;
     // per-matrix bases; 32-bit offsets below (rows * D * 2 < 2^32)
     const unsigned char* xb = reinterpret_cast<const unsigned char*>(
@@ -702,9 +706,9 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
     if (kk > 0) {
         const uint32_t tkey = sel[0];
-        take_w = sel[1 + wv];
-        csr = sel[5 + wv];
-        const uint32_t eq_w = sel[9 + wv];
+        take_w = sel[kSelTake + wv];
+        csr = sel[kSelCsr + wv];
+        const uint32_t eq_w = sel[kSelEq + wv];
         tf = h2f(tkey);
         split = take_w > 0 && take_w < eq_w;
         thr = (take_w > 0 && take_w == eq_w) ? (tkey > 0 ? h2f(tkey - 1) : -1.0f) : tf;
@@ -717,9 +721,9 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     uint16_t* cm = o.col + (size_t)mm * kk;
     uint16_t* vm = o.val + (size_t)mm * kk;
-    f16v acc[3];
+    f16v acc[2];
 #pragma unroll
-    for (int b = 0; b < 3; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
     uint32_t ties_seen = 0;
@@ -727,7 +731,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     auto load_slab = [&](uint4 (&xr)[SS], int sl) {
 #pragma unroll
         for (int u = 0; u < SS; ++u) {
-            const int row = wr0 + sl * 16 + u * RPS + rl;
+            const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
             const bool ok = sl < nslab && row < rows;
             const uint32_t rc = (uint32_t)min(row, rows - 1);   // always a valid address
             const uint4 xv = ld_at<uint4>(xb, (rc * D + colq * 8) * 2);
@@ -739,7 +743,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         unsigned char* slab = s_big + (sl & 1) * 2 * kPlane;
 #pragma unroll
         for (int u = 0; u < SS; ++u) {
-            const int row = wr0 + sl * 16 + u * RPS + rl;
+            const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
             const bool valid = row < rows;
             const uint32_t urow = valid ? (uint32_t)row : 0u;
             float xf[8], v[8];
@@ -781,8 +785,11 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                 while (om != 0u) {
                     const uint32_t e = (uint32_t)__builtin_ctz(om);
                     om &= om - 1u;
-                    const uint32_t w = (e & 4u) ? ((e & 2u) ? xr[u].w : xr[u].z)
-                                                : ((e & 2u) ? xr[u].y : xr[u].x);
+                    // the dword holding column e, picked with bit selects
+                    const uint32_t s1 = 0u - ((e >> 1) & 1u), s2 = 0u - ((e >> 2) & 1u);
+                    const uint32_t lo2 = xr[u].x ^ ((xr[u].x ^ xr[u].y) & s1);
+                    const uint32_t hi2 = xr[u].z ^ ((xr[u].z ^ xr[u].w) & s1);
+                    const uint32_t w = lo2 ^ ((lo2 ^ hi2) & s2);
                     if (pos < kk) {
                         st_at<uint16_t>(cm, pos * 2, (uint16_t)(colq * 8 + e));
                         st_at<uint16_t>(vm, pos * 2, (uint16_t)((e & 1u) ? (w >> 16) : w));
@@ -856,7 +863,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
                     hw[i] = __builtin_bit_cast(uint32_t, h2);
                     lw[i] = __builtin_bit_cast(uint32_t, l2);
                 }
-                const int srow = 16 * wv + u * RPS + rl;
+                const int srow = kWaveSlab * wv + u * RPS + rl;
                 const int off = srow * (D * 2) + swz_chunk<D>(srow, 2 * colq) * 8;
                 *reinterpret_cast<uint4*>(slab + off) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
                 *reinterpret_cast<uint4*>(slab + kPlane + off) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
@@ -889,7 +896,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
     {
         const int nb = blocks_of<D>(wv);
 #pragma unroll
-        for (int b = 0; b < 3; ++b) {
+        for (int b = 0; b < 2; ++b) {
             if (b >= nb) break;
             int I, J;
             block_of<D>(wv, b, I, J);
@@ -902,7 +909,7 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         }
     }
     // B0[j][c] = top 24 bits of splitmix64 output j*r + c + 1, times 2^-23, minus 1
-    for (int i = tid; i < D * RKX; i += kThreads) {
+    for (int i = tid; i < D * RKX; i += kCompressThreads) {
         const int j = i / RKX, c = i % RKX;
         float v = 0.0f;
         if (c < rank) {
@@ -915,18 +922,18 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
 
     // ---- power steps on C (fp64)
     const double cscale = ldexp(1.0, -2 * ex);
-    const int j = tid % D, h = tid / D;
+    const int j = tid % D, h = tid / D;   // h < NH: the threads doing the power steps
     for (int it = 0; it < a.iters; ++it) {
         const bool last = it == a.iters - 1;
         double wp[RKX];
 #pragma unroll
         for (int c = 0; c < RKX; ++c) wp[c] = 0.0;
-        for (int c0 = h * (D / NH); c0 < (h + 1) * (D / NH); ++c0) {
+        for (int c0 = h * (D / NH); c0 < (h + 1) * (D / NH) && h < NH; ++c0) {
             const double cv = (double)Cm[c0 * D + j];   // C[j][c0], by symmetry
 #pragma unroll
             for (int c = 0; c < RKX; ++c) wp[c] += cv * (double)s_b[c0 * RKX + c];
         }
-        if (h > 0) {
+        if (h > 0 && h < NH) {
 #pragma unroll
             for (int c = 0; c < RKX; ++c) s_w[((h - 1) * D + j) * RKX + c] = wp[c];
         }
@@ -960,27 +967,23 @@ __global__ void __launch_bounds__(kThreads) compress_kernel(CompressArgs a) {
         if (tid == 0) gram_to_m<RKX>(s_g, s_m);
         __syncthreads();
         if (h == 0) {
-            double bn[RKX], bf[RKX];
+            // B' = W M and B_prev M, column by column from the last: M is upper
+            // triangular, so column c needs rows 0..c of B_prev, which are
+            // still unchanged when column c of B' is written
+            float* Bo = o.B + ((size_t)mm * D + j) * rank;
+            float* Bf = a.bf + ((size_t)mm * D + j) * RKX;
 #pragma unroll
-            for (int c = 0; c < RKX; ++c) {
+            for (int c = RKX - 1; c >= 0; --c) {
                 double x1 = 0.0, x2 = 0.0;
 #pragma unroll
                 for (int c2 = 0; c2 <= c; ++c2) {
                     x1 += wp[c2] * s_m[c2 * RKX + c];
                     x2 += (double)s_b[j * RKX + c2] * s_m[c2 * RKX + c];
                 }
-                bn[c] = x1;
-                bf[c] = x2;
-            }
-#pragma unroll
-            for (int c = 0; c < RKX; ++c) s_b[j * RKX + c] = (float)bn[c];
-            if (last) {
-                float* Bo = o.B + ((size_t)mm * D + j) * rank;
-                float* Bf = a.bf + ((size_t)mm * D + j) * RKX;
-#pragma unroll
-                for (int c = 0; c < RKX; ++c) {
-                    if (c < rank) Bo[c] = (float)bn[c];
-                    Bf[c] = (float)bf[c];
+                s_b[j * RKX + c] = (float)x1;
+                if (last) {
+                    if (c < rank) Bo[c] = (float)x1;
+                    Bf[c] = (float)x2;
                 }
             }
         }
@@ -1003,8 +1006,8 @@ __device__ __forceinline__ void tie_rows(const uint32_t* sel, int rows, int& r_a
     r_all = rows;
     r_none = rows;
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const uint32_t take = sel[1 + b], eq = sel[9 + b];
+    for (int b = 0; b < kCompressWaves; ++b) {
+        const uint32_t take = sel[kSelTake + b], eq = sel[kSelEq + b];
         if (take < eq && r_all == rows) {
             r_all = min(b * rw, rows);
             r_none = take > 0 ? min((b + 1) * rw, rows) : r_all;
@@ -1160,9 +1163,9 @@ hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
     {
         Timed t(kKCompress, st);
         if (a.out.group == D)
-            hipLaunchKernelGGL((compress_kernel<D, RK, D / 8>), dim3(M), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((compress_kernel<D, RK, D / 8>), dim3(M), dim3(kCompressThreads), 0, st, a);
         else
-            hipLaunchKernelGGL((compress_kernel<D, RK, 0>), dim3(M), dim3(kThreads), 0, st, a);
+            hipLaunchKernelGGL((compress_kernel<D, RK, 0>), dim3(M), dim3(kCompressThreads), 0, st, a);
         e = hipGetLastError();
     }
     if constexpr (RK > 0) {

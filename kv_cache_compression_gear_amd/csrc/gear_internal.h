@@ -75,14 +75,22 @@ struct CompressArgs {
     uint32_t* sel;         // workspace [M][kSelStride]: outlier threshold, per-block quotas
     float* bf;             // workspace [M][d][rank_slots(rank)]: maps R to A
 };
-constexpr int kSelStride = 16;
+// Selection results per matrix: [0] threshold key T, then per row block b
+// (= wave of the compress kernel): [kSelTake + b] ties at T it takes,
+// [kSelCsr + b] its first CSR position, [kSelEq + b] ties at T it holds;
+// [kSelBound] a key bounding |x| over the non-outliers.
+constexpr int kCompressWaves = 8;    // waves (row blocks) per compressed matrix
+constexpr int kSelTake = 1, kSelCsr = 9, kSelEq = 17, kSelBound = 25;
+constexpr int kSelStride = 32;
 // Rank rounded up to the register tile the kernels are compiled for.
 inline int rank_slots(int r) { return r == 0 ? 0 : r <= 2 ? 2 : r <= 4 ? 4 : 8; }
-// Rows of a matrix owned by each of the 4 waves of a compress workgroup (a
-// multiple of 16, so every wave contributes whole 16-row MFMA k-slices).  The
-// selection and the A-projection kernels use the same split to find which
-// wave's tie quota a row falls under.
-__host__ __device__ inline int wave_rows(int rows) { return ((rows + 3) / 4 + 15) / 16 * 16; }
+// Rows of a matrix owned by each of the kCompressWaves waves of a compress
+// workgroup (a multiple of 8: every wave adds whole 8-row slices to the
+// 64-row MFMA slabs).  The selection and the A-projection kernels use the
+// same split to find which wave's tie quota a row falls under.
+__host__ __device__ inline int wave_rows(int rows) {
+    return ((rows + kCompressWaves - 1) / kCompressWaves + 7) / 8 * 8;
+}
 size_t compress_workspace(int64_t M, int d, int rank);
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
 
