@@ -998,7 +998,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
 // flat order, so rows below r_all take all of them, rows at or above r_none
 // none, and only rows in [r_all, r_none) (the one row block whose quota splits
 // the ties) look the taken ties up in their CSR entries.
-constexpr int kLrSteps = 16;   // token-row steps per wave
+constexpr int kLrSteps = 4;    // 16-row steps per wave
 
 // Ties taken, by flat order: rows [0, r_all) take all, [r_all, r_none) some.
 __device__ __forceinline__ void tie_rows(const uint32_t* sel, int rows, int& r_all, int& r_none) {
@@ -1015,32 +1015,44 @@ __device__ __forceinline__ void tie_rows(const uint32_t* sel, int rows, int& r_a
     }
 }
 
+template <bool B>
+struct BoolTag { static constexpr bool value = B; };
+
+// A = R Bf on the matrix cores with v_mfma_f32_16x16x4_f32: M = 16 token
+// rows, N = 16 (the r columns of Bf, zero beyond r), K = 4 per instruction.
+// Lane l holds row l % 16 and the CPL = D/4 consecutive columns starting at
+// CPL (l / 16); the j-th instruction contracts column CPL q + j of the four
+// lane groups q, so CPL instructions cover all D columns and no cross-lane sum
+// is needed.  The output lanes n = l % 16 < r hold A[row][n] for the rows
+// 4 (l / 16) + 0..3 of the step.
 template <int D, int RK>
 __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
-    constexpr int LPR = D / 8, RPS = 64 / LPR;
-    constexpr int U = 4;
-    constexpr int ROWS_W = RPS * kLrSteps, ROWS_WG = 4 * ROWS_W;
+    constexpr int CPL = D / 4;                // columns per lane
+    constexpr int NX = CPL / 8;               // 16-byte chunks of X per lane
+    constexpr int ROWS_W = 16 * kLrSteps, ROWS_WG = 4 * ROWS_W;
+    typedef float f4v __attribute__((ext_vector_type(4)));
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int colq = lane % LPR, rl = lane / LPR;
+    const int rr = lane & 15, q = lane >> 4;
     const Packed& o = a.out;
     const int rows = o.rows, rank = o.rank, bits = o.bits;
-    const int ngr = D / o.group, gl = o.group / 8;
+    const int g = o.group, ngr = D / g;
+    const int ngl = g >= CPL ? 1 : CPL / g;   // groups within a lane's columns (<= 4)
     const uint32_t cmask = (1u << bits) - 1u;
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
     const int64_t mm = blockIdx.x / nblk;
     const int r0 = (int)(blockIdx.x % nblk) * ROWS_WG + wv * ROWS_W;
-    // per-matrix bases; 32-bit byte offsets below (rows * D * 2 < 2^32)
+    const int c0 = CPL * q;                   // first column of this lane
+    // per-matrix bases; 32-bit offsets below (rows * D * 2 < 2^32)
     const unsigned char* xb = reinterpret_cast<const unsigned char*>(
         mm < a.m_split ? a.x + (size_t)mm * rows * D : a.x2 + (size_t)(mm - a.m_split) * rows * D);
     const unsigned char* cb = o.codes + (size_t)mm * rows * (D * bits / 8);
     const float* scb = o.scale + (size_t)mm * rows * ngr;
     const float* zpb = o.zero + (size_t)mm * rows * ngr;
-    float Bm[8][RK];
+    float Bv[CPL];                            // B operand: Bf[c0 + j][n = rr]
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int c = 0; c < RK; ++c) Bm[e][c] = a.bf[((size_t)mm * D + colq * 8 + e) * RK + c];
+    for (int jj = 0; jj < CPL; ++jj)
+        Bv[jj] = rr < RK ? a.bf[((size_t)mm * D + c0 + jj) * RK + rr] : 0.0f;
 
     float tf = __builtin_inff(), tf_lo = __builtin_inff();
     int r_all = rows, r_none = rows;
@@ -1056,99 +1068,111 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const uint16_t* cm = o.col + (size_t)mm * kk;
     float* Am = o.A + (size_t)mm * rows * rank;
 
-    uint4 xr[2][U];
-    uint32_t cw[2][U];
-    float sc[2][U], zp[2][U];
-    auto load = [&](int buf, int s0) {
+    uint4 xr[1][NX];
+    uint4 cw[1];
+    float sc[1][4], zp[1][4];
+    auto load = [&](int buf, int s) {
+        const int row = r0 + s * 16 + rr;
+        const uint32_t rc = (uint32_t)min(row, rows - 1);   // always a valid address
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = r0 + (s0 + u) * RPS + rl;
-            const bool ok = s0 + u < kLrSteps && row < rows;
-            const uint32_t rr = ok ? (uint32_t)row : 0u;
-            const uint4 xv = ld_at<uint4>(xb, (rr * D + colq * 8) * 2);
-            const uint32_t cv = bits == 4 ? ld_at<uint32_t>(cb, rr * (D / 2) + colq * 4)
-                                          : (uint32_t)ld_at<uint16_t>(cb, rr * (D / 4) + colq * 2);
-            const uint32_t go = (rr * ngr + colq / gl) * 4;
-            const float scv = ld_at<float>(scb, go), zpv = ld_at<float>(zpb, go);
-            xr[buf][u] = ok ? xv : make_uint4(0u, 0u, 0u, 0u);
-            cw[buf][u] = ok ? cv : 0u;
-            sc[buf][u] = ok ? scv : 0.0f;
-            zp[buf][u] = ok ? zpv : 0.0f;
+        for (int c = 0; c < NX; ++c) xr[buf][c] = ld_at<uint4>(xb, (rc * D + c0 + 8 * c) * 2);
+        const uint32_t cbytes = (uint32_t)(CPL * bits / 8);  // 16, 8 or 4
+        const uint32_t coff = rc * (D * bits / 8) + (uint32_t)(c0 * bits / 8);
+        if (cbytes == 16) {
+            cw[buf] = ld_at<uint4>(cb, coff);
+        } else if (cbytes == 8) {
+            const uint2 v = ld_at<uint2>(cb, coff);
+            cw[buf] = make_uint4(v.x, v.y, 0u, 0u);
+        } else {
+            cw[buf] = make_uint4(ld_at<uint32_t>(cb, coff), 0u, 0u, 0u);
         }
-    };
-    auto compute = [&](int buf, int s0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int row = r0 + (s0 + u) * RPS + rl;
-            const bool valid = row < rows;
-            const float th = row < r_all ? tf_lo : tf;
-            float v[8];
-            bool eqa = false;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float xf = h2f(half_of(xr[buf][u], e));
-                v[e] = fabsf(xf) > th ? 0.0f : xf;
-                if (wave_split) eqa |= fabsf(xf) == tf;
-            }
-            if (wave_split) {
-                eqa = eqa && valid && row >= r_all && row < r_none;
-                if (__ballot(eqa) != 0ull && eqa) {
-                    // taken ties of this lane: those listed in the row's CSR
-                    uint32_t tm = 0u;
-                    const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
-#pragma unroll 1
-                    for (int i = beg; i < end; ++i) {
-                        const int cj = cm[i];
-                        if ((cj >> 3) == colq) tm |= 1u << (cj & 7);
-                    }
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (((tm >> e) & 1u) && fabsf(v[e]) == tf) v[e] = 0.0f;
-                }
-            }
-            float p[RK];
-#pragma unroll
-            for (int c = 0; c < RK; ++c) p[c] = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float code = (float)((cw[buf][u] >> (e * bits)) & cmask);
-                const float R = fmaf(-code, sc[buf][u], v[e] - zp[buf][u]);
-#pragma unroll
-                for (int c = 0; c < RK; ++c) p[c] = fmaf(R, Bm[e][c], p[c]);
-            }
-#pragma unroll
-            for (int c = 0; c < RK; ++c) p[c] = row_allreduce<LPR>(p[c]);
-            if (valid && colq == 0) {
-                if (rank == RK) {
-                    float* dst = Am + (size_t)row * RK;
-                    if (RK == 8) {
-                        *reinterpret_cast<float4*>(dst) = make_float4(p[0], p[1 % RK], p[2 % RK], p[3 % RK]);
-                        *reinterpret_cast<float4*>(dst + 4) = make_float4(p[4 % RK], p[5 % RK], p[6 % RK], p[7 % RK]);
-                    } else if (RK == 4) {
-                        *reinterpret_cast<float4*>(dst) = make_float4(p[0], p[1 % RK], p[2 % RK], p[3 % RK]);
-                    } else {
-                        *reinterpret_cast<float2*>(dst) = make_float2(p[0], p[1 % RK]);
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < RK; ++c)
-                        if (c < rank) Am[(size_t)row * rank + c] = p[c];
-                }
+        for (int t = 0; t < 4; ++t) {
+            if (t < ngl) {
+                const uint32_t go = (rc * ngr + (c0 + t * g) / g) * 4;
+                sc[buf][t] = ld_at<float>(scb, go);
+                zp[buf][t] = ld_at<float>(zpb, go);
             }
         }
     };
-    load(0, 0);
+    auto compute = [&](int buf, int s, auto split_tag, auto bits4_tag, auto one_group_tag) {
+        constexpr bool SPLIT = decltype(split_tag)::value;
+        constexpr bool BITS4 = decltype(bits4_tag)::value;      // else 2-bit codes
+        constexpr bool ONEG = decltype(one_group_tag)::value;   // one group per lane
+        const int row = r0 + s * 16 + rr;
+        const bool valid = row < rows;
+        const float th = row < r_all ? tf_lo : tf;
+        // ties of the split block taken by this row: bits of tm (column c0 + j)
+        uint32_t tm = 0u;
+        if (SPLIT) {
+            bool any_eq = false;
+#pragma unroll
+            for (int c = 0; c < NX; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) any_eq |= fabsf(h2f(half_of(xr[buf][c], e))) == tf;
+            any_eq = any_eq && valid && row >= r_all && row < r_none;
+            if (__ballot(any_eq) != 0ull && any_eq) {
+                const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
 #pragma unroll 1
-    for (int s0 = 0; s0 < kLrSteps; s0 += 2 * U) {
-        load(1, s0 + U);
-        compute(0, s0);
-        if (s0 + 2 * U < kLrSteps) load(0, s0 + 2 * U);
-        compute(1, s0 + U);
-    }
+                for (int i = beg; i < end; ++i) {
+                    const int cj = (int)cm[i] - c0;
+                    if (cj >= 0 && cj < CPL) tm |= 1u << cj;
+                }
+            }
+        }
+        f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        const uint32_t cwd[4] = {cw[buf].x, cw[buf].y, cw[buf].z, cw[buf].w};
+#pragma unroll
+        for (int c = 0; c < NX; ++c) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int jj = 8 * c + e;
+                const float xf = h2f(half_of(xr[buf][c], e));
+                bool out = fabsf(xf) > th;
+                if (SPLIT) out = out || ((tm >> jj) & 1u);
+                const float v = out ? 0.0f : xf;
+                constexpr int BB = BITS4 ? 4 : 2;
+                const float code = (float)((cwd[(jj * BB) >> 5] >> ((jj * BB) & 31)) & (BITS4 ? 15u : 3u));
+                float scv = sc[buf][0], zpv = zp[buf][0];
+                if (!ONEG) {   // groups of 8 or 16 columns: group of column jj
+                    const int t = jj / (g == 8 ? 8 : 16);
+                    scv = t == 0 ? sc[buf][0] : t == 1 ? sc[buf][1] : t == 2 ? sc[buf][2] : sc[buf][3];
+                    zpv = t == 0 ? zp[buf][0] : t == 1 ? zp[buf][1] : t == 2 ? zp[buf][2] : zp[buf][3];
+                }
+                const float R = fmaf(-code, scv, v - zpv);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(R, Bv[jj], acc, 0, 0, 0);
+            }
+        }
+        if (rr < rank) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int orow = r0 + s * 16 + 4 * q + i;
+                if (orow < rows) Am[(size_t)orow * rank + rr] = acc[i];
+            }
+        }
+    };
+    auto run = [&](auto split_tag, auto bits4_tag, auto one_group_tag) {
+#pragma unroll 1
+        for (int s = 0; s < kLrSteps; ++s) {
+            load(0, s);
+            compute(0, s, split_tag, bits4_tag, one_group_tag);
+        }
+    };
+    auto run2 = [&](auto split_tag) {
+        if (bits == 4) {
+            if (ngl == 1) run(split_tag, BoolTag<true>{}, BoolTag<true>{});
+            else run(split_tag, BoolTag<true>{}, BoolTag<false>{});
+        } else {
+            if (ngl == 1) run(split_tag, BoolTag<false>{}, BoolTag<true>{});
+            else run(split_tag, BoolTag<false>{}, BoolTag<false>{});
+        }
+    };
+    if (wave_split) run2(BoolTag<true>{});
+    else run2(BoolTag<false>{});
 }
 
 template <int D>
-constexpr int lowrank_rows_per_wg() { return 4 * (64 / (D / 8)) * kLrSteps; }
+constexpr int lowrank_rows_per_wg() { return 4 * 16 * kLrSteps; }
 
 template <int D, int RK>
 hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
