@@ -544,6 +544,8 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 typedef short s4v __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef short s2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s4v lds_s4v;
 
 constexpr int kSlabRows = 64;     // 8 rows from each of the 8 waves
@@ -634,11 +636,13 @@ __device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int 
 
 // Inclusive prefix sum over the wave in lane order with DPP only: shifts of
 // 1, 2, 4, 8 within rows of 16 lanes, then row_bcast:15 and row_bcast:31.
+// Lanes with no source lane read 0 (bound_ctrl), rows outside the row mask
+// keep x, so every step is a single v_add_u32_dpp.
 __device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);
-    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);
     x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);
     x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);
     return x;
@@ -697,10 +701,11 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     float* scale_m = o.scale + (size_t)mm * rows * ngr;
     float* zero_m = o.zero + (size_t)mm * rows * ngr;
 
-    // ---- outlier rule from the selection: |x| > thr, plus (in the one row
-    // block whose quota splits the ties at key T) ties ranked in flat order
+    // ---- outlier rule from the selection, on keys (|x| bit patterns, monotone
+    // in |x|): key > thrk, plus (in the one row block whose quota splits the
+    // ties at key T) ties ranked in flat order.  thrk = 0x7fff: none.
     uint32_t take_w = 0, csr = 0;
-    float thr = __builtin_inff(), tf = __builtin_inff();
+    int thrk = 0x7fff, tk = -1;
     bool split = false;
     float bound = 0.0f;
     const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
@@ -709,14 +714,17 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
         take_w = sel[kSelTake + wv];
         csr = sel[kSelCsr + wv];
         const uint32_t eq_w = sel[kSelEq + wv];
-        tf = h2f(tkey);
         split = take_w > 0 && take_w < eq_w;
-        thr = (take_w > 0 && take_w == eq_w) ? (tkey > 0 ? h2f(tkey - 1) : -1.0f) : tf;
+        tk = (int)tkey;
+        thrk = (take_w > 0 && take_w == eq_w) ? (int)tkey - 1 : (int)tkey;
     }
+    // both 16-bit halves hold thrk (thrk in [-1, 0x7fff], so thrk - key fits
+    // an int16 and is negative exactly for the outliers)
+    const uint32_t thr2 = ((uint32_t)thrk & 0xffffu) * 0x10001u;
     if (LR) bound = h2f(sel[kSelBound]);
     const int ex = LR ? residual_exponent(bound) : 0;
     const float sx = ldexpf(1.0f, ex), rsx = ldexpf(1.0f, -ex);
-    const float thr_s = thr * sx, tf_s = tf * sx;
+    const float m1 = -(sx * rsx);   // -1, opaque to the compiler: keeps fma_mix below
 
     int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     uint16_t* cm = o.col + (size_t)mm * kk;
@@ -741,25 +749,29 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
 
     auto do_slab = [&](const uint4 (&xr)[SS], int sl) {
         unsigned char* slab = s_big + (sl & 1) * 2 * kPlane;
+        uint32_t dm[SS][4], om[SS];
+        // ---- outlier mask: dm = x with the outliers set to +0, om bit e set
+        // for column 8 colq + e
 #pragma unroll
         for (int u = 0; u < SS; ++u) {
             const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
             const bool valid = row < rows;
-            const uint32_t urow = valid ? (uint32_t)row : 0u;
-            float xf[8], v[8];
-            uint32_t om = 0u;   // this lane's outliers (bit e: column 8 colq + e)
+            const uint32_t t2 = valid ? thr2 : 0x7fff7fffu;
+            const uint32_t d[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+            uint32_t bits2 = 0u;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                xf[e] = h2f(half_of(xr[u], e)) * sx;
-                const bool gt = valid && fabsf(xf[e]) > thr_s;
-                v[e] = gt ? 0.0f : xf[e];
-                if (kk > 0) om |= gt ? (1u << e) : 0u;
+            for (int i = 0; i < 4; ++i) {
+                const s2v r = __builtin_bit_cast(s2v, t2) - __builtin_bit_cast(s2v, d[i] & 0x7fff7fffu);
+                const uint32_t m = __builtin_bit_cast(uint32_t, r >> (s2v){15, 15});
+                dm[u][i] = d[i] & ~m;
+                bits2 |= m & ((1u << (2 * i)) | (1u << (2 * i + 17)));
             }
+            om[u] = (bits2 | (bits2 >> 16)) & 0xffu;
             if (split) {   // wave-uniform: the one block whose ties are split
                 uint32_t eqm = 0u;
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    eqm |= (valid && fabsf(xf[e]) == tf_s) ? (1u << e) : 0u;
+                    eqm |= (valid && (int)((d[e >> 1] >> (16 * (e & 1))) & 0x7fffu) == tk) ? (1u << e) : 0u;
                 if (__ballot(eqm != 0u) != 0ull && ties_seen < take_w) {
                     uint32_t tot;
                     uint32_t r = ties_seen + wave_excl_scan(__builtin_popcount(eqm), lane, &tot);
@@ -770,25 +782,41 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                         ++r;
                     }
                     ties_seen += tot;
-                    om |= tm;
+                    om[u] |= tm;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) v[e] = ((tm >> e) & 1u) ? 0.0f : v[e];
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t clr = (((tm >> (2 * i)) & 1u) ? 0xffffu : 0u) |
+                                             (((tm >> (2 * i + 1)) & 1u) ? 0xffff0000u : 0u);
+                        dm[u][i] &= ~clr;
+                    }
                 }
             }
-            // ---- CSR: row pointer, then this lane's outliers in column order
-            if (kk > 0) {
-                const uint32_t cnt = __builtin_popcount(om);
-                const uint32_t inc = wave_incl_scan_dpp(cnt);
-                const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
-                uint32_t pos = csr + inc - cnt;
-                if (valid && colq == 0) st_at<int32_t>(rp, urow * 4, (int32_t)pos);
-                while (om != 0u) {
-                    const uint32_t e = (uint32_t)__builtin_ctz(om);
-                    om &= om - 1u;
+        }
+        // ---- CSR: row pointers, then each lane's outliers in column order.
+        // One scan serves all SS steps: step u's count sits in bits 16u..16u+15
+        // (at most 512 per step).
+        if (kk > 0) {
+            uint32_t cnt = 0u;
+#pragma unroll
+            for (int u = 0; u < SS; ++u) cnt |= (uint32_t)__builtin_popcount(om[u]) << (16 * u);
+            const uint32_t inc = wave_incl_scan_dpp(cnt);
+            const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+            const uint32_t ex_l = inc - cnt;
+            uint32_t base = csr;
+#pragma unroll
+            for (int u = 0; u < SS; ++u) {
+                const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
+                uint32_t pos = base + ((ex_l >> (16 * u)) & 0xffffu);
+                if (row < rows && colq == 0) st_at<int32_t>(rp, (uint32_t)row * 4, (int32_t)pos);
+                uint32_t m = om[u];
+                const uint4 xw = xr[u];
+                while (m != 0u) {
+                    const uint32_t e = (uint32_t)__builtin_ctz(m);
+                    m &= m - 1u;
                     // the dword holding column e, picked with bit selects
                     const uint32_t s1 = 0u - ((e >> 1) & 1u), s2 = 0u - ((e >> 2) & 1u);
-                    const uint32_t lo2 = xr[u].x ^ ((xr[u].x ^ xr[u].y) & s1);
-                    const uint32_t hi2 = xr[u].z ^ ((xr[u].z ^ xr[u].w) & s1);
+                    const uint32_t lo2 = xw.x ^ ((xw.x ^ xw.y) & s1);
+                    const uint32_t hi2 = xw.z ^ ((xw.z ^ xw.w) & s1);
                     const uint32_t w = lo2 ^ ((lo2 ^ hi2) & s2);
                     if (pos < kk) {
                         st_at<uint16_t>(cm, pos * 2, (uint16_t)(colq * 8 + e));
@@ -796,34 +824,58 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                     }
                     ++pos;
                 }
-                csr += tot;
-            } else if (valid && colq == 0) {
-                st_at<int32_t>(rp, urow * 4, 0);
+                base += (tot >> (16 * u)) & 0xffffu;
             }
+            csr = base;
+        } else {
+#pragma unroll
+            for (int u = 0; u < SS; ++u) {
+                const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
+                if (row < rows && colq == 0) st_at<int32_t>(rp, (uint32_t)row * 4, 0);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SS; ++u) {
+            const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
+            const bool valid = row < rows;
+            const uint32_t urow = valid ? (uint32_t)row : 0u;
             // ---- D = X - S, group quantization (in units scaled by 2^ex: every
-            // step below is exact under the scaling), R = D - deq
-            float mn = fminf(fminf(fminf(v[0], v[1]), fminf(v[2], v[3])),
-                             fminf(fminf(v[4], v[5]), fminf(v[6], v[7])));
-            float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                             fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+            // step below is exact under the scaling), R = D - deq.  min and max
+            // are taken on the fp16 values (exact), then scaled.
+            const h2v a0 = __builtin_bit_cast(h2v, dm[u][0]), a1 = __builtin_bit_cast(h2v, dm[u][1]);
+            const h2v a2 = __builtin_bit_cast(h2v, dm[u][2]), a3 = __builtin_bit_cast(h2v, dm[u][3]);
+            const h2v n2 = __builtin_elementwise_min(__builtin_elementwise_min(a0, a1),
+                                                     __builtin_elementwise_min(a2, a3));
+            const h2v x2 = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
+                                                     __builtin_elementwise_max(a2, a3));
+            float mn = (float)__builtin_elementwise_min(n2[0], n2[1]) * sx;
+            float mx = (float)__builtin_elementwise_max(x2[0], x2[1]) * sx;
             group_minmax<GL>(mn, mx, gl);
             const float y = mx - mn;
             const float q0 = y * rq;
             const float sc = fmaf(fmaf(-q0, qmax, y), rq, q0) + 0.0f;   // RN(y / qmax), +0 for 0
             const float inv = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
-            float t[8], cf[8];
+            // t * inv is within a few ulp of the correctly rounded quotient, so
+            // rint can differ from it only when t / sc is within 1e-5 of a
+            // half-integer, that is when |R| > 0.49999 sc
+            const float hs = 0.49999f * sc;
+            const h2v hv[4] = {a0, a1, a2, a3};
+            float t[8], cf[8], R[8];
             bool near_tie = false;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                t[e] = v[e] - mn;
-                const float q = t[e] * inv;
-                cf[e] = rintf(q);
-                near_tie |= fabsf(q - cf[e]) > 0.49999f;
+                t[e] = fmaf((float)hv[e >> 1][e & 1], sx, -mn);   // = x 2^ex - mn, one rounding
+                cf[e] = rintf(t[e] * inv);
+                R[e] = fmaf(-cf[e], sc, t[e]);
+                near_tie |= fabsf(R[e]) > hs;
             }
             if (__ballot(near_tie) != 0ull && near_tie) {
-                // within 1e-5 of a half-integer: round the exact quotient
+                // round the exact quotient
 #pragma unroll
-                for (int e = 0; e < 8; ++e) cf[e] = rintf(t[e] / sc);
+                for (int e = 0; e < 8; ++e) {
+                    cf[e] = rintf(t[e] / sc);
+                    R[e] = fmaf(-cf[e], sc, t[e]);
+                }
             }
             // 0 <= t <= mx - mn, so rint(t / sc) already lies in [0, 2^b - 1]
             uint32_t word = 0;
@@ -838,9 +890,6 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                         fmaf(cf[4 * i + 3], 64.0f, fmaf(cf[4 * i + 2], 16.0f, fmaf(cf[4 * i + 1], 4.0f, cf[4 * i]))),
                         i, word);
             }
-            float R[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) R[e] = fmaf(-cf[e], sc, t[e]);
             if (valid) {
                 if (bits == 4)
                     st_at<uint32_t>(codes_m, urow * (D / 2) + colq * 4, word);
@@ -853,13 +902,13 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 }
             }
             if (LR) {
-                // fp16 hi + lo of R * 2^ex, row-major into the slab
+                // fp16 hi (toward zero) + lo of R * 2^ex, row-major into the slab
                 uint32_t hw[4], lw[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const auto h2 = __builtin_amdgcn_cvt_pkrtz(R[2 * i], R[2 * i + 1]);
-                    const auto l2 = __builtin_amdgcn_cvt_pkrtz(R[2 * i] - (float)h2[0],
-                                                               R[2 * i + 1] - (float)h2[1]);
+                    const auto l2 = __builtin_amdgcn_cvt_pkrtz(fmaf((float)h2[0], m1, R[2 * i]),
+                                                               fmaf((float)h2[1], m1, R[2 * i + 1]));
                     hw[i] = __builtin_bit_cast(uint32_t, h2);
                     lw[i] = __builtin_bit_cast(uint32_t, l2);
                 }
@@ -1041,7 +1090,8 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
     const int64_t mm = blockIdx.x / nblk;
-    const int r0 = (int)(blockIdx.x % nblk) * ROWS_WG + wv * ROWS_W;
+    const int blk = (int)(blockIdx.x % nblk);
+    const int r0 = blk * ROWS_WG + wv * ROWS_W;
     const int c0 = CPL * q;                   // first column of this lane
     // per-matrix bases; 32-bit offsets below (rows * D * 2 < 2^32)
     const unsigned char* xb = reinterpret_cast<const unsigned char*>(
