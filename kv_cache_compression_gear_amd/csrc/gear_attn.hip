@@ -121,7 +121,8 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
-    const int pair = blockIdx.x / a.splits, split = blockIdx.x % a.splits;
+    const int nsp = a.splits - a.split0;   // splits [split0, splits) of every (b, kv-head)
+    const int pair = blockIdx.x / nsp, split = a.split0 + blockIdx.x % nsp;
     const int b = pair / a.Hkv, hk = pair % a.Hkv;
     const int pt = a.prompt.count ? a.prompt.chunks * a.prompt.p.rows : 0;
     const int N = pt + a.fills.count * a.fills.p.rows + a.buf_len;
@@ -517,7 +518,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) s_red[(wv * G + h) * D + colq * 8 + e] = acc[h][e];
     }
     __syncthreads();
-    float* part = a.partial + (size_t)blockIdx.x * G * (D + 2);
+    float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
     for (int i = tid; i < G * D; i += kThreads) {
         const int h = i / D, j = i % D;
         part[h * (D + 2) + j] = s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j] +
@@ -526,6 +527,368 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     if (tid < G) {
         part[tid * (D + 2) + D] = n > 0 ? s_stat[tid] : -INFINITY;
         part[tid * (D + 2) + D + 1] = n > 0 ? s_stat[G + tid] : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Whole prompt splits: kTPS tokens inside one compressed K matrix and its V
+// matrix, at most kFastGroups quantization groups per token.  The same sums
+// as attn_split_kernel, organised around two rounds of loads so that a
+// workgroup waits on memory twice instead of once per batch of tokens:
+//   1. q, the K codes (registers), K's scales, zeros and A rows, both
+//      matrices' row pointers and both B matrices (LDS);
+//   2. issued before the K scores are computed and consumed after: the V
+//      codes, V's scales, zeros and A rows, and both matrices' CSR entries
+//      (a contiguous range, loaded coalesced).
+// 8 waves; wave w takes tokens [32 w, 32 w + 32), RPS per step.  The sparse
+// V terms p_t s_tj go to a per-wave LDS row (one LDS add per entry), added
+// to the wave's sums at the end.
+constexpr int kFastCap = 2048;     // outliers of one matrix split staged
+constexpr int kFastGroups = 2;     // quantization groups per token staged
+constexpr int kFastWaves = 8;
+constexpr int kFastThreads = 64 * kFastWaves;
+
+// codes of 8 consecutive columns as floats (code e in bits [BITS e, BITS e + BITS))
+template <int BITS>
+__device__ __forceinline__ void unpack8(uint32_t w, float (&cf)[8]) {
+    if (BITS == 4) {
+        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            cf[2 * i] = (float)((lo >> (8 * i)) & 0xffu);
+            cf[2 * i + 1] = (float)((hi >> (8 * i)) & 0xffu);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cf[e] = (float)((w >> (2 * e)) & 3u);
+    }
+}
+
+template <int D, int G, int BITS>
+__global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a) {
+    constexpr int LPR = D / 8, RPS = 64 / LPR, TPW = kTPS / kFastWaves, SPW = TPW / RPS;
+    constexpr int CPT = kFastCap / kFastThreads;      // staged CSR entries per thread
+    constexpr int ROWB = D * BITS / 8;                 // code bytes per token
+    constexpr int kVsBytes = 4 * G * D * 4;           // sparse V sums of the 4 token waves
+    constexpr int kRedBytes = 4 * G * D * 4;
+    constexpr int kCsrBytes = kRedBytes > kFastCap * 4 ? kRedBytes : kFastCap * 4;
+    static_assert(kTPS * kFastGroups / 4 <= 128 && kTPS * kMaxRank / 4 <= kFastThreads &&
+                  D * kMaxRank / 4 <= kFastThreads, "one float4 per thread stages the side data");
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    __shared__ float s_q[G * D];
+    __shared__ float s_sc[kTPS * G];                   // scores, then probabilities
+    __shared__ __attribute__((aligned(16))) float s_gs[kTPS * kFastGroups];
+    __shared__ __attribute__((aligned(16))) float s_gz[kTPS * kFastGroups];
+    __shared__ __attribute__((aligned(16))) float s_a[kTPS * kMaxRank];
+    __shared__ float s_bkt[kMaxRank * D];              // B_K transposed: [c][j]
+    __shared__ __attribute__((aligned(16))) float s_bv[D * kMaxRank];
+    __shared__ float s_qb[G * kMaxRank];
+    __shared__ int32_t s_rk[kTPS + 1];
+    __shared__ int32_t s_rv[kTPS + 1];
+    // CSR entries (then the cross-wave sums), sparse V sums
+    __shared__ __attribute__((aligned(16))) unsigned char s_big[kCsrBytes + kVsBytes];
+    __shared__ float s_wm[4 * G];                      // per-wave max and sum (token waves 0..3)
+    __shared__ float s_ws[4 * G];
+    __shared__ float s_pa[kFastWaves * G * kMaxRank];
+    uint32_t* s_cv = reinterpret_cast<uint32_t*>(s_big);
+    float* s_vs = reinterpret_cast<float*>(s_big + kCsrBytes);
+    float* s_red = reinterpret_cast<float*>(s_big);
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int colq = lane % LPR, rl = lane / LPR;
+    const int pair = blockIdx.x / a.split0, split = blockIdx.x % a.split0;
+    const int b = pair / a.Hkv, hk = pair % a.Hkv;
+    const int t0 = split * kTPS;
+    const Piece pc = find_piece(a, b, hk, t0, t0 + kTPS);
+    const Packed& p = pc.p;
+    const int r = p.rank, gl = p.group / 8, ngr = D / p.group;
+    const uint32_t kk = (uint32_t)p.k;
+    const size_t mrk = (size_t)pc.mk * p.rows + pc.row0, mrv = (size_t)pc.mv * p.rows + pc.row0;
+    // this lane's first token; later steps add RPS tokens
+    const int tok0 = wv * TPW + rl;
+    const uint32_t coff0 = (uint32_t)(tok0 * ROWB + colq * BITS);
+    const int gi = colq / gl;
+
+    // ---------------- round 1
+    float q[G][8], qs[G];
+    {
+        const uint16_t* qb = a.q + ((size_t)b * a.Hq + hk * G) * D;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const uint4 w = *reinterpret_cast<const uint4*>(qb + h * D + colq * 8);
+            const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+            qs[h] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                q[h][e] = h2f(w4[e >> 1] >> (16 * (e & 1)));
+                qs[h] += q[h][e];
+            }
+        }
+        for (int i = tid; i < G * D; i += kFastThreads) s_q[i] = h2f(qb[i]);
+    }
+    uint32_t wk[SPW];
+    const unsigned char* ck = p.codes + mrk * ROWB;
+    const unsigned char* cvb = p.codes + mrv * ROWB;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+        wk[s] = BITS == 4 ? ld_at<uint32_t>(ck, coff0 + s * RPS * ROWB)
+                          : (uint32_t)ld_at<uint16_t>(ck, coff0 + s * RPS * ROWB);
+    // scales and zeros: kTPS * ngr floats each (<= 512: one float4 per thread,
+    // threads [0, 128) scales, [128, 256) zeros); A: kTPS * r floats (<= 2048,
+    // one float4 per thread)
+    const int ng4 = kTPS * ngr / 4, na4 = kTPS * r / 4, nb4 = D * r / 4;
+    const f4v z4 = {0.f, 0.f, 0.f, 0.f};
+    struct Side {
+        f4v gsz, av;
+    };
+    auto load_side = [&](size_t mrow) {
+        const int i = tid & 127;
+        const float* src = (tid < 128 ? p.scale : p.zero) + mrow * ngr;
+        Side sd;
+        sd.gsz = (tid < 256 && i < ng4) ? reinterpret_cast<const f4v*>(src)[i] : z4;
+        sd.av = tid < na4 ? reinterpret_cast<const f4v*>(p.A + mrow * r)[tid] : z4;
+        return sd;
+    };
+    auto store_side = [&](const Side sd) {
+        const int i = tid & 127;
+        if (tid < 256 && i < ng4) reinterpret_cast<f4v*>(tid < 128 ? s_gs : s_gz)[i] = sd.gsz;
+        if (tid < na4) reinterpret_cast<f4v*>(s_a)[tid] = sd.av;
+    };
+    {
+        const Side sk = load_side(mrk);
+        const int32_t* rpk = p.row_ptr + (size_t)pc.mk * (p.rows + 1) + pc.row0;
+        const int32_t* rpv = p.row_ptr + (size_t)pc.mv * (p.rows + 1) + pc.row0;
+        // threads [0, kTPS] read K's row pointers, [256, 256 + kTPS] V's
+        const int ri = tid & 255;
+        const int32_t rp0 = (tid < 256 ? rpk : rpv)[ri];
+        const int32_t rp1 = ri == 0 ? (tid < 256 ? rpk : rpv)[kTPS] : 0;
+        const f4v bk = tid < nb4 ? reinterpret_cast<const f4v*>(p.B + (size_t)pc.mk * D * r)[tid] : z4;
+        const f4v bv = tid < nb4 ? reinterpret_cast<const f4v*>(p.B + (size_t)pc.mv * D * r)[tid] : z4;
+        store_side(sk);
+        int32_t* srp = tid < 256 ? s_rk : s_rv;
+        srp[ri] = min(max(rp0, 0), (int)kk);
+        if (ri == 0) srp[kTPS] = min(max(rp1, 0), (int)kk);
+        if (tid < nb4) {
+            reinterpret_cast<f4v*>(s_bv)[tid] = bv;
+            // element 4 tid + i of B_K (row-major [j][c]) into [c][j]
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = 4 * tid + i;
+                s_bkt[(f % r) * D + f / r] = bk[i];
+            }
+        }
+        for (int i = tid; i < kVsBytes / 16; i += kFastThreads)
+            reinterpret_cast<uint4*>(s_vs)[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+
+    // ---------------- round 2 (issued now, consumed later)
+    const int beg_k = s_rk[0], cnt_k = max(s_rk[kTPS] - beg_k, 0);
+    const int beg_v = s_rv[0], cnt_v = max(s_rv[kTPS] - beg_v, 0);
+    const bool stg_k = cnt_k <= kFastCap, stg_v = cnt_v <= kFastCap;
+    const uint16_t* colk = p.col + (size_t)pc.mk * kk;
+    const uint16_t* valk = p.val + (size_t)pc.mk * kk;
+    const uint16_t* colv = p.col + (size_t)pc.mv * kk;
+    const uint16_t* valv = p.val + (size_t)pc.mv * kk;
+    uint32_t ek[CPT], ev[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int i = tid + j * kFastThreads;
+        ek[j] = (stg_k && i < cnt_k) ? ((uint32_t)colk[beg_k + i] | ((uint32_t)valk[beg_k + i] << 16)) : 0u;
+        ev[j] = (stg_v && i < cnt_v) ? ((uint32_t)colv[beg_v + i] | ((uint32_t)valv[beg_v + i] << 16)) : 0u;
+    }
+    uint32_t wvv[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+        wvv[s] = BITS == 4 ? ld_at<uint32_t>(cvb, coff0 + s * RPS * ROWB)
+                           : (uint32_t)ld_at<uint16_t>(cvb, coff0 + s * RPS * ROWB);
+    const Side sv = load_side(mrv);
+
+    // (B_K^T q)[h][c]: 16 lanes per (h, c), 8 columns each, summed over the
+    // lane row
+    for (int i = tid; i < G * kMaxRank * 16; i += kFastThreads) {
+        const int hc = i / 16, j0 = (i % 16) * (D / 16);
+        const int h = hc / kMaxRank, c = hc % kMaxRank;
+        float v = 0.0f;
+        if (c < r) {
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) v = fmaf(s_q[h * D + j0 + j], s_bkt[c * D + j0 + j], v);
+        }
+        v = row_allreduce<16>(v);
+        if ((i % 16) == 0) s_qb[hc] = v;
+    }
+    __syncthreads();
+
+    // ---------------- phase 1: dense part of q . K^_t
+    float qbl[G];   // (B^T q)[colq] in the lanes colq < r
+#pragma unroll
+    for (int h = 0; h < G; ++h) qbl[h] = colq < r ? s_qb[h * kMaxRank + colq] : 0.0f;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        const int tok = tok0 + s * RPS;
+        const float scv = s_gs[tok * ngr + gi], zpv = s_gz[tok * ngr + gi];
+        const float av = colq < r ? s_a[tok * r + colq] : 0.0f;
+        float cf[8];
+        unpack8<BITS>(wk[s], cf);
+        float part[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) part[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], cf[e], part[h]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float v = row_allreduce<LPR>(fmaf(av, qbl[h], fmaf(scv, part[h], zpv * qs[h])));
+            if (colq == 0) s_sc[tok * G + h] = v;
+        }
+    }
+    // K's CSR entries into LDS
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+        if (stg_k && tid + j * kFastThreads < cnt_k) s_cv[tid + j * kFastThreads] = ek[j];
+    __syncthreads();
+
+    // ---------------- sparse part (one thread per token, waves 0..3), softmax
+    float pr[G];
+    if (tid < kTPS) {
+        float add[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) add[h] = 0.0f;
+        for (int k = s_rk[tid]; k < s_rk[tid + 1]; ++k) {
+            const uint32_t e = stg_k ? s_cv[k - beg_k] : ((uint32_t)colk[k] | ((uint32_t)valk[k] << 16));
+            const int cj = (int)(e & (D - 1));
+            const float v = h2f(e >> 16);
+#pragma unroll
+            for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            pr[h] = a.sm_scale * (s_sc[tid * G + h] + add[h]);
+            float m = pr[h];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            if (lane == 0) s_wm[wv * G + h] = m;
+        }
+    }
+    __syncthreads();
+    if (tid < kTPS) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float m = fmaxf(fmaxf(s_wm[h], s_wm[G + h]), fmaxf(s_wm[2 * G + h], s_wm[3 * G + h]));
+            pr[h] = expf(pr[h] - m);
+            s_sc[tid * G + h] = pr[h];
+            float sm = pr[h];
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) sm += __shfl_xor(sm, off, 64);
+            if (lane == 0) s_ws[wv * G + h] = sm;
+        }
+    }
+    // V's side data and CSR entries replace K's
+    store_side(sv);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+        if (stg_v && tid + j * kFastThreads < cnt_v) s_cv[tid + j * kFastThreads] = ev[j];
+    __syncthreads();
+    // sparse V terms p_t s_tj of token tid into its wave's LDS row (entries in
+    // CSR order, one LDS add each; the wave's adds execute in program order)
+    if (tid < kTPS) {
+        float* vs = s_vs + wv * G * D;
+        for (int k = s_rv[tid]; k < s_rv[tid + 1]; ++k) {
+            const uint32_t e = stg_v ? s_cv[k - beg_v] : ((uint32_t)colv[k] | ((uint32_t)valv[k] << 16));
+            const float v = h2f(e >> 16);
+#pragma unroll
+            for (int h = 0; h < G; ++h) atomicAdd(&vs[h * D + (e & (D - 1))], pr[h] * v);
+        }
+    }
+
+    // ---------------- phase 2: sum_t p_t V^_t = sum_t (p_t scale_t) codes_t
+    // + sum_t p_t zero_t + sparse + low-rank
+    float acc[G][8], pa[G], pz[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        pa[h] = 0.0f;
+        pz[h] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    }
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+        const int tok = tok0 + s * RPS;
+        const float scv = s_gs[tok * ngr + gi], zpv = s_gz[tok * ngr + gi];
+        const float av = colq < r ? s_a[tok * r + colq] : 0.0f;
+        float cf[8];
+        unpack8<BITS>(wvv[s], cf);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float pp = s_sc[tok * G + h];
+            pa[h] = fmaf(pp, av, pa[h]);
+            pz[h] = fmaf(pp, zpv, pz[h]);
+            const float ps = pp * scv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ps, cf[e], acc[h][e]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] += pz[h];
+    // low-rank part: acc += B_V (sum_t p_t A_t); the per-rank sums over the
+    // workgroup's tokens are added by one row group
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h) pa[h] += __shfl_xor(pa[h], off, 64);
+    if (rl == 0 && colq < r) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_pa[(wv * G + h) * kMaxRank + colq] = pa[h];
+    }
+    __syncthreads();
+    if (wv == 0 && rl == 0) {
+        for (int c = 0; c < r; ++c) {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float tot = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kFastWaves; ++w) tot += s_pa[(w * G + h) * kMaxRank + c];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(tot, s_bv[(colq * 8 + e) * r + c], acc[h][e]);
+            }
+        }
+    }
+    // reduce over the row groups of the wave, then over the waves: waves 4..7
+    // hand theirs to waves 0..3, which hand the sums to the store
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+    if (rl == 0 && wv >= 4) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[((wv - 4) * G + h) * D + colq * 8 + e] = acc[h][e];
+    }
+    __syncthreads();
+    if (rl == 0 && wv < 4) {
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s_red[(wv * G + h) * D + colq * 8 + e] += acc[h][e];
+    }
+    __syncthreads();
+    float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
+    for (int i = tid; i < G * D; i += kFastThreads) {
+        const int h = i / D, j = i % D;
+        part[h * (D + 2) + j] = (s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j]) +
+                                (s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j]) +
+                                ((s_vs[(0 * G + h) * D + j] + s_vs[(1 * G + h) * D + j]) +
+                                 (s_vs[(2 * G + h) * D + j] + s_vs[(3 * G + h) * D + j]));
+    }
+    if (tid < G) {
+        part[tid * (D + 2) + D] = fmaxf(fmaxf(s_wm[tid], s_wm[G + tid]), fmaxf(s_wm[2 * G + tid], s_wm[3 * G + tid]));
+        part[tid * (D + 2) + D + 1] = s_ws[tid] + s_ws[G + tid] + s_ws[2 * G + tid] + s_ws[3 * G + tid];
     }
 }
 
@@ -579,13 +942,30 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
     }
 }
 
+// Splits [0, split0) go to attn_prompt_kernel: the prompt's splits when every
+// one of them lies inside one compressed chunk and the token's groups fit
+// its staging; the rest (fills, the fp16 buffer, other shapes) to
+// attn_split_kernel.
 template <int D, int G>
-hipError_t launch_dg(const AttnArgs& a, hipStream_t st) {
-    const unsigned grid = (unsigned)(a.B * a.Hkv * a.splits);
+hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
+    AttnArgs a = a0;
+    a.split0 = 0;
+    if (a.prompt.count == 1 && a.tokens_per_split == kTPS && a.prompt.p.rows % kTPS == 0 &&
+        D / a.prompt.p.group <= kFastGroups)
+        a.split0 = min(a.splits, a.prompt.chunks * a.prompt.p.rows / kTPS);
+    const unsigned pairs = (unsigned)(a.B * a.Hkv);
     hipError_t e;
     {
         Timed t(kKAttnSplit, st);
-        hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(grid), dim3(kThreads), 0, st, a);
+        if (a.split0 > 0) {
+            if (a.prompt.p.bits == 4)
+                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4>), dim3(pairs * a.split0), dim3(kFastThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2>), dim3(pairs * a.split0), dim3(kFastThreads), 0, st, a);
+        }
+        if (a.splits > a.split0)
+            hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(pairs * (a.splits - a.split0)), dim3(kThreads),
+                               0, st, a);
         e = hipGetLastError();
     }
     if (e != hipSuccess) return e;

@@ -123,6 +123,7 @@ struct AttnArgs {
     float* partial;        // workspace: [B*Hkv][splits][G][d + 2]
     int32_t splits;
     int32_t tokens_per_split;
+    int32_t split0;        // splits [0, split0) are whole prompt splits (fast kernel)
 };
 size_t attn_workspace_bytes(int B, int Hkv, int Hq, int d, int64_t tokens, int* splits,
                             int* tokens_per_split);

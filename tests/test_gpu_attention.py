@@ -41,6 +41,12 @@ def _new_cache(B, Hkv, Hq, d, pp, fp, n_prompt, nb, max_new):
     ("gqa4_prompt_ragged", 2, 2, 8, 128, 700, P(4, 128, 20000, 4, 3)),
     ("gqa8_chunked", 1, 2, 16, 128, 1024, P(4, 128, 10000, 4, 3, chunk_tokens=512)),
     ("gqa2_2bit", 2, 2, 4, 128, 300, P(2, 64, 50000, 8, 4)),
+    # whole 256-token prompt splits: two groups per token, rank 8, 2-bit codes
+    ("whole_splits_2bit_r8", 1, 2, 4, 128, 512, P(2, 64, 50000, 8, 4)),
+    # more outliers in a split than the prompt kernel stages in LDS
+    ("whole_splits_dense_outliers", 1, 2, 2, 128, 512, P(4, 128, 100000, 4, 2)),
+    # head_dim 64, two groups per token, no low-rank term
+    ("whole_splits_d64_r0", 2, 2, 2, 64, 768, P(4, 32, 20000, 0, 0)),
 ])
 def test_decode_attention_over_compressed_prompt(name, B, Hkv, Hq, d, n, pp):
     _say(f"[attention] {name}")
