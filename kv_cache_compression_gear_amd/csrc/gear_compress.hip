@@ -1074,6 +1074,17 @@ struct BoolTag { static constexpr bool value = B; };
 // lane groups q, so CPL instructions cover all D columns and no cross-lane sum
 // is needed.  The output lanes n = l % 16 < r hold A[row][n] for the rows
 // 4 (l / 16) + 0..3 of the step.
+// byte I of x as a float, one instruction (v_cvt_f32_ubyteI)
+template <int I>
+__device__ __forceinline__ float ubyte_f(uint32_t x) {
+    float f;
+    if (I == 0) asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(x));
+    else if (I == 1) asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(x));
+    else if (I == 2) asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(x));
+    else asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(x));
+    return f;
+}
+
 template <int D, int RK>
 __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     constexpr int CPL = D / 4;                // columns per lane
@@ -1086,7 +1097,6 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const int rows = o.rows, rank = o.rank, bits = o.bits;
     const int g = o.group, ngr = D / g;
     const int ngl = g >= CPL ? 1 : CPL / g;   // groups within a lane's columns (<= 4)
-    const uint32_t cmask = (1u << bits) - 1u;
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
     const int64_t mm = blockIdx.x / nblk;
@@ -1104,54 +1114,67 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     for (int jj = 0; jj < CPL; ++jj)
         Bv[jj] = rr < RK ? a.bf[((size_t)mm * D + c0 + jj) * RK + rr] : 0.0f;
 
-    float tf = __builtin_inff(), tf_lo = __builtin_inff();
+    // outlier rule on keys (|x| bit patterns): key > thrk, thrk = T - 1 in the
+    // rows that take all ties at key T, T elsewhere, 0x7fff without outliers;
+    // plus, in the one row block whose quota splits the ties, the ties its
+    // CSR entries hold
+    int thr_all = 0x7fff, thr_none = 0x7fff, tk = -1;
     int r_all = rows, r_none = rows;
     if (kk > 0) {
         const uint32_t* sel = a.sel + (size_t)mm * kSelStride;
-        const uint32_t tkey = sel[0];
-        tf = h2f(tkey);
-        tf_lo = tkey > 0 ? h2f(tkey - 1) : -1.0f;
+        tk = (int)sel[0];
+        thr_all = tk - 1;
+        thr_none = tk;
         tie_rows(sel, rows, r_all, r_none);
     }
     const bool wave_split = r0 < r_none && r0 + ROWS_W > r_all;   // wave-uniform
     const int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     const uint16_t* cm = o.col + (size_t)mm * kk;
     float* Am = o.A + (size_t)mm * rows * rank;
+    float one = 1.0f;   // opaque 1: keeps x - zero a single mixed fma
+    asm volatile("" : "+s"(one));
 
-    uint4 xr[1][NX];
-    uint4 cw[1];
-    float sc[1][4], zp[1][4];
-    auto load = [&](int buf, int s) {
+    struct Buf {
+        uint4 x[NX];
+        uint4 cw;
+        float sc[4], zp[4];
+    };
+    auto load = [&](int s) {
+        Buf bf;
         const int row = r0 + s * 16 + rr;
         const uint32_t rc = (uint32_t)min(row, rows - 1);   // always a valid address
 #pragma unroll
-        for (int c = 0; c < NX; ++c) xr[buf][c] = ld_at<uint4>(xb, (rc * D + c0 + 8 * c) * 2);
+        for (int c = 0; c < NX; ++c) bf.x[c] = ld_at<uint4>(xb, (rc * D + c0 + 8 * c) * 2);
         const uint32_t cbytes = (uint32_t)(CPL * bits / 8);  // 16, 8 or 4
         const uint32_t coff = rc * (D * bits / 8) + (uint32_t)(c0 * bits / 8);
         if (cbytes == 16) {
-            cw[buf] = ld_at<uint4>(cb, coff);
+            bf.cw = ld_at<uint4>(cb, coff);
         } else if (cbytes == 8) {
             const uint2 v = ld_at<uint2>(cb, coff);
-            cw[buf] = make_uint4(v.x, v.y, 0u, 0u);
+            bf.cw = make_uint4(v.x, v.y, 0u, 0u);
         } else {
-            cw[buf] = make_uint4(ld_at<uint32_t>(cb, coff), 0u, 0u, 0u);
+            bf.cw = make_uint4(ld_at<uint32_t>(cb, coff), 0u, 0u, 0u);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            bf.sc[t] = 0.0f;
+            bf.zp[t] = 0.0f;
             if (t < ngl) {
                 const uint32_t go = (rc * ngr + (c0 + t * g) / g) * 4;
-                sc[buf][t] = ld_at<float>(scb, go);
-                zp[buf][t] = ld_at<float>(zpb, go);
+                bf.sc[t] = ld_at<float>(scb, go);
+                bf.zp[t] = ld_at<float>(zpb, go);
             }
         }
+        return bf;
     };
-    auto compute = [&](int buf, int s, auto split_tag, auto bits4_tag, auto one_group_tag) {
+    auto compute = [&](const Buf& bf, int s, auto split_tag, auto bits4_tag, auto one_group_tag) {
         constexpr bool SPLIT = decltype(split_tag)::value;
         constexpr bool BITS4 = decltype(bits4_tag)::value;      // else 2-bit codes
         constexpr bool ONEG = decltype(one_group_tag)::value;   // one group per lane
         const int row = r0 + s * 16 + rr;
         const bool valid = row < rows;
-        const float th = row < r_all ? tf_lo : tf;
+        const int thrk = row < r_all ? thr_all : thr_none;
+        const uint32_t t2 = ((uint32_t)thrk & 0xffffu) * 0x10001u;   // thrk in both halves
         // ties of the split block taken by this row: bits of tm (column c0 + j)
         uint32_t tm = 0u;
         if (SPLIT) {
@@ -1159,7 +1182,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
 #pragma unroll
             for (int c = 0; c < NX; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) any_eq |= fabsf(h2f(half_of(xr[buf][c], e))) == tf;
+                for (int e = 0; e < 8; ++e) any_eq |= (int)(half_of(bf.x[c], e) & 0x7fffu) == tk;
             any_eq = any_eq && valid && row >= r_all && row < r_none;
             if (__ballot(any_eq) != 0ull && any_eq) {
                 const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
@@ -1171,25 +1194,43 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
             }
         }
         f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        const uint32_t cwd[4] = {cw[buf].x, cw[buf].y, cw[buf].z, cw[buf].w};
+        const uint32_t cwd[4] = {bf.cw.x, bf.cw.y, bf.cw.z, bf.cw.w};
 #pragma unroll
         for (int c = 0; c < NX; ++c) {
+            // D = X - S on the fp16 bits: the outliers become +0
+            const uint32_t d[4] = {bf.x[c].x, bf.x[c].y, bf.x[c].z, bf.x[c].w};
+            uint32_t dm[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const s2v r = __builtin_bit_cast(s2v, t2) - __builtin_bit_cast(s2v, d[i] & 0x7fff7fffu);
+                uint32_t m = __builtin_bit_cast(uint32_t, r >> (s2v){15, 15});
+                if (SPLIT)
+                    m |= (((tm >> (8 * c + 2 * i)) & 1u) ? 0xffffu : 0u) |
+                         (((tm >> (8 * c + 2 * i + 1)) & 1u) ? 0xffff0000u : 0u);
+                dm[i] = d[i] & ~m;
+            }
+            float cf[8];
+            if (BITS4) {
+                const uint32_t lo = cwd[c] & 0x0F0F0F0Fu, hi = (cwd[c] >> 4) & 0x0F0F0F0Fu;
+                cf[0] = ubyte_f<0>(lo), cf[2] = ubyte_f<1>(lo), cf[4] = ubyte_f<2>(lo), cf[6] = ubyte_f<3>(lo);
+                cf[1] = ubyte_f<0>(hi), cf[3] = ubyte_f<1>(hi), cf[5] = ubyte_f<2>(hi), cf[7] = ubyte_f<3>(hi);
+            } else {
+                const uint32_t w = cwd[c >> 1] >> (16 * (c & 1));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) cf[e] = (float)((w >> (2 * e)) & 3u);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int jj = 8 * c + e;
-                const float xf = h2f(half_of(xr[buf][c], e));
-                bool out = fabsf(xf) > th;
-                if (SPLIT) out = out || ((tm >> jj) & 1u);
-                const float v = out ? 0.0f : xf;
-                constexpr int BB = BITS4 ? 4 : 2;
-                const float code = (float)((cwd[(jj * BB) >> 5] >> ((jj * BB) & 31)) & (BITS4 ? 15u : 3u));
-                float scv = sc[buf][0], zpv = zp[buf][0];
+                float scv = bf.sc[0], zpv = bf.zp[0];
                 if (!ONEG) {   // groups of 8 or 16 columns: group of column jj
                     const int t = jj / (g == 8 ? 8 : 16);
-                    scv = t == 0 ? sc[buf][0] : t == 1 ? sc[buf][1] : t == 2 ? sc[buf][2] : sc[buf][3];
-                    zpv = t == 0 ? zp[buf][0] : t == 1 ? zp[buf][1] : t == 2 ? zp[buf][2] : zp[buf][3];
+                    scv = t == 0 ? bf.sc[0] : t == 1 ? bf.sc[1] : t == 2 ? bf.sc[2] : bf.sc[3];
+                    zpv = t == 0 ? bf.zp[0] : t == 1 ? bf.zp[1] : t == 2 ? bf.zp[2] : bf.zp[3];
                 }
-                const float R = fmaf(-code, scv, v - zpv);
+                // R = (x or 0) - zero - code * scale; x - zero in one mixed fma
+                const float xz = fmaf(h2f(dm[e >> 1] >> (16 * (e & 1))), one, -zpv);
+                const float R = fmaf(-cf[e], scv, xz);
                 acc = __builtin_amdgcn_mfma_f32_16x16x4f32(R, Bv[jj], acc, 0, 0, 0);
             }
         }
@@ -1201,11 +1242,13 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
             }
         }
     };
+    // two steps in flight: the next step's loads are issued before this
+    // step's arithmetic
     auto run = [&](auto split_tag, auto bits4_tag, auto one_group_tag) {
 #pragma unroll 1
         for (int s = 0; s < kLrSteps; ++s) {
-            load(0, s);
-            compute(0, s, split_tag, bits4_tag, one_group_tag);
+            const Buf cur = load(s);
+            compute(cur, s, split_tag, bits4_tag, one_group_tag);
         }
     };
     auto run2 = [&](auto split_tag) {
