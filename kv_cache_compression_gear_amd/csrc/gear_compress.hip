@@ -1073,7 +1073,9 @@ struct BoolTag { static constexpr bool value = B; };
 // CPL (l / 16); the j-th instruction contracts column CPL q + j of the four
 // lane groups q, so CPL instructions cover all D columns and no cross-lane sum
 // is needed.  The output lanes n = l % 16 < r hold A[row][n] for the rows
-// 4 (l / 16) + 0..3 of the step.
+// 4 (l / 16) + 0..3 of the step.  X is loaded row-contiguously (each load
+// instruction covers whole rows) and regrouped into that layout through a
+// per-wave LDS tile whose 16-byte chunks are XOR-swizzled by row.
 // byte I of x as a float, one instruction (v_cvt_f32_ubyteI)
 template <int I>
 __device__ __forceinline__ float ubyte_f(uint32_t x) {
@@ -1134,6 +1136,12 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     float one = 1.0f;   // opaque 1: keeps x - zero a single mixed fma
     asm volatile("" : "+s"(one));
 
+    // per-wave tile of 16 rows of X: [row][chunk ^ swizzle(row)], 16-byte chunks
+    constexpr int CPR = D / 8;                // chunks per row (16 or 8)
+    constexpr int RPI = 64 / CPR;             // rows per load instruction (4 or 8)
+    __shared__ __attribute__((aligned(16))) uint4 s_x[4][16 * CPR];
+    uint4* tile = s_x[wv];
+    auto swz = [](int row, int ch) { return ch ^ (row & (CPR - 1)); };
     struct Buf {
         uint4 x[NX];
         uint4 cw;
@@ -1143,8 +1151,13 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
         Buf bf;
         const int row = r0 + s * 16 + rr;
         const uint32_t rc = (uint32_t)min(row, rows - 1);   // always a valid address
+        // X: instruction c covers rows RPI c .. RPI c + RPI - 1 of the step, lane
+        // l chunk l % CPR of row RPI c + l / CPR (NX = 16 / RPI instructions)
 #pragma unroll
-        for (int c = 0; c < NX; ++c) bf.x[c] = ld_at<uint4>(xb, (rc * D + c0 + 8 * c) * 2);
+        for (int c = 0; c < NX; ++c) {
+            const uint32_t xr = (uint32_t)min(r0 + s * 16 + RPI * c + lane / CPR, rows - 1);
+            bf.x[c] = ld_at<uint4>(xb, (xr * D + 8 * (lane % CPR)) * 2);
+        }
         const uint32_t cbytes = (uint32_t)(CPL * bits / 8);  // 16, 8 or 4
         const uint32_t coff = rc * (D * bits / 8) + (uint32_t)(c0 * bits / 8);
         if (cbytes == 16) {
@@ -1175,6 +1188,19 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
         const bool valid = row < rows;
         const int thrk = row < r_all ? thr_all : thr_none;
         const uint32_t t2 = ((uint32_t)thrk & 0xffffu) * 0x10001u;   // thrk in both halves
+        // regroup X through the wave's tile: lane (rr, q) takes row rr, chunks
+        // CPL q / 8 .. CPL q / 8 + NX - 1 (LDS operations of a wave execute in
+        // order; the tile is rewritten only after this step's reads)
+        uint4 xq[NX];
+#pragma unroll
+        for (int c = 0; c < NX; ++c) {
+            const int trow = RPI * c + lane / CPR;
+            tile[trow * CPR + swz(trow, lane % CPR)] = bf.x[c];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int c = 0; c < NX; ++c) xq[c] = tile[rr * CPR + swz(rr, (c0 / 8) + c)];
+        __builtin_amdgcn_wave_barrier();
         // ties of the split block taken by this row: bits of tm (column c0 + j)
         uint32_t tm = 0u;
         if (SPLIT) {
@@ -1182,7 +1208,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
 #pragma unroll
             for (int c = 0; c < NX; ++c)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) any_eq |= (int)(half_of(bf.x[c], e) & 0x7fffu) == tk;
+                for (int e = 0; e < 8; ++e) any_eq |= (int)(half_of(xq[c], e) & 0x7fffu) == tk;
             any_eq = any_eq && valid && row >= r_all && row < r_none;
             if (__ballot(any_eq) != 0ull && any_eq) {
                 const int beg = max(rp[row], 0), end = min(rp[row + 1], (int32_t)kk);
@@ -1198,7 +1224,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
 #pragma unroll
         for (int c = 0; c < NX; ++c) {
             // D = X - S on the fp16 bits: the outliers become +0
-            const uint32_t d[4] = {bf.x[c].x, bf.x[c].y, bf.x[c].z, bf.x[c].w};
+            const uint32_t d[4] = {xq[c].x, xq[c].y, xq[c].z, xq[c].w};
             uint32_t dm[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
