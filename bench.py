@@ -12,16 +12,18 @@ One step = one pass of the whole path over one 7B-shaped attention layer
 Inputs are synthetic, seeded, already resident in HBM.  `value` is fp16 KV
 bytes per step / step time (GB/s).  Prints one JSON line.
 
-The `roofline` object is for the kernel with the largest share of the timed
-region, timed live with HIP events recorded by the library on the launch
-stream (gear_timing_*); `traffic` is its measured HBM bytes per launch from
+The K timed steps run uninstrumented; K further steps then run with the
+library's per-kernel HIP events on (gear_timing_*) and per-phase events, which
+give `phases_ms`, `kernels_ms` and the `roofline` object: the kernel with the
+largest share of a step, its launch time measured live on the launch stream.
+`traffic` is its measured HBM bytes per launch from
 the committed rocprofv3 counter summary under profiles/, when that summary was
 taken from the current kernel sources (else null).  Next to it, the CPU
 oracle is timed on a bounded sample of the same workload (`cpu_baseline`).
 A second block times the streaming GQA decode workload (batch 64, 32 query /
 8 KV heads, 2048-token prompt, 256 decode steps).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu-baseline]
                     [--no-stream] [--copy-calibration]
     python bench.py --summarize-pmc counter_collection.csv   (profile helper)
 """
@@ -163,16 +165,21 @@ def _packed_bytes(pk) -> int:
 
 
 def _stream_decode(gear, WORKLOADS, torch):
-    """Streaming GQA decode: append + decode attention for 256 steps."""
+    """Streaming GQA decode: append + decode attention for 256 steps, timed
+    uninstrumented; the same steps on a second cache (same prompt) give the
+    per-kernel breakdown."""
     w = WORKLOADS["stream_gqa"]
     B, H, n, d, Hq = w.batch, w.heads, w.seq, w.head_dim, w.q_heads
     p = gear.Params(w.bits, w.group, w.outlier_ppm, w.rank, w.power_iters)
     fp = gear.Params(w.bits, w.group, w.outlier_ppm, w.fill_rank, w.power_iters)
     syn = w.kv_synth("cuda")
     k, v = syn.prompt(n)
-    cache = gear.Cache(B, H, d, p, fp, n, buf_tokens=w.buf_tokens, max_new_tokens=w.decode_steps,
+    caches = []
+    for _ in range(2):
+        c = gear.Cache(B, H, d, p, fp, n, buf_tokens=w.buf_tokens, max_new_tokens=w.decode_steps,
                        q_heads=Hq)
-    cache.load_prompt(k.contiguous(), v.contiguous())
+        c.load_prompt(k.contiguous(), v.contiguous())
+        caches.append(c)
     del k, v
     steps = w.decode_steps
     nk = torch.empty((steps, B, H, d), dtype=torch.float16, device="cuda")
@@ -191,13 +198,17 @@ def _stream_decode(gear, WORKLOADS, torch):
     warm.decode_attn(qs[0], out=out)
     torch.cuda.synchronize()
     del warm
-    gear.timing_enable(True)
     t0 = time.perf_counter()
     for i in range(steps):
-        cache.append(nk[i], nv[i])
-        cache.decode_attn(qs[i], out=out)
+        caches[0].append(nk[i], nv[i])
+        caches[0].decode_attn(qs[i], out=out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    gear.timing_enable(True)
+    for i in range(steps):
+        caches[1].append(nk[i], nv[i])
+        caches[1].decode_attn(qs[i], out=out)
+    torch.cuda.synchronize()
     kt = gear.timing_read()
     gear.timing_enable(False)
     attn_ms = sum(kt.get(k2, (0, 0.0))[1] for k2 in ("attn_split", "attn_combine"))
@@ -214,7 +225,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="7b_layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256)
@@ -256,7 +267,9 @@ def main():
     k, v = syn.prompt(n)
     x = torch.cat([k.reshape(B * H, n, d), v.reshape(B * H, n, d)]).contiguous()
     M = x.shape[0]
-    total = args.warmup + args.steps
+    # warm-up steps, the timed steps, then as many steps again with per-kernel
+    # and per-phase events recorded (kept out of the timed region)
+    total = args.warmup + 2 * args.steps
     new_k = torch.empty((total, B, H, d), dtype=torch.float16, device="cuda")
     new_v = torch.empty_like(new_k)
     qs = torch.empty((total, B, Hq, d), dtype=torch.float16, device="cuda")
@@ -276,32 +289,40 @@ def main():
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(total)]
 
-    def step(i):
+    def step(i, marks=False):
         e = ev[i]
-        e[0].record()
+        if marks:
+            e[0].record()
         gear.compress(x, p, out=packed, workspace=ws)
-        e[1].record()
+        if marks:
+            e[1].record()
         gear.decompress(packed, out=xhat)
-        e[2].record()
+        if marks:
+            e[2].record()
         cache.append(new_k[i], new_v[i])
         cache.decode_attn(qs[i], out=out)
-        e[3].record()
+        if marks:
+            e[3].record()
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    gear.timing_enable(True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, total):
+    for i in range(args.warmup, args.warmup + args.steps):
         step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # the same steps again, instrumented: per-phase events and the library's
+    # per-kernel HIP events on the launch stream
+    gear.timing_enable(True)
+    for i in range(args.warmup + args.steps, total):
+        step(i, marks=True)
+    torch.cuda.synchronize()
     ktimes = gear.timing_read()
     gear.timing_enable(False)
 
     ms_step = (t1 - t0) * 1e3 / args.steps
-    timed = ev[args.warmup:]
+    timed = ev[args.warmup + args.steps:]
     comp_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in timed]))
     decomp_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in timed]))
     dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in timed]))
