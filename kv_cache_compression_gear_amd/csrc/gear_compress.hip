@@ -145,13 +145,13 @@ __device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, double* Mo
 constexpr int kCoarse = 4096;   // pass-1 bins: |x| bit pattern >> 3
 constexpr int kFine = 8;        // pass-2 bins inside the chosen coarse bin
 constexpr int kFineSlot = kFine + 1;
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 
 // ---------------------------------------------------------------------------
 // Outlier threshold: the k-th largest |x| of a matrix, with ties broken by
-// the lower flat index.  One 16-wave workgroup per matrix.  The rows are split
-// exactly as the compress kernel splits them over its 8 waves (wave_rows);
-// each of those row blocks is read here by 2 consecutive waves.  Output per
+// the lower flat index.  One 8-wave workgroup per matrix (two fit on a CU).
+// The rows are split exactly as the compress kernel splits them over its 8
+// waves (wave_rows); wave b reads row block b.  Output per
 // matrix (kSelStride words, layout in gear_internal.h): the threshold key T,
 // per row block the ties at T it takes, its first CSR position and the ties it
 // holds, and a key bounding |x| over the entries that are not outliers (T, or
@@ -159,20 +159,25 @@ constexpr int kSelThreads = 1024;
 //
 // Common path (one pass over X plus a 1/16 sample): a histogram of a sample
 // of rows gives a key L0 that at least ~1.25 k entries reach; one pass then
-// counts, per row block, every key in the window [L0, L0 + 4096) exactly and
+// counts, per row block, every key in the window [L0, L0 + 1024) exactly and
 // every key above it.  If the k-th largest key lies in the window this is
 // the exact answer (checked from the counts); otherwise a two-pass radix
 // select over all keys (4096 coarse bins, then 8 fine bins) is used.
 template <int D, int U>
 __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR;
-    constexpr int NW = kSelThreads / 64;       // 16 waves
+    constexpr int NW = kSelThreads / 64;       // 8 waves
     constexpr int NB = kCompressWaves;         // row blocks
     constexpr int WPB = NW / NB;               // waves per row block
-    constexpr int kWin = 4096;                 // exact window of keys
+    // exact window of keys: one binade of fp16 (a factor of 2 in |x|); the
+    // sample places L0 where ~25% more than k entries lie above, typically a
+    // few dozen keys below the threshold.  A miss takes the radix path.
+    constexpr int kWin = 1024;
+    constexpr int BPC = kCoarse / kSelThreads;   // coarse bins per thread
+    constexpr int BPW = kWin / kSelThreads;      // window bins per thread
     constexpr int kSampleEvery = 16;           // sample = every 16th step
     __shared__ uint32_t s_hist[kCoarse];
-    __shared__ uint32_t s_win[NB * kWin];
+    __shared__ __attribute__((aligned(16))) uint32_t s_win[NB * kWin];
     __shared__ uint32_t s_cnt[2 * NW];
     __shared__ uint32_t s_fine[NW * kFineSlot];
     __shared__ uint32_t s_tmp[NW];
@@ -218,7 +223,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         return;
     }
     for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
-    for (int i = tid; i < NB * kWin; i += kSelThreads) s_win[i] = 0u;
+    for (int i = tid; i < NB * kWin / 4; i += kSelThreads)
+        reinterpret_cast<uint4*>(s_win)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tid < NW * kFineSlot) s_fine[tid] = 0u;
     if (tid < 4 + NB) s_res[tid] = 0u;
     __syncthreads();
@@ -232,12 +238,16 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
                           : make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    // Thread t owns 4 consecutive bins of a 4096-bin table, the top ones first;
-    // returns the bin where the count from the top, started at `base`,
-    // reaches `target` (writes it to *out; no write if never reached).
-    auto find_bin = [&](const uint32_t (&h)[4], uint32_t base, uint32_t target, uint32_t* out) {
-        const int b0 = (kSelThreads - 1 - tid) * 4;
-        const uint32_t sum = h[0] + h[1] + h[2] + h[3];
+    // Thread t owns the BP consecutive bins (BP = elements of h) of a table of
+    // BP * kSelThreads bins, the top ones first; returns the bin where the
+    // count from the top, started at `base`, reaches `target` (writes it to
+    // *out; no write if never reached).
+    auto find_bin = [&](const auto& h, uint32_t base, uint32_t target, uint32_t* out) {
+        constexpr int BP = sizeof(h) / sizeof(h[0]);
+        const int b0 = (kSelThreads - 1 - tid) * BP;
+        uint32_t sum = 0;
+#pragma unroll
+        for (int q = 0; q < BP; ++q) sum += h[q];
         uint32_t x = sum;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -250,7 +260,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         uint32_t cum = base + x - sum;
         for (int w = 0; w < wv; ++w) cum += s_tmp[w];
 #pragma unroll
-        for (int q = 3; q >= 0; --q) {
+        for (int q = BP - 1; q >= 0; --q) {
             if (cum < target && cum + h[q] >= target) *out = (uint32_t)(b0 + q);
             cum += h[q];
         }
@@ -290,31 +300,37 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     const uint32_t target = (uint32_t)(1.25 * expect + 4.0 * sqrt(expect) + 8.0);
     uint32_t L0 = 0;
     if (target <= total_samp) {
-        uint32_t h[4];
-        const int b0 = (kSelThreads - 1 - tid) * 4;
+        uint32_t h[BPC];
+        const int b0 = (kSelThreads - 1 - tid) * BPC;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = s_hist[b0 + q];
+        for (int q = 0; q < BPC; ++q) h[q] = s_hist[b0 + q];
         find_bin(h, 0u, target, &s_res[0]);
         __syncthreads();
         L0 = s_res[0] << 3;
     }
 
-    // ---- window pass: exact counts of keys in [L0, L0 + kWin), count above
+    // ---- window pass: exact counts of keys in [L0, L0 + kWin), count above.
+    // On the two keys of a dword at once: adding 0x8000 - L to each 15-bit key
+    // sets its bit 15 exactly when key >= L (no carry leaves a half).
     uint32_t above = 0;
+    const uint32_t thw = L0 + kWin;
+    const uint32_t add_l = (0x8000u - L0) * 0x10001u;
+    const uint32_t add_t = thw < 0x8000u ? (0x8000u - thw) * 0x10001u : 0u;
+    const uint32_t msk_t = thw < 0x8000u ? 0x80008000u : 0u;   // no key reaches 0x8000
     auto window = [&](const uint4 (&xr)[U], const bool (&ok)[U]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (!ok[u]) continue;
             const uint32_t w4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
-            bool any = false;
+            uint32_t ge_l = 0u;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t key = __builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 16u : 0u, 15u);
-                const uint32_t dlt = key - L0;
-                above += (key >= L0 + kWin) ? 1u : 0u;
-                any |= dlt < (uint32_t)kWin;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t k2 = w4[i] & 0x7fff7fffu;
+                ge_l |= (k2 + add_l) & 0x80008000u;
+                above += __builtin_popcount((k2 + add_t) & msk_t);
             }
-            if (any) {
+            // keys >= L0 + kWin also set ge_l: the loop below re-checks the window
+            if (ge_l != 0u) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t key = __builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 16u : 0u, 15u);
@@ -342,10 +358,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     uint32_t above_tot = 0;
     for (int w = 0; w < NW; ++w) above_tot += s_cnt[NW + w];
     {
-        uint32_t h[4];
-        const int b0 = (kSelThreads - 1 - tid) * 4;
+        uint32_t h[BPW];
+        const int b0 = (kSelThreads - 1 - tid) * BPW;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < BPW; ++q) {
             h[q] = 0u;
 #pragma unroll
             for (int b = 0; b < NB; ++b) h[q] += s_win[b * kWin + b0 + q];
@@ -358,12 +374,12 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     const uint32_t jstar = s_res[1];
     if (jstar != 0xffffffffu) {
         // exact threshold T = L0 + j*; per block: ties at T, count above T
-        const int b0 = (kSelThreads - 1 - tid) * 4;
+        const int b0 = (kSelThreads - 1 - tid) * BPW;
         uint32_t gtp[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) gtp[b] = 0u;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+        for (int q = 0; q < BPW; ++q)
             if ((uint32_t)(b0 + q) > jstar) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) gtp[b] += s_win[b * kWin + b0 + q];
@@ -429,10 +445,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     }
     __syncthreads();
     {
-        uint32_t h[4];
-        const int b0 = (kSelThreads - 1 - tid) * 4;
+        uint32_t h[BPC];
+        const int b0 = (kSelThreads - 1 - tid) * BPC;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) h[q] = s_hist[b0 + q];
+        for (int q = 0; q < BPC; ++q) h[q] = s_hist[b0 + q];
         find_bin(h, 0u, kk, &s_res[2]);
         __syncthreads();
     }
