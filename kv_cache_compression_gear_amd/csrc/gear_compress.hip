@@ -58,6 +58,24 @@ __device__ __forceinline__ float row_allreduce(float v) {
     return v;
 }
 
+// fp64 lane exchange: the two halves through DPP
+template <int CTRL>
+__device__ __forceinline__ double dpp64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(double, ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+// fp64 sum over each aligned group of N lanes (N = 8 or 16), result in every lane
+template <int N>
+__device__ __forceinline__ double row_sum64(double v) {
+    v += dpp64<0xB1>(v);
+    v += dpp64<0x4E>(v);
+    v += dpp64<0x141>(v);
+    if (N >= 16) v += dpp64<0x140>(v);
+    return v;
+}
+
 // min and max over each aligned group of g lanes, g in {1, 2, 4, 8, 16}
 // (g = G when G > 0).
 template <int G>
@@ -100,6 +118,7 @@ __device__ __forceinline__ uint64_t splitmix64(uint64_t seed, uint64_t i) {
 template <int RK>
 __device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, double* Mout /* LDS */) {
     double c[RK][RK];
+    double rinv[RK];   // 1 / C[i][i], 0 for a dead pivot
     bool alive[RK];
 #pragma unroll
     for (int i = 0; i < RK; ++i)
@@ -112,21 +131,23 @@ __device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, double* Mo
             double v = c[i][j];
 #pragma unroll
             for (int k = 0; k < i; ++k) v -= c[k][i] * c[k][j];
-            c[i][j] = alive[i] ? v / c[i][i] : 0.0;
+            c[i][j] = v * rinv[i];
         }
         const double pre2 = c[j][j];
         double post2 = pre2;
 #pragma unroll
         for (int k = 0; k < j; ++k) post2 -= c[k][j] * c[k][j];
         alive[j] = (pre2 > 0.0) && (post2 > 1e-12 * pre2);
-        c[j][j] = alive[j] ? sqrt(post2) : 0.0;
+        const double sq = alive[j] ? sqrt(post2) : 0.0;
+        c[j][j] = sq;
+        rinv[j] = alive[j] ? 1.0 / sq : 0.0;
     }
     // M = C^-1 in place (upper triangular; column j only needs columns < j of
     // the inverse and column j of C, overwritten top to bottom); a dead pivot
     // gives a zero row and column.
 #pragma unroll
     for (int j = 0; j < RK; ++j) {
-        const double inv = alive[j] ? 1.0 / c[j][j] : 0.0;
+        const double inv = rinv[j];
 #pragma unroll
         for (int i = 0; i < j; ++i) {
             double v = 0.0;
@@ -683,7 +704,10 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     constexpr bool LR = RK > 0;
     constexpr int RKX = LR ? RK : 1;
     constexpr int NP = RKX * (RKX + 1) / 2;
-    constexpr int PT = 256;                 // threads taking part in the power steps
+    // threads taking part in the power steps: all of them, except at D = 128
+    // with rank 8, where their partial sums would not fit the LDS budget of
+    // two workgroups per CU
+    constexpr int PT = (D == 128 && RK == 8) ? 256 : kCompressThreads;
     constexpr int NH = PT / D;              // threads per row of C in the power steps
     constexpr int kPlane = kSlabRows * D * 2;
     constexpr int kBig = LR ? (4 * kPlane > D * D * 4 ? 4 * kPlane : D * D * 4) : 16;
@@ -988,15 +1012,22 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     // ---- power steps on C (fp64)
     const double cscale = ldexp(1.0, -2 * ex);
     const int j = tid % D, h = tid / D;   // h < NH: the threads doing the power steps
+    constexpr int CPH = D / NH;           // columns of C summed by one thread
+    // G = B^T W: LPP lanes per entry (c1 <= c2), each summing every LPP-th j
+    constexpr int LPP = NP * 16 <= kCompressThreads ? 16 : 8;
     for (int it = 0; it < a.iters; ++it) {
         const bool last = it == a.iters - 1;
         double wp[RKX];
 #pragma unroll
         for (int c = 0; c < RKX; ++c) wp[c] = 0.0;
-        for (int c0 = h * (D / NH); c0 < (h + 1) * (D / NH) && h < NH; ++c0) {
-            const double cv = (double)Cm[c0 * D + j];   // C[j][c0], by symmetry
+        if (h < NH) {
+#pragma unroll 8
+            for (int i = 0; i < CPH; ++i) {
+                const int c0 = h * CPH + i;
+                const double cv = (double)Cm[c0 * D + j];   // C[j][c0], by symmetry
 #pragma unroll
-            for (int c = 0; c < RKX; ++c) wp[c] += cv * (double)s_b[c0 * RKX + c];
+                for (int c = 0; c < RKX; ++c) wp[c] += cv * (double)s_b[c0 * RKX + c];
+            }
         }
         if (h > 0 && h < NH) {
 #pragma unroll
@@ -1016,17 +1047,25 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             for (int c = 0; c < RKX; ++c) s_w[j * RKX + c] = wp[c];
         }
         __syncthreads();
-        if (tid < NP) {
-            int c1 = 0, rem = tid;
+        if (tid < NP * LPP) {   // whole aligned groups of LPP lanes
+            const int pi = tid / LPP, sub = tid % LPP;
+            int c1 = 0, rem = pi;
             while (rem >= RKX - c1) {
                 rem -= RKX - c1;
                 ++c1;
             }
             const int c2 = c1 + rem;
             double g = 0.0;
-            for (int jj = 0; jj < D; ++jj) g += (double)s_b[jj * RKX + c1] * s_w[jj * RKX + c2];
-            s_g[c1 * RKX + c2] = g;
-            s_g[c2 * RKX + c1] = g;
+#pragma unroll 4
+            for (int i = 0; i < D / LPP; ++i) {
+                const int jj = sub + LPP * i;
+                g += (double)s_b[jj * RKX + c1] * s_w[jj * RKX + c2];
+            }
+            g = row_sum64<LPP>(g);
+            if (sub == 0) {
+                s_g[c1 * RKX + c2] = g;
+                s_g[c2 * RKX + c1] = g;
+            }
         }
         __syncthreads();
         if (tid == 0) gram_to_m<RKX>(s_g, s_m);
