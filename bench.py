@@ -48,13 +48,15 @@ COPY_BYTES = 256 << 20          # plain copy used to calibrate the byte counters
 # kernel -> source file it is built from
 KERNEL_SOURCE = {"select": "gear_compress.hip", "compress": "gear_compress.hip",
                  "lowrank_a": "gear_compress.hip", "decompress": "gear_decompress.hip",
-                 "attn_split": "gear_attn.hip", "attn_combine": "gear_attn.hip",
-                 "buffer_append": "gear_attn.hip"}
+                 "attn_prompt": "gear_attn.hip", "attn_split": "gear_attn.hip",
+                 "attn_combine": "gear_attn.hip", "buffer_append": "gear_attn.hip"}
 # device symbol of each kernel (for rocprofv3 summaries)
+# ("attn_prompt" and "attn_split" are timed together by the library, as
+# "attn_split": the decode attention over all splits)
 KERNEL_SYMBOL = {"select": "select_kernel", "compress": "compress_kernel",
                  "lowrank_a": "lowrank_a_kernel", "decompress": "decompress_kernel",
-                 "attn_split": "attn_split_kernel", "attn_combine": "attn_combine_kernel",
-                 "buffer_append": "buffer_append_kernel"}
+                 "attn_prompt": "attn_prompt_kernel", "attn_split": "attn_split_kernel",
+                 "attn_combine": "attn_combine_kernel", "buffer_append": "buffer_append_kernel"}
 
 
 def source_digest(kernel: str) -> str:
