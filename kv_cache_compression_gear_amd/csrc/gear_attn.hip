@@ -95,6 +95,66 @@ __device__ __forceinline__ float row_allreduce(float v) {
     return v;
 }
 
+// Lanes l ^ 16 and l ^ 32 through the gfx950 permlane swaps (no LDS): each
+// swap leaves a lane's own value in one result and its partner's in the
+// other, so op(first, second) is the same in both partners.  Both results
+// are pinned as integers before they are read as floats: reading them as
+// floats directly, this compiler takes the first result for both.
+template <bool S32>
+__device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    uint32_t x, y;
+    if (S32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        x = p[0];
+        y = p[1];
+    } else {
+        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        x = p[0];
+        y = p[1];
+    }
+    asm("" : "+v"(x), "+v"(y));
+    a = __builtin_bit_cast(float, x);
+    b = __builtin_bit_cast(float, y);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+    float a, b;
+    swap_pair<false>(v, a, b);
+    return a + b;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    float a, b;
+    swap_pair<true>(v, a, b);
+    return a + b;
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    float a, b;
+    swap_pair<false>(v, a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    float a, b;
+    swap_pair<true>(v, a, b);
+    return fmaxf(a, b);
+}
+// sum and max over the 64 lanes of the wave, result in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+    return sum_xor32(sum_xor16(row_allreduce<16>(v)));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    return max_xor32(max_xor16(v));
+}
+// sum over the lanes of the wave with the same lane % LPR (LPR = 8 or 16)
+template <int LPR>
+__device__ __forceinline__ float sum_rowgroups(float v) {
+    if (LPR == 8) v += dpp<0x128>(v);   // row_ror:8 = lane ^ 8 within the row
+    return sum_xor32(sum_xor16(v));
+}
+
 constexpr int kAttnCsrCap = 2048;   // outliers of one piece staged in LDS
 constexpr int kAU = 4;              // token steps per batch of loads
 
@@ -552,7 +612,10 @@ constexpr int kFastThreads = 64 * kFastWaves;
 template <int BITS>
 __device__ __forceinline__ void unpack8(uint32_t w, float (&cf)[8]) {
     if (BITS == 4) {
-        const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+        // the nibble masks are hidden from the compiler, so that each code is
+        // one v_cvt_f32_ubyteN of a masked word (not a field extract + convert)
+        uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+        asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             cf[2 * i] = (float)((lo >> (8 * i)) & 0xffu);
@@ -596,8 +659,9 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int colq = lane % LPR, rl = lane / LPR;
-    const int pair = blockIdx.x / a.split0, split = blockIdx.x % a.split0;
-    const int b = pair / a.Hkv, hk = pair % a.Hkv;
+    // grid (split0, Hkv, B)
+    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int pair = b * a.Hkv + hk;
     const int t0 = split * kTPS;
     const Piece pc = find_piece(a, b, hk, t0, t0 + kTPS);
     const Packed& p = pc.p;
@@ -662,21 +726,23 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
         const int ri = tid & 255;
         const int32_t rp0 = (tid < 256 ? rpk : rpv)[ri];
         const int32_t rp1 = ri == 0 ? (tid < 256 ? rpk : rpv)[kTPS] : 0;
-        const f4v bk = tid < nb4 ? reinterpret_cast<const f4v*>(p.B + (size_t)pc.mk * D * r)[tid] : z4;
+        // B_K transposed: thread i takes element [c = i / D][j = i % D] (r D <= 1024)
+        const float* bkm = p.B + (size_t)pc.mk * D * r;
+        float bkt[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = tid + u * kFastThreads;
+            bkt[u] = i < r * D ? bkm[(i % D) * r + i / D] : 0.0f;
+        }
         const f4v bv = tid < nb4 ? reinterpret_cast<const f4v*>(p.B + (size_t)pc.mv * D * r)[tid] : z4;
         store_side(sk);
         int32_t* srp = tid < 256 ? s_rk : s_rv;
         srp[ri] = min(max(rp0, 0), (int)kk);
         if (ri == 0) srp[kTPS] = min(max(rp1, 0), (int)kk);
-        if (tid < nb4) {
-            reinterpret_cast<f4v*>(s_bv)[tid] = bv;
-            // element 4 tid + i of B_K (row-major [j][c]) into [c][j]
+        if (tid < nb4) reinterpret_cast<f4v*>(s_bv)[tid] = bv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int f = 4 * tid + i;
-                s_bkt[(f % r) * D + f / r] = bk[i];
-            }
-        }
+        for (int u = 0; u < 2; ++u)
+            if (tid + u * kFastThreads < r * D) s_bkt[tid + u * kFastThreads] = bkt[u];
         for (int i = tid; i < kVsBytes / 16; i += kFastThreads)
             reinterpret_cast<uint4*>(s_vs)[i] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -723,11 +789,15 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
     float qbl[G];   // (B^T q)[colq] in the lanes colq < r
 #pragma unroll
     for (int h = 0; h < G; ++h) qbl[h] = colq < r ? s_qb[h * kMaxRank + colq] : 0.0f;
+    // side data of token tok0 + s RPS at gidx0 + s gstep (scale, zero) and
+    // aidx0 + s astep (A)
+    const int gidx0 = tok0 * ngr + gi, gstep = RPS * ngr;
+    const int aidx0 = tok0 * r + colq, astep = RPS * r;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
         const int tok = tok0 + s * RPS;
-        const float scv = s_gs[tok * ngr + gi], zpv = s_gz[tok * ngr + gi];
-        const float av = colq < r ? s_a[tok * r + colq] : 0.0f;
+        const float scv = s_gs[gidx0 + s * gstep], zpv = s_gz[gidx0 + s * gstep];
+        const float av = colq < r ? s_a[aidx0 + s * astep] : 0.0f;
         float cf[8];
         unpack8<BITS>(wk[s], cf);
         float part[G];
@@ -765,9 +835,7 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             pr[h] = a.sm_scale * (s_sc[tid * G + h] + add[h]);
-            float m = pr[h];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+            const float m = wave_max(pr[h]);
             if (lane == 0) s_wm[wv * G + h] = m;
         }
     }
@@ -778,9 +846,7 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
             const float m = fmaxf(fmaxf(s_wm[h], s_wm[G + h]), fmaxf(s_wm[2 * G + h], s_wm[3 * G + h]));
             pr[h] = expf(pr[h] - m);
             s_sc[tid * G + h] = pr[h];
-            float sm = pr[h];
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) sm += __shfl_xor(sm, off, 64);
+            const float sm = wave_sum(pr[h]);
             if (lane == 0) s_ws[wv * G + h] = sm;
         }
     }
@@ -815,8 +881,8 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
         const int tok = tok0 + s * RPS;
-        const float scv = s_gs[tok * ngr + gi], zpv = s_gz[tok * ngr + gi];
-        const float av = colq < r ? s_a[tok * r + colq] : 0.0f;
+        const float scv = s_gs[gidx0 + s * gstep], zpv = s_gz[gidx0 + s * gstep];
+        const float av = colq < r ? s_a[aidx0 + s * astep] : 0.0f;
         float cf[8];
         unpack8<BITS>(wvv[s], cf);
 #pragma unroll
@@ -836,9 +902,7 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
     // low-rank part: acc += B_V (sum_t p_t A_t); the per-rank sums over the
     // workgroup's tokens are added by one row group
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < G; ++h) pa[h] += __shfl_xor(pa[h], off, 64);
+    for (int h = 0; h < G; ++h) pa[h] = sum_rowgroups<LPR>(pa[h]);
     if (rl == 0 && colq < r) {
 #pragma unroll
         for (int h = 0; h < G; ++h) s_pa[(wv * G + h) * kMaxRank + colq] = pa[h];
@@ -859,11 +923,9 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
     // reduce over the row groups of the wave, then over the waves: waves 4..7
     // hand theirs to waves 0..3, which hand the sums to the store
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+        for (int e = 0; e < 8; ++e) acc[h][e] = sum_rowgroups<LPR>(acc[h][e]);
     if (rl == 0 && wv >= 4) {
 #pragma unroll
         for (int h = 0; h < G; ++h)
@@ -958,10 +1020,11 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
     {
         Timed t(kKAttnSplit, st);
         if (a.split0 > 0) {
+            const dim3 grid((unsigned)a.split0, (unsigned)a.Hkv, (unsigned)a.B);
             if (a.prompt.p.bits == 4)
-                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4>), dim3(pairs * a.split0), dim3(kFastThreads), 0, st, a);
+                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4>), grid, dim3(kFastThreads), 0, st, a);
             else
-                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2>), dim3(pairs * a.split0), dim3(kFastThreads), 0, st, a);
+                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2>), grid, dim3(kFastThreads), 0, st, a);
         }
         if (a.splits > a.split0)
             hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(pairs * (a.splits - a.split0)), dim3(kThreads),
