@@ -122,7 +122,8 @@ size_t gear_compress_workspace_bytes(const gear_params* p, const gear_shape* s);
  * initialised (it carries per-matrix results between the call's kernels: 64
  * bytes of outlier-selection results and head_dim x 8 floats of the low-rank
  * fit per compressed matrix); it must not be shared by calls that may run
- * concurrently.
+ * concurrently.  Every entry of x_f16 must be finite: NaN or infinity is not
+ * detected, and the packed result for such input is unspecified.
  */
 gear_status gear_compress(const gear_params* p, const gear_shape* s, const void* x_f16,
                           void* packed, void* workspace, size_t workspace_bytes,
@@ -176,7 +177,8 @@ gear_status gear_cache_create(const gear_cache_config* c, void* arena, size_t ar
 void gear_cache_destroy(gear_cache* cache);
 
 /* Compresses the prompt: k_f16, v_f16 are [B][Hkv][prompt_tokens][d].  Only
-   valid on a cache with no tokens yet. */
+   valid on a cache with no tokens yet.  Entries must be finite (as for
+   gear_compress). */
 gear_status gear_cache_load_prompt(gear_cache* cache, const void* k_f16, const void* v_f16,
                                    void* workspace, size_t workspace_bytes, void* stream);
 
@@ -184,7 +186,8 @@ gear_status gear_cache_load_prompt(gear_cache* cache, const void* k_f16, const v
  * Appends n_new tokens per sequence: k_new_f16, v_new_f16 are
  * [B][Hkv][n_new][d].  Tokens go to the buffer in order; every time the
  * buffer holds buf_tokens tokens it is compressed (fill settings) into a new
- * segment and emptied, before the next token is placed.
+ * segment and emptied, before the next token is placed.  Entries must be
+ * finite (as for gear_compress).
  * GEAR_ERR_CAPACITY if the total would exceed max_new_tokens.
  */
 gear_status gear_append_tokens(gear_cache* cache, const void* k_new_f16, const void* v_new_f16,
@@ -197,7 +200,8 @@ gear_status gear_append_tokens(gear_cache* cache, const void* k_new_f16, const v
  *   out[b][h] = sum_t softmax_t(sm_scale * q[b][h] . K^_t) V^_t
  * with K^, V^ of KV head floor(h * Hkv / q_heads).  q_f16 is [B][q_heads][d],
  * out_f32 is [B][q_heads][d].  q_heads must be a multiple of Hkv.  With no
- * cached tokens the output is zero.
+ * cached tokens the output is zero.  q_f16 must be finite (NaN or infinity is
+ * not detected; the output for it is unspecified).
  */
 gear_status gear_decode_attn(const gear_cache* cache, const void* q_f16, int32_t q_heads,
                              float sm_scale, float* out_f32, void* workspace,
