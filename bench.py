@@ -34,6 +34,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 from collections import defaultdict
@@ -60,11 +61,16 @@ KERNEL_SYMBOL = {"select": "select_kernel", "compress": "compress_kernel",
 
 
 def source_digest(kernel: str) -> str:
-    """sha256 (first 16 hex digits) over the kernel's source and the shared header."""
+    """sha256 (first 16 hex digits) over the code of the kernel's source and of
+    the shared header, comments and whitespace removed (so that an edit of a
+    comment does not mark the counters stale)."""
     h = hashlib.sha256()
     for name in (KERNEL_SOURCE[kernel], "gear_internal.h"):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -119,9 +119,9 @@ size_t gear_compress_workspace_bytes(const gear_params* p, const gear_shape* s);
  * Compress: x_f16 (the stack described by s) -> packed (gear_packed_bytes).
  * Runs the outlier filter, group quantization and the low-rank fit of every
  * matrix.  workspace: >= gear_compress_workspace_bytes, contents need not be
- * initialised (it carries per-matrix results between the call's kernels: 64
- * bytes of outlier-selection results and head_dim x 8 floats of the low-rank
- * fit per compressed matrix); it must not be shared by calls that may run
+ * initialised (it carries per-matrix results between the call's kernels:
+ * 128 bytes of outlier-selection results and up to head_dim x 8 floats of the
+ * low-rank fit per compressed matrix); it must not be shared by calls that may run
  * concurrently.  Every entry of x_f16 must be finite: NaN or infinity is not
  * detected, and the packed result for such input is unspecified.
  */

@@ -10,9 +10,9 @@
 //   A, B = t PowerSGD steps on R = D - deq(Q) from a fixed B0, L = A B^T.
 //
 // Design (MI355X): three launches per call.
-//   * select_kernel (16 waves per matrix): the threshold key T of the k-th
+//   * select_kernel (8 waves per matrix): the threshold key T of the k-th
 //     largest |x|, each row block's share of the ties at T and its first CSR
-//     position.  A 1/16 row sample places a 4096-key window that one exact
+//     position.  A 1/16 row sample places a 1024-key window that one exact
 //     counting pass resolves; a two-pass radix select is the fallback.
 //   * compress_kernel (8 waves per matrix, one pass over X): outlier mask, CSR
 //     emit (DPP prefix sums), bit-exact fp32 group quantization (rint of the
