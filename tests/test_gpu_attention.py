@@ -172,3 +172,33 @@ def test_streaming_full_gqa_workload_sampled():
             torch.cuda.synchronize()
             ref = oc.decode_attention(q[sel].cpu().numpy())
             _attn_check(out[sel], ref, what=f"step {s}")
+
+
+def test_decode_attention_full_7b_layer_sampled():
+    """The benchmark's decode step at full size: 8 x 32 heads, 4096-token
+    prompt, one appended token, one query per head (the whole-split prompt
+    kernel with staged outliers, plus the buffer tail); batches {0, 7} x heads
+    0..3 against the oracle (heads attend independently at one query head per
+    KV head)."""
+    w = WORKLOADS["7b_layer"]
+    B, H, n, d = w.batch, w.heads, w.seq, w.head_dim
+    Hq = w.q_heads or H
+    assert Hq == H
+    _say(f"[attention full] 7b_layer B={B} H={H} prompt={n}")
+    pp = P(w.bits, w.group, w.outlier_ppm, w.rank, w.power_iters)
+    fp = P(w.bits, w.group, w.outlier_ppm, w.fill_rank, w.power_iters)
+    syn = w.kv_synth("cuda")
+    k, v = syn.prompt(n)
+    cache = _new_cache(B, H, Hq, d, pp, fp, n, w.buf_tokens, 1)
+    cache.load_prompt(k, v)
+    kn, vn = syn.step()
+    q = syn.queries(Hq)
+    cache.append(kn, vn)
+    out = cache.decode_attn(q)
+    torch.cuda.synchronize()
+    bsel, hs = [0, B - 1], slice(0, 4)
+    oc = orc.OracleCache(len(bsel), 4, d, to_orc_params(pp), to_orc_params(fp), w.buf_tokens)
+    oc.load_prompt(k[bsel][:, hs].cpu().numpy(), v[bsel][:, hs].cpu().numpy())
+    oc.append(kn[bsel][:, hs].cpu().numpy(), vn[bsel][:, hs].cpu().numpy())
+    ref = oc.decode_attention(q[bsel][:, hs].cpu().numpy())
+    _attn_check(out[bsel][:, hs], ref, what="7b_layer sampled")
