@@ -646,27 +646,44 @@ __device__ __forceinline__ void block_of(int wv, int b, int& I, int& J) {
     }
 }
 
+// This wave's Gram blocks over one slab.  The blocks use at most two column
+// blocks X and Y of R; per 16-row chunk each one's hi and lo operands are
+// read once, and the next chunk's operands are read while this chunk's
+// MFMAs run (two register sets, alternating).
 template <int D>
 __device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane, f16v (&acc)[2]) {
     constexpr int kPlane = kSlabRows * D * 2;
     const unsigned char* hi = slab;
     const unsigned char* lo = slab + kPlane;
     const int nb = blocks_of<D>(wv);
+    if (nb == 0) return;   // wave-uniform
+    int I0, J0, I1 = 0, J1 = 0;
+    block_of<D>(wv, 0, I0, J0);
+    if (nb > 1) block_of<D>(wv, 1, I1, J1);
+    const int X = I0;
+    const int Y = J0 != X ? J0 : (nb > 1 ? (I1 != X ? I1 : J1) : X);
+    const bool useY = Y != X;
+    const bool diag0 = J0 == X;          // block 0: (X, X), else (X, Y)
+    const bool ymajor1 = I1 != X;        // block 1: (Y, X), else (X, Y)
+    h8v xh[2], xl[2], yh[2], yl[2];
+    auto rd = [&](int kc, int buf) {
+        xh[buf] = read_operand<D>(hi, 16 * kc, 32 * X, lane);
+        xl[buf] = read_operand<D>(lo, 16 * kc, 32 * X, lane);
+        if (useY) {
+            yh[buf] = read_operand<D>(hi, 16 * kc, 32 * Y, lane);
+            yl[buf] = read_operand<D>(lo, 16 * kc, 32 * Y, lane);
+        }
+    };
+    rd(0, 0);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (b >= nb) break;   // wave-uniform
-        int I, J;
-        block_of<D>(wv, b, I, J);
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-            const int kb = 16 * kc;
-            const h8v hi_i = read_operand<D>(hi, kb, 32 * I, lane), lo_i = read_operand<D>(lo, kb, 32 * I, lane);
-            if (I == J) {
-                acc[b] = mma3(hi_i, lo_i, hi_i, lo_i, acc[b]);
-            } else {
-                const h8v hi_j = read_operand<D>(hi, kb, 32 * J, lane), lo_j = read_operand<D>(lo, kb, 32 * J, lane);
-                acc[b] = mma3(hi_i, lo_i, hi_j, lo_j, acc[b]);
-            }
+    for (int kc = 0; kc < 4; ++kc) {
+        const int c = kc & 1;
+        if (kc < 3) rd(kc + 1, c ^ 1);
+        if (diag0) acc[0] = mma3(xh[c], xl[c], xh[c], xl[c], acc[0]);
+        else acc[0] = mma3(xh[c], xl[c], yh[c], yl[c], acc[0]);
+        if (nb > 1) {
+            if (ymajor1) acc[1] = mma3(yh[c], yl[c], xh[c], xl[c], acc[1]);
+            else acc[1] = mma3(xh[c], xl[c], yh[c], yl[c], acc[1]);
         }
     }
 }
