@@ -1145,9 +1145,9 @@ struct BoolTag { static constexpr bool value = B; };
 // CPL (l / 16); the j-th instruction contracts column CPL q + j of the four
 // lane groups q, so CPL instructions cover all D columns and no cross-lane sum
 // is needed.  The output lanes n = l % 16 < r hold A[row][n] for the rows
-// 4 (l / 16) + 0..3 of the step.  X is loaded row-contiguously (each load
-// instruction covers whole rows) and regrouped into that layout through a
-// per-wave LDS tile whose 16-byte chunks are XOR-swizzled by row.
+// 4 (l / 16) + 0..3 of the step.  X goes from HBM straight into a per-wave
+// LDS tile (row-contiguous load instructions, 16-byte chunks XOR-swizzled by
+// row) and is read from there in that layout.
 // byte I of x as a float, one instruction (v_cvt_f32_ubyteI)
 template <int I>
 __device__ __forceinline__ float ubyte_f(uint32_t x) {
@@ -1159,7 +1159,10 @@ __device__ __forceinline__ float ubyte_f(uint32_t x) {
     return f;
 }
 
-template <int D, int RK>
+// BITS4: 4-bit codes (else 2-bit); ONEG: a lane's columns lie in one
+// quantization group.  Compile-time, so that each variant gets the registers
+// it needs on its own.
+template <int D, int RK, bool BITS4, bool ONEG>
 __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     constexpr int CPL = D / 4;                // columns per lane
     constexpr int NX = CPL / 8;               // 16-byte chunks of X per lane
@@ -1168,7 +1171,8 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rr = lane & 15, q = lane >> 4;
     const Packed& o = a.out;
-    const int rows = o.rows, rank = o.rank, bits = o.bits;
+    const int rows = o.rows, rank = o.rank;
+    constexpr int bits = BITS4 ? 4 : 2;
     const int g = o.group, ngr = D / g;
     const int ngl = g >= CPL ? 1 : CPL / g;   // groups within a lane's columns (<= 4)
     const uint32_t kk = (uint32_t)o.k;
@@ -1208,14 +1212,28 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     float one = 1.0f;   // opaque 1: keeps x - zero a single mixed fma
     asm volatile("" : "+s"(one));
 
-    // per-wave tile of 16 rows of X: [row][chunk ^ swizzle(row)], 16-byte chunks
+    // per-wave tiles of 16 rows of X, two (steps alternate): [row][chunk ^
+    // swizzle(row)], 16-byte chunks.  X goes from HBM straight into a tile
+    // (global_load_lds_dwordx4: lane l of a load instruction fills slot l of
+    // its 64-slot range, no registers), the next step's while this step
+    // computes.
     constexpr int CPR = D / 8;                // chunks per row (16 or 8)
-    constexpr int RPI = 64 / CPR;             // rows per load instruction (4 or 8)
-    __shared__ __attribute__((aligned(16))) uint4 s_x[4][16 * CPR];
-    uint4* tile = s_x[wv];
+    constexpr int NLD = 16 * CPR / 64;        // load instructions per tile
+    __shared__ __attribute__((aligned(16))) uint4 s_x[4][2][16 * CPR];
     auto swz = [](int row, int ch) { return ch ^ (row & (CPR - 1)); };
+    auto issue_x = [&](int s, int buf) {
+        uint4* t = s_x[wv][buf];
+#pragma unroll
+        for (int c = 0; c < NLD; ++c) {
+            const int slot = 64 * c + lane, trow = slot / CPR;
+            const int ch = swz(trow, slot % CPR);   // the chunk stored at this slot
+            const uint32_t xr = (uint32_t)min(r0 + s * 16 + trow, rows - 1);   // valid address
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(xb + (xr * D + ch * 8) * 2),
+                (__attribute__((address_space(3))) void*)(t + 64 * c), 16, 0, 0);
+        }
+    };
     struct Buf {
-        uint4 x[NX];
         uint4 cw;
         float sc[4], zp[4];
     };
@@ -1223,18 +1241,11 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
         Buf bf;
         const int row = r0 + s * 16 + rr;
         const uint32_t rc = (uint32_t)min(row, rows - 1);   // always a valid address
-        // X: instruction c covers rows RPI c .. RPI c + RPI - 1 of the step, lane
-        // l chunk l % CPR of row RPI c + l / CPR (NX = 16 / RPI instructions)
-#pragma unroll
-        for (int c = 0; c < NX; ++c) {
-            const uint32_t xr = (uint32_t)min(r0 + s * 16 + RPI * c + lane / CPR, rows - 1);
-            bf.x[c] = ld_at<uint4>(xb, (xr * D + 8 * (lane % CPR)) * 2);
-        }
-        const uint32_t cbytes = (uint32_t)(CPL * bits / 8);  // 16, 8 or 4
+        constexpr uint32_t cbytes = (uint32_t)(CPL * bits / 8);  // 16, 8 or 4
         const uint32_t coff = rc * (D * bits / 8) + (uint32_t)(c0 * bits / 8);
-        if (cbytes == 16) {
+        if constexpr (cbytes == 16) {
             bf.cw = ld_at<uint4>(cb, coff);
-        } else if (cbytes == 8) {
+        } else if constexpr (cbytes == 8) {
             const uint2 v = ld_at<uint2>(cb, coff);
             bf.cw = make_uint4(v.x, v.y, 0u, 0u);
         } else {
@@ -1252,27 +1263,12 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
         }
         return bf;
     };
-    auto compute = [&](const Buf& bf, int s, auto split_tag, auto bits4_tag, auto one_group_tag) {
+    auto compute = [&](const uint4 (&xq)[NX], const Buf& bf, int s, auto split_tag) {
         constexpr bool SPLIT = decltype(split_tag)::value;
-        constexpr bool BITS4 = decltype(bits4_tag)::value;      // else 2-bit codes
-        constexpr bool ONEG = decltype(one_group_tag)::value;   // one group per lane
         const int row = r0 + s * 16 + rr;
         const bool valid = row < rows;
         const int thrk = row < r_all ? thr_all : thr_none;
         const uint32_t t2 = ((uint32_t)thrk & 0xffffu) * 0x10001u;   // thrk in both halves
-        // regroup X through the wave's tile: lane (rr, q) takes row rr, chunks
-        // CPL q / 8 .. CPL q / 8 + NX - 1 (LDS operations of a wave execute in
-        // order; the tile is rewritten only after this step's reads)
-        uint4 xq[NX];
-#pragma unroll
-        for (int c = 0; c < NX; ++c) {
-            const int trow = RPI * c + lane / CPR;
-            tile[trow * CPR + swz(trow, lane % CPR)] = bf.x[c];
-        }
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int c = 0; c < NX; ++c) xq[c] = tile[rr * CPR + swz(rr, (c0 / 8) + c)];
-        __builtin_amdgcn_wave_barrier();
         // ties of the split block taken by this row: bits of tm (column c0 + j)
         uint32_t tm = 0u;
         if (SPLIT) {
@@ -1340,26 +1336,33 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
             }
         }
     };
-    // two steps in flight: the next step's loads are issued before this
-    // step's arithmetic
-    auto run = [&](auto split_tag, auto bits4_tag, auto one_group_tag) {
+    // Per step: this step's X from its tile into registers (lane (rr, q) takes
+    // row rr, chunks CPL q / 8 .. CPL q / 8 + NX - 1), then the next step's
+    // loads are issued, then this step's arithmetic.  The compiler waits for
+    // every outstanding load before the first tile read after a tile load,
+    // so the next step's loads are issued only after this step's reads; they
+    // go to the other tile.
+    auto run = [&](auto split_tag) {
+        issue_x(0, 0);
+        Buf cur = load(0);
 #pragma unroll 1
         for (int s = 0; s < kLrSteps; ++s) {
-            const Buf cur = load(s);
-            compute(cur, s, split_tag, bits4_tag, one_group_tag);
+            const uint4* t = s_x[wv][s & 1];
+            uint4 xq[NX];
+#pragma unroll
+            for (int c = 0; c < NX; ++c) xq[c] = t[rr * CPR + swz(rr, (c0 / 8) + c)];
+            __builtin_amdgcn_sched_barrier(0);
+            Buf nxt = cur;
+            if (s + 1 < kLrSteps) {
+                issue_x(s + 1, (s + 1) & 1);
+                nxt = load(s + 1);
+            }
+            compute(xq, cur, s, split_tag);
+            cur = nxt;
         }
     };
-    auto run2 = [&](auto split_tag) {
-        if (bits == 4) {
-            if (ngl == 1) run(split_tag, BoolTag<true>{}, BoolTag<true>{});
-            else run(split_tag, BoolTag<true>{}, BoolTag<false>{});
-        } else {
-            if (ngl == 1) run(split_tag, BoolTag<false>{}, BoolTag<true>{});
-            else run(split_tag, BoolTag<false>{}, BoolTag<false>{});
-        }
-    };
-    if (wave_split) run2(BoolTag<true>{});
-    else run2(BoolTag<false>{});
+    if (wave_split) run(BoolTag<true>{});
+    else run(BoolTag<false>{});
 }
 
 template <int D>
@@ -1389,7 +1392,15 @@ hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
         const int64_t blocks = a.out.M * ((a.out.rows + RPW - 1) / RPW);
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         Timed t(kKLowrankA, st);
-        hipLaunchKernelGGL((lowrank_a_kernel<D, RK>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+        const bool one_group = a.out.group >= D / 4;   // a lane's D/4 columns in one group
+        const dim3 grid((unsigned)blocks), wg(kThreads);
+        if (a.out.bits == 4) {
+            if (one_group) hipLaunchKernelGGL((lowrank_a_kernel<D, RK, true, true>), grid, wg, 0, st, a);
+            else hipLaunchKernelGGL((lowrank_a_kernel<D, RK, true, false>), grid, wg, 0, st, a);
+        } else {
+            if (one_group) hipLaunchKernelGGL((lowrank_a_kernel<D, RK, false, true>), grid, wg, 0, st, a);
+            else hipLaunchKernelGGL((lowrank_a_kernel<D, RK, false, false>), grid, wg, 0, st, a);
+        }
         e = hipGetLastError();
     }
     return e;
