@@ -593,13 +593,14 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // Whole prompt splits: kTPS tokens inside one compressed K matrix and its V
 // matrix, at most kFastGroups quantization groups per token.  The same sums
-// as attn_split_kernel, organised around two rounds of loads so that a
-// workgroup waits on memory twice instead of once per batch of tokens:
+// as attn_split_kernel, organised around a few rounds of loads so that a
+// workgroup waits on memory a few times instead of once per batch of tokens:
 //   1. q, the K codes (registers), K's scales, zeros and A rows, both
 //      matrices' row pointers and both B matrices (LDS);
-//   2. issued before the K scores are computed and consumed after: the V
-//      codes, V's scales, zeros and A rows, and both matrices' CSR entries
-//      (a contiguous range, loaded coalesced).
+//   2. issued before the K scores are computed and consumed after: both
+//      matrices' CSR entries (a contiguous range, loaded coalesced); V's
+//      codes, scales, zeros and A rows are issued after the K scores and
+//      consumed after the softmax.
 // 8 waves; wave w takes tokens [32 w, 32 w + 32), RPS per step.  The sparse
 // V terms p_t s_tj go to a per-wave LDS row (one LDS add per entry), added
 // to the wave's sums at the end.
@@ -627,8 +628,14 @@ __device__ __forceinline__ void unpack8(uint32_t w, float (&cf)[8]) {
     }
 }
 
+// waves per SIMD the registers are budgeted for: 8 at one query head per KV
+// head (4 workgroups per CU, within LDS; fits without spills), else 2 (the
+// compiler's choice)
+template <int G>
+constexpr int prompt_waves() { return G == 1 ? 8 : 2; }
+
 template <int D, int G, int BITS>
-__global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TPW = kTPS / kFastWaves, SPW = TPW / RPS;
     constexpr int CPT = kFastCap / kFastThreads;      // staged CSR entries per thread
     constexpr int ROWB = D * BITS / 8;                 // code bytes per token
@@ -763,12 +770,6 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
         ek[j] = (stg_k && i < cnt_k) ? ((uint32_t)colk[beg_k + i] | ((uint32_t)valk[beg_k + i] << 16)) : 0u;
         ev[j] = (stg_v && i < cnt_v) ? ((uint32_t)colv[beg_v + i] | ((uint32_t)valv[beg_v + i] << 16)) : 0u;
     }
-    uint32_t wvv[SPW];
-#pragma unroll
-    for (int s = 0; s < SPW; ++s)
-        wvv[s] = BITS == 4 ? ld_at<uint32_t>(cvb, coff0 + s * RPS * ROWB)
-                           : (uint32_t)ld_at<uint16_t>(cvb, coff0 + s * RPS * ROWB);
-    const Side sv = load_side(mrv);
 
     // (B_K^T q)[h][c]: 16 lanes per (h, c), 8 columns each, summed over the
     // lane row
@@ -817,6 +818,14 @@ __global__ void __launch_bounds__(kFastThreads, 2) attn_prompt_kernel(AttnArgs a
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         if (stg_k && tid + j * kFastThreads < cnt_k) s_cv[tid + j * kFastThreads] = ek[j];
+    // V's codes and side data, consumed after the softmax (issued only now,
+    // so that they hold no registers during the K phase)
+    uint32_t wvv[SPW];
+#pragma unroll
+    for (int s = 0; s < SPW; ++s)
+        wvv[s] = BITS == 4 ? ld_at<uint32_t>(cvb, coff0 + s * RPS * ROWB)
+                           : (uint32_t)ld_at<uint16_t>(cvb, coff0 + s * RPS * ROWB);
+    const Side sv = load_side(mrv);
     __syncthreads();
 
     // ---------------- sparse part (one thread per token, waves 0..3), softmax
