@@ -639,7 +639,12 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     constexpr int LPR = D / 8, RPS = 64 / LPR, TPW = kTPS / kFastWaves, SPW = TPW / RPS;
     constexpr int CPT = kFastCap / kFastThreads;      // staged CSR entries per thread
     constexpr int ROWB = D * BITS / 8;                 // code bytes per token
-    constexpr int kVsBytes = 4 * G * D * 4;           // sparse V sums of the 4 token waves
+    // threads per token for the sparse V terms (one head: its even and odd
+    // entries on two threads, so all 8 waves take part; with more heads the
+    // LDS adds per entry dominate and 4 waves keep the other 4 free)
+    constexpr int VSP = G == 1 ? 2 : 1;
+    constexpr int kVsRows = 4 * VSP;                   // sparse V sums, one row per wave
+    constexpr int kVsBytes = kVsRows * G * D * 4;
     constexpr int kRedBytes = 4 * G * D * 4;
     constexpr int kCsrBytes = kRedBytes > kFastCap * 4 ? kRedBytes : kFastCap * 4;
     static_assert(kTPS * kFastGroups / 4 <= 128 && kTPS * kMaxRank / 4 <= kFastThreads &&
@@ -865,15 +870,21 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     for (int j = 0; j < CPT; ++j)
         if (stg_v && tid + j * kFastThreads < cnt_v) s_cv[tid + j * kFastThreads] = ev[j];
     __syncthreads();
-    // sparse V terms p_t s_tj of token tid into its wave's LDS row (entries in
-    // CSR order, one LDS add each; the wave's adds execute in program order)
-    if (tid < kTPS) {
+    // sparse V terms p_t s_tj into the wave's LDS row: entry i (CSR order) of
+    // token t by thread t + kTPS (i mod VSP), one LDS add each (a wave's adds
+    // execute in program order, rows are per wave, so the sums are
+    // deterministic)
+    if (tid < kTPS * VSP) {
+        const int t = tid & (kTPS - 1), par = tid / kTPS;
+        float pt[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pt[h] = par == 0 ? pr[h] : s_sc[t * G + h];
         float* vs = s_vs + wv * G * D;
-        for (int k = s_rv[tid]; k < s_rv[tid + 1]; ++k) {
+        for (int k = s_rv[t] + par; k < s_rv[t + 1]; k += VSP) {
             const uint32_t e = stg_v ? s_cv[k - beg_v] : ((uint32_t)colv[k] | ((uint32_t)valv[k] << 16));
             const float v = h2f(e >> 16);
 #pragma unroll
-            for (int h = 0; h < G; ++h) atomicAdd(&vs[h * D + (e & (D - 1))], pr[h] * v);
+            for (int h = 0; h < G; ++h) atomicAdd(&vs[h * D + (e & (D - 1))], pt[h] * v);
         }
     }
 
@@ -952,10 +963,12 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
     for (int i = tid; i < G * D; i += kFastThreads) {
         const int h = i / D, j = i % D;
+        const float* vs = s_vs + h * D + j;   // row w at vs[w * G * D]
+        constexpr int RS = G * D;
+        float sp = (vs[0 * RS] + vs[1 * RS]) + (vs[2 * RS] + vs[3 * RS]);
+        if (kVsRows == 8) sp += (vs[4 * RS] + vs[5 * RS]) + (vs[6 * RS] + vs[7 * RS]);
         part[h * (D + 2) + j] = (s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j]) +
-                                (s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j]) +
-                                ((s_vs[(0 * G + h) * D + j] + s_vs[(1 * G + h) * D + j]) +
-                                 (s_vs[(2 * G + h) * D + j] + s_vs[(3 * G + h) * D + j]));
+                                (s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j]) + sp;
     }
     if (tid < G) {
         part[tid * (D + 2) + D] = fmaxf(fmaxf(s_wm[tid], s_wm[G + tid]), fmaxf(s_wm[2 * G + tid], s_wm[3 * G + tid]));
