@@ -629,22 +629,26 @@ __device__ __forceinline__ void unpack8(uint32_t w, float (&cf)[8]) {
 }
 
 // waves per SIMD the registers are budgeted for: 8 at one query head per KV
-// head (4 workgroups per CU, within LDS; fits without spills), else 2 (the
-// compiler's choice)
+// head (4 workgroups per CU, within LDS; fits without spills), 4 at four (2
+// workgroups per CU; a few VGPRs spill), else 2 (the compiler's choice)
 template <int G>
-constexpr int prompt_waves() { return G == 1 ? 8 : 2; }
+constexpr int prompt_waves() { return G == 1 ? 8 : G == 4 ? 4 : 2; }
 
 template <int D, int G, int BITS>
 __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TPW = kTPS / kFastWaves, SPW = TPW / RPS;
     constexpr int CPT = kFastCap / kFastThreads;      // staged CSR entries per thread
     constexpr int ROWB = D * BITS / 8;                 // code bytes per token
-    // threads per token for the sparse V terms (one head: its even and odd
-    // entries on two threads, so all 8 waves take part; with more heads the
-    // LDS adds per entry dominate and 4 waves keep the other 4 free)
-    constexpr int VSP = G == 1 ? 2 : 1;
-    constexpr int kVsRows = 4 * VSP;                   // sparse V sums, one row per wave
-    constexpr int kVsBytes = kVsRows * G * D * 4;
+    // Sparse V terms.  With up to 2 heads: LDS adds into per-wave rows, a
+    // token's even and odd entries on two threads (all 8 waves take part).
+    // With 4 or more heads (one LDS add per entry and head) the outliers are
+    // folded into the dequantised values instead, through a per-wave fp16
+    // tile of the step's RPS tokens.
+    constexpr bool VTILE = G >= 4;
+    constexpr int VSP = 2;                             // threads per token
+    constexpr int kVsRows = 4 * VSP;                   // one row per wave
+    constexpr int kTileBytes = RPS * D * 2;            // 1 KB
+    constexpr int kVsBytes = VTILE ? kFastWaves * kTileBytes : kVsRows * G * D * 4;
     constexpr int kRedBytes = 4 * G * D * 4;
     constexpr int kCsrBytes = kRedBytes > kFastCap * 4 ? kRedBytes : kFastCap * 4;
     static_assert(kTPS * kFastGroups / 4 <= 128 && kTPS * kMaxRank / 4 <= kFastThreads &&
@@ -874,7 +878,7 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     // token t by thread t + kTPS (i mod VSP), one LDS add each (a wave's adds
     // execute in program order, rows are per wave, so the sums are
     // deterministic)
-    if (tid < kTPS * VSP) {
+    if (!VTILE && tid < kTPS * VSP) {
         const int t = tid & (kTPS - 1), par = tid / kTPS;
         float pt[G];
 #pragma unroll
@@ -898,6 +902,7 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
     }
+    uint16_t* tile = reinterpret_cast<uint16_t*>(s_big + kCsrBytes) + wv * (kTileBytes / 2);
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
         const int tok = tok0 + s * RPS;
@@ -905,14 +910,44 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
         const float av = colq < r ? s_a[aidx0 + s * astep] : 0.0f;
         float cf[8];
         unpack8<BITS>(wvv[s], cf);
+        if constexpr (VTILE) {
+            // the V outliers of the wave's RPS tokens of this step into its tile
+            // (the LPR lanes of a token take its entries in turn), this lane's 8
+            // values read back, its 16 bytes cleared (LDS operations of one wave
+            // execute in order; each step's instructions are kept to the step)
+            __builtin_amdgcn_sched_barrier(0);
+            const int kb = s_rv[tok], ke = s_rv[tok + 1];
+            for (int k = kb + colq; k < ke; k += LPR) {
+                const uint32_t e = stg_v ? s_cv[k - beg_v] : ((uint32_t)colv[k] | ((uint32_t)valv[k] << 16));
+                tile[rl * D + (e & (D - 1))] = (uint16_t)(e >> 16);
+            }
+            __builtin_amdgcn_wave_barrier();
+            uint4* mine = reinterpret_cast<uint4*>(tile + rl * D + colq * 8);
+            const uint4 sv4 = *mine;
+            *mine = make_uint4(0u, 0u, 0u, 0u);
+            __builtin_amdgcn_wave_barrier();
+            const uint32_t sw[4] = {sv4.x, sv4.y, sv4.z, sv4.w};
+            float dv[8];   // code scale + outlier (a mixed fma), zero added below
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float pp = s_sc[tok * G + h];
-            pa[h] = fmaf(pp, av, pa[h]);
-            pz[h] = fmaf(pp, zpv, pz[h]);
-            const float ps = pp * scv;
+            for (int e = 0; e < 8; ++e) dv[e] = fmaf(cf[e], scv, h2f(sw[e >> 1] >> (16 * (e & 1))));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ps, cf[e], acc[h][e]);
+            for (int h = 0; h < G; ++h) {
+                const float pp = s_sc[tok * G + h];
+                pa[h] = fmaf(pp, av, pa[h]);
+                pz[h] = fmaf(pp, zpv, pz[h]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pp, dv[e], acc[h][e]);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float pp = s_sc[tok * G + h];
+                pa[h] = fmaf(pp, av, pa[h]);
+                pz[h] = fmaf(pp, zpv, pz[h]);
+                const float ps = pp * scv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ps, cf[e], acc[h][e]);
+            }
         }
     }
 #pragma unroll
@@ -965,8 +1000,9 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
         const int h = i / D, j = i % D;
         const float* vs = s_vs + h * D + j;   // row w at vs[w * G * D]
         constexpr int RS = G * D;
-        float sp = (vs[0 * RS] + vs[1 * RS]) + (vs[2 * RS] + vs[3 * RS]);
-        if (kVsRows == 8) sp += (vs[4 * RS] + vs[5 * RS]) + (vs[6 * RS] + vs[7 * RS]);
+        float sp = 0.0f;
+        if (!VTILE) sp = (vs[0 * RS] + vs[1 * RS]) + (vs[2 * RS] + vs[3 * RS]);
+        if (!VTILE && kVsRows == 8) sp += (vs[4 * RS] + vs[5 * RS]) + (vs[6 * RS] + vs[7 * RS]);
         part[h * (D + 2) + j] = (s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j]) +
                                 (s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j]) + sp;
     }
