@@ -10,9 +10,9 @@
 // loads of all its tokens (one 32- or 16-bit code word, the group's scale and
 // zero, the token's A row) and the block's row pointers before computing.
 // The block's CSR entries (one contiguous range) are then loaded coalesced
-// into LDS and written into a dense fp16 LDS tile (one thread per row, in CSR
-// order), read back as 8 values per lane; each lane writes 8 fp16 values as
-// one 16-byte store.
+// into LDS and written into a dense fp16 LDS tile (each row's entries shared
+// out over kThreads / rows threads), read back as 8 values per lane; each lane
+// writes 8 fp16 values as one 16-byte store.
 #include "gear_internal.h"
 
 namespace gear {
@@ -139,10 +139,17 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
             if (tid + j * kThreads < cnt) s_cv[tid + j * kThreads] = ent[j];
         __syncthreads();
     }
-    for (int i = tid; i < nrows; i += kThreads) {
-        for (int k = s_rp[i]; k < s_rp[i + 1]; ++k) {
-            const uint32_t e = staged ? s_cv[k - beg] : ((uint32_t)cm[k] | ((uint32_t)vm[k] << 16));
-            s_s[i * D + (e & (D - 1))] = (uint16_t)(e >> 16);
+    // into the dense tile: a row's entries shared out over TPR threads (all
+    // waves take part; each (row, column) is written once)
+    {
+        constexpr int TPR = kThreads / ROWS_WG;
+        static_assert(TPR >= 1 && kThreads % ROWS_WG == 0, "threads per row");
+        const int i = tid / TPR, par = tid % TPR;
+        if (i < nrows) {
+            for (int k = s_rp[i] + par; k < s_rp[i + 1]; k += TPR) {
+                const uint32_t e = staged ? s_cv[k - beg] : ((uint32_t)cm[k] | ((uint32_t)vm[k] << 16));
+                s_s[i * D + (e & (D - 1))] = (uint16_t)(e >> 16);
+            }
         }
     }
     float Bm[8][RKX];
