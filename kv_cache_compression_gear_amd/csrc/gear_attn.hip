@@ -602,8 +602,9 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 //      codes, scales, zeros and A rows are issued after the K scores and
 //      consumed after the softmax.
 // 8 waves; wave w takes tokens [32 w, 32 w + 32), RPS per step.  The sparse
-// V terms p_t s_tj go to a per-wave LDS row (one LDS add per entry), added
-// to the wave's sums at the end.
+// V terms p_t s_tj go to per-wave LDS rows (one LDS add per entry and head)
+// with one or two query heads per KV head; with more they are folded into
+// the dequantised values through a per-wave tile of the step's tokens.
 constexpr int kFastCap = 2048;     // outliers of one matrix split staged
 constexpr int kFastGroups = 2;     // quantization groups per token staged
 constexpr int kFastWaves = 8;
