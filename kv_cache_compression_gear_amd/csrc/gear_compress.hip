@@ -867,19 +867,31 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 if (row < rows && colq == 0) st_at<int32_t>(rp, (uint32_t)row * 4, (int32_t)pos);
                 uint32_t m = om[u];
                 const uint4 xw = xr[u];
-                while (m != 0u) {
-                    const uint32_t e = (uint32_t)__builtin_ctz(m);
-                    m &= m - 1u;
-                    // the dword holding column e, picked with bit selects
+                // column e of the lane and its fp16 bits (the dword holding it
+                // picked with bit selects)
+                auto emit = [&](uint32_t e, uint32_t at) {
                     const uint32_t s1 = 0u - ((e >> 1) & 1u), s2 = 0u - ((e >> 2) & 1u);
                     const uint32_t lo2 = xw.x ^ ((xw.x ^ xw.y) & s1);
                     const uint32_t hi2 = xw.z ^ ((xw.z ^ xw.w) & s1);
                     const uint32_t w = lo2 ^ ((lo2 ^ hi2) & s2);
-                    if (pos < kk) {
-                        st_at<uint16_t>(cm, pos * 2, (uint16_t)(colq * 8 + e));
-                        st_at<uint16_t>(vm, pos * 2, (uint16_t)((e & 1u) ? (w >> 16) : w));
+                    if (at < kk) {
+                        st_at<uint16_t>(cm, at * 2, (uint16_t)(colq * 8 + e));
+                        st_at<uint16_t>(vm, at * 2, (uint16_t)((e & 1u) ? (w >> 16) : w));
                     }
-                    ++pos;
+                };
+                // a lane rarely holds more than two outliers of a row: the
+                // first two without a loop, the rest in one
+                if (__ballot(m != 0u) != 0ull) {   // wave-uniform
+                    const uint32_t m1 = m & (m - 1u), m2 = m1 & (m1 - 1u);
+                    if (m != 0u) emit((uint32_t)__builtin_ctz(m), pos);
+                    if (m1 != 0u) emit((uint32_t)__builtin_ctz(m1), pos + 1u);
+                    pos += 2u;
+                    m = m2;
+                    while (m != 0u) {
+                        emit((uint32_t)__builtin_ctz(m), pos);
+                        m &= m - 1u;
+                        ++pos;
+                    }
                 }
                 base += (tot >> (16 * u)) & 0xffffu;
             }
