@@ -30,6 +30,16 @@
 namespace gear {
 namespace {
 
+// Work-item and workgroup ids read from the hardware registers.  This file is
+// built with IEEE mode off, and the device library's id functions (built with
+// it on) are then not inlined: as calls, they return the ids in vector
+// registers, so everything derived from the workgroup id (the matrix, its base
+// addresses and its selection results) would be held and computed per lane.
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ uint32_t group_id() { return __builtin_amdgcn_workgroup_id_x(); }
+// wave index within the workgroup, known to the compiler as wave-uniform
+__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
 __device__ __forceinline__ float h2f(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
@@ -204,10 +214,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     __shared__ uint32_t s_tmp[NW];
     __shared__ uint32_t s_res[4 + kCompressWaves];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
-    const int64_t mm = blockIdx.x;
+    const int64_t mm = group_id();
     const int rows = o.rows;
     const uint32_t kk = (uint32_t)o.k;
     uint32_t* sel = a.sel + (size_t)mm * kSelStride;
@@ -734,10 +744,10 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     __shared__ double s_g[RKX * RKX];
     __shared__ double s_m[RKX * RKX];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
-    const int64_t mm = blockIdx.x;
+    const int64_t mm = group_id();
     const int rows = o.rows;
     const int bits = o.bits;
     const int gl = GL > 0 ? GL : o.group / 8, ngr = D / (8 * gl);
@@ -825,10 +835,17 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             }
             om[u] = (bits2 | (bits2 >> 16)) & 0xffu;
             if (split) {   // wave-uniform: the one block whose ties are split
-                uint32_t eqm = 0u;
+                // key == tk per 16-bit half: (key ^ tk) - 1 is negative
+                // exactly for a zero half (both are 15-bit)
+                const uint32_t tk2 = ((uint32_t)tk & 0x7fffu) * 0x10001u;
+                uint32_t eq2 = 0u;
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    eqm |= (valid && (int)((d[e >> 1] >> (16 * (e & 1))) & 0x7fffu) == tk) ? (1u << e) : 0u;
+                for (int i = 0; i < 4; ++i) {
+                    const s2v z = __builtin_bit_cast(s2v, (d[i] & 0x7fff7fffu) ^ tk2) - (s2v){1, 1};
+                    const uint32_t m = __builtin_bit_cast(uint32_t, z >> (s2v){15, 15});
+                    eq2 |= m & ((1u << (2 * i)) | (1u << (2 * i + 17)));
+                }
+                const uint32_t eqm = valid ? (eq2 | (eq2 >> 16)) & 0xffu : 0u;
                 if (__ballot(eqm != 0u) != 0ull && ties_seen < take_w) {
                     uint32_t tot;
                     uint32_t r = ties_seen + wave_excl_scan(__builtin_popcount(eqm), lane, &tot);
@@ -922,8 +939,12 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             group_minmax<GL>(mn, mx, gl);
             const float y = mx - mn;
             const float q0 = y * rq;
-            const float sc = fmaf(fmaf(-q0, qmax, y), rq, q0) + 0.0f;   // RN(y / qmax), +0 for 0
-            const float inv = sc != 0.0f ? __builtin_amdgcn_rcpf(sc) : 0.0f;
+            // RN(y / qmax); y = +0 gives +0 (every term is +0 or a +0 - 0 sum)
+            const float sc = fmaf(fmaf(-q0, qmax, y), rq, q0);
+            // a finite reciprocal also for sc = 0 (then every t is 0 and its
+            // code 0); for a tiny sc the near-tie test below sends the group
+            // to the exact division
+            const float inv = fminf(__builtin_amdgcn_rcpf(sc), 3.4028234664e38f);
             // t * inv is within a few ulp of the correctly rounded quotient, so
             // rint can differ from it only when t / sc is within 1e-5 of a
             // half-integer, that is when |R| > 0.49999 sc
@@ -938,7 +959,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 R[e] = fmaf(-cf[e], sc, t[e]);
                 near_tie |= fabsf(R[e]) > hs;
             }
-            if (__ballot(near_tie) != 0ull && near_tie) {
+            if (near_tie) {
                 // round the exact quotient
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
@@ -1180,7 +1201,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     constexpr int NX = CPL / 8;               // 16-byte chunks of X per lane
     constexpr int ROWS_W = 16 * kLrSteps, ROWS_WG = 4 * ROWS_W;
     typedef float f4v __attribute__((ext_vector_type(4)));
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int rr = lane & 15, q = lane >> 4;
     const Packed& o = a.out;
     const int rows = o.rows, rank = o.rank;
@@ -1189,8 +1210,8 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const int ngl = g >= CPL ? 1 : CPL / g;   // groups within a lane's columns (<= 4)
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
-    const int64_t mm = blockIdx.x / nblk;
-    const int blk = (int)(blockIdx.x % nblk);
+    const int64_t mm = group_id() / nblk;
+    const int blk = (int)(group_id() % nblk);
     const int r0 = blk * ROWS_WG + wv * ROWS_W;
     const int c0 = CPL * q;                   // first column of this lane
     // per-matrix bases; 32-bit offsets below (rows * D * 2 < 2^32)
