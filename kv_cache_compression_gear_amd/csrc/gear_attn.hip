@@ -179,10 +179,10 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float s_tile[4 * RPS * D];
     __shared__ float s_pa[4 * G * kMaxRank];
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const int nsp = a.splits - a.split0;   // splits [split0, splits) of every (b, kv-head)
-    const int pair = blockIdx.x / nsp, split = a.split0 + blockIdx.x % nsp;
+    const int pair = (int)(group_id_x() / nsp), split = a.split0 + (int)(group_id_x() % nsp);
     const int b = pair / a.Hkv, hk = pair % a.Hkv;
     const int pt = a.prompt.count ? a.prompt.chunks * a.prompt.p.rows : 0;
     const int N = pt + a.fills.count * a.fills.p.rows + a.buf_len;
@@ -674,10 +674,10 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     float* s_vs = reinterpret_cast<float*>(s_big + kCsrBytes);
     float* s_red = reinterpret_cast<float*>(s_big);
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     // grid (split0, Hkv, B)
-    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int split = (int)group_id_x(), hk = (int)group_id_y(), b = (int)group_id_z();
     const int pair = b * a.Hkv + hk;
     const int t0 = split * kTPS;
     const Piece pc = find_piece(a, b, hk, t0, t0 + kTPS);
@@ -1021,11 +1021,11 @@ __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
     __shared__ float s_m[kThreads / 64];
     __shared__ float s_num[kThreads];
     __shared__ float s_den[kThreads];
-    const int bh = blockIdx.x;                 // b * Hq + hq
+    const int bh = (int)group_id_x();                 // b * Hq + hq
     const int b = bh / a.Hq, hq = bh % a.Hq;
     const int hk = hq / G, h = hq % G;
     const int pair = b * a.Hkv + hk;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const float* base = a.partial + ((size_t)pair * a.splits * G + h) * (D + 2);
     const size_t stride = (size_t)G * (D + 2);   // between splits
     float m = -INFINITY;
@@ -1112,12 +1112,13 @@ hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
 
 __global__ void buffer_append_kernel(const uint16_t* k_new, const uint16_t* v_new, uint16_t* buf,
                                      int B, int H, int d, int cap, int pos, int n_new,
-                                     int src_tokens, int src_off) {
-    // one thread per 8 fp16 values (16 bytes)
+                                     int src_tokens, int src_off, int nblocks) {
+    // one thread per 8 fp16 values (16 bytes); a grid-stride loop over nblocks
+    // workgroups of kThreads
     const int per_row = d / 8;
     const size_t total = (size_t)2 * B * H * n_new * per_row;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (size_t)gridDim.x * blockDim.x) {
+    for (size_t i = (size_t)group_id_x() * kThreads + thread_id(); i < total;
+         i += (size_t)nblocks * kThreads) {
         const int c8 = (int)(i % per_row);
         size_t rest = i / per_row;
         const int tok = (int)(rest % n_new);
@@ -1161,7 +1162,7 @@ hipError_t launch_buffer_append(const uint16_t* k_new, const uint16_t* v_new, ui
     if (blocks > 4096) blocks = 4096;
     Timed t(kKBufferAppend, st);
     hipLaunchKernelGGL(buffer_append_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, st, k_new,
-                       v_new, buf, B, H, d, cap, pos, n_new, src_tokens, src_off);
+                       v_new, buf, B, H, d, cap, pos, n_new, src_tokens, src_off, (int)blocks);
     return hipGetLastError();
 }
 

@@ -30,16 +30,6 @@
 namespace gear {
 namespace {
 
-// Work-item and workgroup ids read from the hardware registers.  This file is
-// built with IEEE mode off, and the device library's id functions (built with
-// it on) are then not inlined: as calls, they return the ids in vector
-// registers, so everything derived from the workgroup id (the matrix, its base
-// addresses and its selection results) would be held and computed per lane.
-__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
-__device__ __forceinline__ uint32_t group_id() { return __builtin_amdgcn_workgroup_id_x(); }
-// wave index within the workgroup, known to the compiler as wave-uniform
-__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
-
 __device__ __forceinline__ float h2f(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
@@ -217,7 +207,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
-    const int64_t mm = group_id();
+    const int64_t mm = group_id_x();
     const int rows = o.rows;
     const uint32_t kk = (uint32_t)o.k;
     uint32_t* sel = a.sel + (size_t)mm * kSelStride;
@@ -747,7 +737,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
-    const int64_t mm = group_id();
+    const int64_t mm = group_id_x();
     const int rows = o.rows;
     const int bits = o.bits;
     const int gl = GL > 0 ? GL : o.group / 8, ngr = D / (8 * gl);
@@ -1210,8 +1200,8 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const int ngl = g >= CPL ? 1 : CPL / g;   // groups within a lane's columns (<= 4)
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
-    const int64_t mm = group_id() / nblk;
-    const int blk = (int)(group_id() % nblk);
+    const int64_t mm = group_id_x() / nblk;
+    const int blk = (int)(group_id_x() % nblk);
     const int r0 = blk * ROWS_WG + wv * ROWS_W;
     const int c0 = CPL * q;                   // first column of this lane
     // per-matrix bases; 32-bit offsets below (rows * D * 2 < 2^32)

@@ -55,12 +55,12 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     __shared__ int32_t s_rp[ROWS_WG + 1];
     __shared__ uint32_t s_cv[kCsrCap];   // column | fp16 value << 16
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const int rows = p.rows;
     const int blocks_per_mat = (rows + ROWS_WG - 1) / ROWS_WG;
-    const int64_t mm = blockIdx.x / blocks_per_mat;
-    const int row0 = (int)(blockIdx.x % blocks_per_mat) * ROWS_WG;
+    const int64_t mm = group_id_x() / blocks_per_mat;
+    const int row0 = (int)(group_id_x() % blocks_per_mat) * ROWS_WG;
     const int nrows = min(ROWS_WG, rows - row0);
     const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
 

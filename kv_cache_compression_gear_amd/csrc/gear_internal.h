@@ -15,6 +15,18 @@ constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v, size_t a = kAlign) { return (v + a - 1) / a * a; }
 
+// Work-item and workgroup ids read from the hardware registers.  In a file
+// built with IEEE mode off, the device library's id functions (built with it
+// on) are not inlined: as calls they return the ids in vector registers, and
+// everything derived from a workgroup id (base addresses, per-block
+// parameters) would then be held and computed per lane.
+__device__ __forceinline__ int thread_id() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ uint32_t group_id_x() { return __builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ uint32_t group_id_y() { return __builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ uint32_t group_id_z() { return __builtin_amdgcn_workgroup_id_z(); }
+// wave index within the workgroup, known to the compiler as wave-uniform
+__device__ __forceinline__ int wave_id(int tid) { return __builtin_amdgcn_readfirstlane(tid >> 6); }
+
 // Loads and stores at a 32-bit byte offset from a (workgroup-uniform) base, so
 // that the address is formed as base + zero-extended offset in one step (the
 // scalar-base addressing form), not with 64-bit vector arithmetic.
