@@ -622,69 +622,53 @@ __device__ __forceinline__ f16v mma3(const h8v& hi_i, const h8v& lo_i, const h8v
     return acc;
 }
 
-// This wave's 32x32 blocks (I, J), I <= J, of C = R^T R, in column units of
-// 32.  D = 128 (10 blocks): waves 0..3 take (w,w) and (w,w+1) (wave 3:
-// (3,3) and (0,3)), wave 4 takes (0,2), wave 5 (1,3).  D = 64 (3 blocks):
-// waves 0..2 take (0,0), (0,1), (1,1).
+// This wave's 32x32 blocks of C = R^T R, in column units of 32: a diagonal
+// block (X, X) and/or an off-diagonal block (X, Y) (C is symmetric, so (X, Y)
+// also gives (Y, X)).  D = 128 (10 blocks): waves 0..3 take (w, w) and
+// (w, (w + 1) mod 4), waves 4 and 5 take (w - 4, w - 2).  D = 64 (3 blocks):
+// wave 0 takes (0, 0), wave 1 (0, 1), wave 2 (1, 1).
+struct WaveBlocks {
+    int X, Y;
+    bool diag, off;
+};
 template <int D>
-__device__ __forceinline__ int blocks_of(int wv) {
-    return D == 128 ? (wv < 4 ? 2 : wv < 6 ? 1 : 0) : (wv < 3 ? 1 : 0);
-}
-template <int D>
-__device__ __forceinline__ void block_of(int wv, int b, int& I, int& J) {
+__device__ __forceinline__ WaveBlocks wave_blocks(int wv) {
     if (D == 128) {
-        if (wv < 4) {
-            I = b == 0 ? wv : (wv == 3 ? 0 : wv);
-            J = b == 0 ? wv : (wv == 3 ? 3 : wv + 1);
-        } else {
-            I = wv - 4;
-            J = wv - 2;
-        }
-    } else {
-        I = wv == 2 ? 1 : 0;
-        J = wv == 0 ? 0 : 1;
+        if (wv < 4) return {wv, (wv + 1) & 3, true, true};
+        return {wv - 4, wv - 2, false, wv < 6};
     }
+    return {wv == 2 ? 1 : 0, 1, wv != 1 && wv < 3, wv == 1};
 }
 
-// This wave's Gram blocks over one slab.  The blocks use at most two column
-// blocks X and Y of R; per 16-row chunk each one's hi and lo operands are
-// read once, and the next chunk's operands are read while this chunk's
-// MFMAs run (two register sets, alternating).
+// This wave's Gram blocks over one slab: acc[0] += the diagonal block,
+// acc[1] += the off-diagonal one.  Per 16-row chunk the hi and lo operands of
+// column blocks X (and Y) are read once, and the next chunk's operands are
+// read while this chunk's MFMAs run (two register sets, alternating).  Each
+// accumulator has one update, skipped or not as a whole (wave-uniform), and
+// never a choice between two updates: the compiler would give the two their
+// own registers and copy the result back, waiting for the MFMAs to finish.
 template <int D>
 __device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane, f16v (&acc)[2]) {
     constexpr int kPlane = kSlabRows * D * 2;
     const unsigned char* hi = slab;
     const unsigned char* lo = slab + kPlane;
-    const int nb = blocks_of<D>(wv);
-    if (nb == 0) return;   // wave-uniform
-    int I0, J0, I1 = 0, J1 = 0;
-    block_of<D>(wv, 0, I0, J0);
-    if (nb > 1) block_of<D>(wv, 1, I1, J1);
-    const int X = I0;
-    const int Y = J0 != X ? J0 : (nb > 1 ? (I1 != X ? I1 : J1) : X);
-    const bool useY = Y != X;
-    const bool diag0 = J0 == X;          // block 0: (X, X), else (X, Y)
-    const bool ymajor1 = I1 != X;        // block 1: (Y, X), else (X, Y)
+    const WaveBlocks wb = wave_blocks<D>(wv);
     h8v xh[2], xl[2], yh[2], yl[2];
-    auto rd = [&](int kc, int buf) {
-        xh[buf] = read_operand<D>(hi, 16 * kc, 32 * X, lane);
-        xl[buf] = read_operand<D>(lo, 16 * kc, 32 * X, lane);
-        if (useY) {
-            yh[buf] = read_operand<D>(hi, 16 * kc, 32 * Y, lane);
-            yl[buf] = read_operand<D>(lo, 16 * kc, 32 * Y, lane);
+    auto rd = [&](int kc, int buf, bool withY) {
+        xh[buf] = read_operand<D>(hi, 16 * kc, 32 * wb.X, lane);
+        xl[buf] = read_operand<D>(lo, 16 * kc, 32 * wb.X, lane);
+        if (withY) {
+            yh[buf] = read_operand<D>(hi, 16 * kc, 32 * wb.Y, lane);
+            yl[buf] = read_operand<D>(lo, 16 * kc, 32 * wb.Y, lane);
         }
     };
-    rd(0, 0);
+    rd(0, 0, wb.off);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
         const int c = kc & 1;
-        if (kc < 3) rd(kc + 1, c ^ 1);
-        if (diag0) acc[0] = mma3(xh[c], xl[c], xh[c], xl[c], acc[0]);
-        else acc[0] = mma3(xh[c], xl[c], yh[c], yl[c], acc[0]);
-        if (nb > 1) {
-            if (ymajor1) acc[1] = mma3(yh[c], yl[c], xh[c], xl[c], acc[1]);
-            else acc[1] = mma3(xh[c], xl[c], yh[c], yl[c], acc[1]);
-        }
+        if (kc < 3) rd(kc + 1, c ^ 1, wb.off);
+        if (wb.diag) acc[0] = mma3(xh[c], xl[c], xh[c], xl[c], acc[0]);
+        if (wb.off) acc[1] = mma3(xh[c], xl[c], yh[c], yl[c], acc[1]);
     }
 }
 
@@ -1023,12 +1007,11 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     __syncthreads();
     float* Cm = reinterpret_cast<float*>(s_big);
     {
-        const int nb = blocks_of<D>(wv);
+        const WaveBlocks wb = wave_blocks<D>(wv);
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            if (b >= nb) break;
-            int I, J;
-            block_of<D>(wv, b, I, J);
+            if (!(b == 0 ? wb.diag : wb.off)) continue;
+            const int I = wb.X, J = b == 0 ? wb.X : wb.Y;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int m = 8 * (v / 4) + 4 * (lane / 32) + (v % 4), n = lane % 32;
