@@ -30,6 +30,15 @@
 namespace gear {
 namespace {
 
+// Raw buffer view of [base, base + bytes) for stores: a store at an offset
+// past the end (kDrop) is dropped by the hardware, so a lane with nothing to
+// store still issues it.  Stores issued on every path let the compiler wait
+// for older loads without waiting for the stores issued after them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kDrop = 0x80000000u;
+
 __device__ __forceinline__ float h2f(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
 }
@@ -741,6 +750,9 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     unsigned char* codes_m = o.codes + (size_t)mm * rows * (D * bits / 8);
     float* scale_m = o.scale + (size_t)mm * rows * ngr;
     float* zero_m = o.zero + (size_t)mm * rows * ngr;
+    const auto codes_r = buffer_of(codes_m, (uint32_t)rows * (D * bits / 8));
+    const auto scale_r = buffer_of(scale_m, (uint32_t)rows * ngr * 4);
+    const auto zero_r = buffer_of(zero_m, (uint32_t)rows * ngr * 4);
 
     // ---- outlier rule from the selection, on keys (|x| bit patterns, monotone
     // in |x|): key > thrk, plus (in the one row block whose quota splits the
@@ -954,17 +966,18 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                         fmaf(cf[4 * i + 3], 64.0f, fmaf(cf[4 * i + 2], 16.0f, fmaf(cf[4 * i + 1], 4.0f, cf[4 * i]))),
                         i, word);
             }
-            if (valid) {
-                if (bits == 4)
-                    st_at<uint32_t>(codes_m, urow * (D / 2) + colq * 4, word);
-                else
-                    st_at<uint16_t>(codes_m, urow * (D / 4) + colq * 2, (uint16_t)word);
-                if ((colq % gl) == 0) {
-                    const uint32_t go = (urow * ngr + colq / gl) * 4;
-                    st_at<float>(scale_m, go, sc * rsx);
-                    st_at<float>(zero_m, go, (mn + 0.0f) * rsx);
-                }
+            // codes, and the group's scale and zero from its first lane
+            if (bits == 4) {
+                const uint32_t co = valid ? urow * (D / 2) + colq * 4 : kDrop;
+                __builtin_amdgcn_raw_buffer_store_b32(word, codes_r, (int)co, 0, 0);
+            } else {
+                const uint32_t co = valid ? urow * (D / 4) + colq * 2 : kDrop;
+                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, codes_r, (int)co, 0, 0);
             }
+            const uint32_t go = (valid && (colq % gl) == 0) ? (urow * ngr + colq / gl) * 4 : kDrop;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc * rsx), scale_r, (int)go, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, (mn + 0.0f) * rsx), zero_r,
+                                                  (int)go, 0, 0);
             if (LR) {
                 // fp16 hi (toward zero) + lo of R * 2^ex, row-major into the slab
                 uint32_t hw[4], lw[4];
