@@ -259,13 +259,17 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     if (tid < 4 + NB) s_res[tid] = 0u;
     __syncthreads();
 
+    // Loads are issued unconditionally (steps past the range read a valid row
+    // and are flagged), so that the compiler can count them and wait for one
+    // batch while the next is in flight; 32-bit offsets from the matrix base
+    // (rows * D * 2 < 2^32).
     auto load = [&](uint4 (&xr)[U], bool (&ok)[U], int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int row = wr0 + (s0 + u) * RPS + rl;
             ok[u] = s0 + u < se && row < rows;
-            xr[u] = ok[u] ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t rc = (uint32_t)min(row, rows - 1);
+            xr[u] = ld_at<uint4>(xm, (rc * D + colq * 8) * 2);
         }
     };
     // Thread t owns the BP consecutive bins (BP = elements of h) of a table of
@@ -306,8 +310,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
             const int s = s0 + q * kSampleEvery;
             const int row = wr0 + s * RPS + rl;
             ok[q] = s < se && row < rows;
-            xr[q] = ok[q] ? *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8)
-                          : make_uint4(0u, 0u, 0u, 0u);
+            const uint32_t rc = (uint32_t)min(row, rows - 1);
+            xr[q] = ld_at<uint4>(xm, (rc * D + colq * 8) * 2);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
