@@ -95,38 +95,6 @@ __device__ __forceinline__ float row_allreduce(float v) {
     return v;
 }
 
-// Lanes l ^ 16 and l ^ 32 through the gfx950 permlane swaps (no LDS): each
-// swap leaves a lane's own value in one result and its partner's in the
-// other, so op(first, second) is the same in both partners.  Both results
-// are pinned as integers before they are read as floats: reading them as
-// floats directly, this compiler takes the first result for both.
-template <bool S32>
-__device__ __forceinline__ void swap_pair(float v, float& a, float& b) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, v);
-    uint32_t x, y;
-    if (S32) {
-        const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-        x = p[0];
-        y = p[1];
-    } else {
-        const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        x = p[0];
-        y = p[1];
-    }
-    asm("" : "+v"(x), "+v"(y));
-    a = __builtin_bit_cast(float, x);
-    b = __builtin_bit_cast(float, y);
-}
-__device__ __forceinline__ float sum_xor16(float v) {
-    float a, b;
-    swap_pair<false>(v, a, b);
-    return a + b;
-}
-__device__ __forceinline__ float sum_xor32(float v) {
-    float a, b;
-    swap_pair<true>(v, a, b);
-    return a + b;
-}
 __device__ __forceinline__ float max_xor16(float v) {
     float a, b;
     swap_pair<false>(v, a, b);

@@ -1210,10 +1210,28 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const unsigned char* cb = o.codes + (size_t)mm * rows * (D * bits / 8);
     const float* scb = o.scale + (size_t)mm * rows * ngr;
     const float* zpb = o.zero + (size_t)mm * rows * ngr;
-    float Bv[CPL];                            // B operand: Bf[c0 + j][n = rr]
+    // rank <= 4 with one group per lane: A on the VALU (lane (rr, q) sums
+    // over its CPL columns, then the four lane groups are added); otherwise on
+    // the matrix cores (at rank 8 they do twice the useful work per
+    // instruction, and with several groups per lane the compiler would hold
+    // all of B's rows in registers)
+    constexpr bool VPATH = RK <= 4 && ONEG;
+    float Bv[VPATH ? 1 : CPL];                // MFMA B operand: Bf[c0 + j][n = rr]
+    __shared__ __attribute__((aligned(16))) float s_bm[VPATH ? D * 4 : 4];   // Bf rows, padded to 4
+    if constexpr (VPATH) {
+        if (tid < D) {
+            const float* src = a.bf + ((size_t)mm * D + tid) * RK;
+            f4v v = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (RK == 4) v = *reinterpret_cast<const f4v*>(src);
+            else v = f4v{src[0], src[1], 0.0f, 0.0f};
+            reinterpret_cast<f4v*>(s_bm)[tid] = v;
+        }
+        __syncthreads();
+    } else {
 #pragma unroll
-    for (int jj = 0; jj < CPL; ++jj)
-        Bv[jj] = rr < RK ? a.bf[((size_t)mm * D + c0 + jj) * RK + rr] : 0.0f;
+        for (int jj = 0; jj < CPL; ++jj)
+            Bv[jj] = rr < RK ? a.bf[((size_t)mm * D + c0 + jj) * RK + rr] : 0.0f;
+    }
 
     // outlier rule on keys (|x| bit patterns): key > thrk, thrk = T - 1 in the
     // rows that take all ties at key T, T elsewhere, 0x7fff without outliers;
@@ -1311,6 +1329,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
             }
         }
         f4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        float av[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // VALU path: this lane's partial A row
         const uint32_t cwd[4] = {bf.cw.x, bf.cw.y, bf.cw.z, bf.cw.w};
 #pragma unroll
         for (int c = 0; c < NX; ++c) {
@@ -1348,10 +1367,30 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
                 // R = (x or 0) - zero - code * scale; x - zero in one mixed fma
                 const float xz = fmaf(h2f(dm[e >> 1] >> (16 * (e & 1))), one, -zpv);
                 const float R = fmaf(-cf[e], scv, xz);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(R, Bv[jj], acc, 0, 0, 0);
+                if constexpr (VPATH) {
+                    const f4v bm = reinterpret_cast<const f4v*>(s_bm)[c0 + jj];
+#pragma unroll
+                    for (int c2 = 0; c2 < RK; ++c2) av[c2] = fmaf(R, bm[c2], av[c2]);
+                } else {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(R, Bv[jj], acc, 0, 0, 0);
+                }
             }
         }
-        if (rr < rank) {
+        if constexpr (VPATH) {
+            // the row's sums over the four lane groups (lanes rr + 16 q)
+#pragma unroll
+            for (int c2 = 0; c2 < RK; ++c2) av[c2] = sum_xor32(sum_xor16(av[c2]));
+            if (q == 0 && valid) {
+                float* dst = Am + (size_t)row * rank;
+                if (RK == 4 && rank == 4) {
+                    *reinterpret_cast<f4v*>(dst) = f4v{av[0], av[1], av[2], av[3]};
+                } else {
+#pragma unroll
+                    for (int c2 = 0; c2 < RK; ++c2)
+                        if (c2 < rank) dst[c2] = av[c2];
+                }
+            }
+        } else if (rr < rank) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int orow = r0 + s * 16 + 4 * q + i;
