@@ -263,9 +263,10 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     // and are flagged), so that the compiler can count them and wait for one
     // batch while the next is in flight; 32-bit offsets from the matrix base
     // (rows * D * 2 < 2^32).
-    auto load = [&](uint4 (&xr)[U], bool (&ok)[U], int s0) {
+    auto load = [&](auto& xr, auto& ok, int s0) {
+        constexpr int UU = sizeof(ok) / sizeof(ok[0]);
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < UU; ++u) {
             const int row = wr0 + (s0 + u) * RPS + rl;
             ok[u] = s0 + u < se && row < rows;
             const uint32_t rc = (uint32_t)min(row, rows - 1);
@@ -456,9 +457,12 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     // ---- fallback: radix select over all keys (4096 coarse bins, then 8 fine)
     for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
     __syncthreads();
-    auto hist = [&](const uint4 (&xr)[U], const bool (&ok)[U]) {
+    // (the fallback is rare: its passes take one step at a time, so that its
+    // registers do not set the common path's register budget)
+    constexpr int UF = 1;
+    auto hist = [&](const uint4 (&xr)[UF], const bool (&ok)[UF]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u)
+        for (int u = 0; u < UF; ++u)
             if (ok[u]) {
                 const uint32_t w4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
 #pragma unroll
@@ -466,16 +470,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
                     atomicAdd(&s_hist[__builtin_amdgcn_ubfe(w4[e >> 1], (e & 1) ? 19u : 3u, 12u)], 1u);
             }
     };
-    {
-        uint4 xa[U], xb[U];
-        bool oka[U], okb[U];
-        load(xa, oka, sb);
-        for (int s0 = sb; s0 < se; s0 += 2 * U) {
-            load(xb, okb, s0 + U);
-            hist(xa, oka);
-            load(xa, oka, s0 + 2 * U);
-            hist(xb, okb);
-        }
+    for (int s0 = sb; s0 < se; s0 += UF) {
+        uint4 xa[UF];
+        bool oka[UF];
+        load(xa, oka, s0);
+        hist(xa, oka);
     }
     __syncthreads();
     {
@@ -488,9 +487,9 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     }
     const uint32_t bstar = s_res[2];
     uint32_t my_above = 0;
-    auto fine = [&](const uint4 (&xr)[U], const bool (&ok)[U]) {
+    auto fine = [&](const uint4 (&xr)[UF], const bool (&ok)[UF]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int u = 0; u < UF; ++u) {
             const uint32_t w4[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
             bool any = false;
 #pragma unroll
@@ -508,16 +507,11 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
             }
         }
     };
-    {
-        uint4 xa[U], xb[U];
-        bool oka[U], okb[U];
-        load(xa, oka, sb);
-        for (int s0 = sb; s0 < se; s0 += 2 * U) {
-            load(xb, okb, s0 + U);
-            fine(xa, oka);
-            load(xa, oka, s0 + 2 * U);
-            fine(xb, okb);
-        }
+    for (int s0 = sb; s0 < se; s0 += UF) {
+        uint4 xa[UF];
+        bool oka[UF];
+        load(xa, oka, s0);
+        fine(xa, oka);
     }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) my_above += __shfl_xor(my_above, off, 64);

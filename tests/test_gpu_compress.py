@@ -96,6 +96,32 @@ def test_compress_parity_full_tiny():
     _full("tiny", None)
 
 
+def test_compress_parity_select_fallback():
+    """Rows that the threshold's sample reads (the first 4 of every 64 at
+    head_dim 128) are scaled by 64 and s = 10% exceeds their share (1/16):
+    the sample places its key window among the scaled values while the k-th
+    largest |x| lies far below it, so the selection takes its radix path."""
+    n, d = 4096, 128
+    p = P(4, 128, 100000, 4, 3)
+    _say(f"[compress parity] select fallback: n={n} d={d} {p}")
+    g = torch.Generator().manual_seed(11)
+    x = torch.randn((2, n, d), generator=g, dtype=torch.float32)
+    x[:, (torch.arange(n) % 64) < 4, :] *= 64.0
+    x = x.to(torch.float16).to("cuda").contiguous()
+    ws = torch.empty(max(gear.compress_workspace_bytes(p, 2, n, d), 256), dtype=torch.uint8, device="cuda")
+    packed = gear.compress(x, p, workspace=ws)
+    xhat = gear.decompress(packed)
+    torch.cuda.synchronize()
+    op = to_orc_params(p)
+    rep = Report()
+    for m in range(2):
+        xm = x[m].cpu().numpy().view(np.uint16)
+        ref = orc.compress_matrix(np.ascontiguousarray(xm), op)
+        check_matrix(xm, packed, m, ref, p, rep, xhat[m].float().cpu().numpy())
+    _say(f"    {rep.summary()}")
+    assert rep.ties <= 1e-6 * max(rep.entries, 1) + 0.5
+
+
 def test_compress_is_deterministic():
     _say("[compress] two calls give identical bytes")
     syn = KVSynth(1, 2, 128, 4, seed=3, device="cuda")
