@@ -10,7 +10,7 @@
 //   A, B = t PowerSGD steps on R = D - deq(Q) from a fixed B0, L = A B^T.
 //
 // Design (MI355X): three launches per call.
-//   * select_kernel (8 waves per matrix): the threshold key T of the k-th
+//   * select_kernel (8 or 16 waves per matrix): the threshold key T of the k-th
 //     largest |x|, each row block's share of the ties at T and its first CSR
 //     position.  A 1/16 row sample places a 1024-key window that one exact
 //     counting pass resolves; a two-pass radix select is the fallback.
@@ -25,6 +25,8 @@
 //   The power steps are those of PowerSGD, with P = R B, A = orth(P),
 //   B = R^T A; orth is a Cholesky factorisation of P^T P = B^T C B, which in
 //   exact arithmetic is modified Gram-Schmidt on P, so L = A B^T is the same.
+#include <atomic>
+
 #include "gear_internal.h"
 
 namespace gear {
@@ -175,13 +177,13 @@ __device__ void gram_to_m(const double* G /* RK*RK symmetric, LDS */, double* Mo
 constexpr int kCoarse = 4096;   // pass-1 bins: |x| bit pattern >> 3
 constexpr int kFine = 8;        // pass-2 bins inside the chosen coarse bin
 constexpr int kFineSlot = kFine + 1;
-constexpr int kSelThreads = 512;
 
 // ---------------------------------------------------------------------------
 // Outlier threshold: the k-th largest |x| of a matrix, with ties broken by
-// the lower flat index.  One 8-wave workgroup per matrix (two fit on a CU).
-// The rows are split exactly as the compress kernel splits them over its 8
-// waves (wave_rows); wave b reads row block b.  Output per
+// the lower flat index.  One workgroup per matrix, of NT = 512 or 1024
+// threads (8 or 16 waves).  The rows are split exactly as the compress
+// kernel splits them over its 8 waves (wave_rows); row block b is read by
+// NT / 512 waves.  Output per
 // matrix (kSelStride words, layout in gear_internal.h): the threshold key T,
 // per row block the ties at T it takes, its first CSR position and the ties it
 // holds, and a key bounding |x| over the entries that are not outliers (T, or
@@ -193,18 +195,18 @@ constexpr int kSelThreads = 512;
 // every key above it.  If the k-th largest key lies in the window this is
 // the exact answer (checked from the counts); otherwise a two-pass radix
 // select over all keys (4096 coarse bins, then 8 fine bins) is used.
-template <int D, int U>
-__global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
+template <int D, int U, int NT>
+__global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR;
-    constexpr int NW = kSelThreads / 64;       // 8 waves
+    constexpr int NW = NT / 64;       // 8 or 16 waves
     constexpr int NB = kCompressWaves;         // row blocks
     constexpr int WPB = NW / NB;               // waves per row block
     // exact window of keys: one binade of fp16 (a factor of 2 in |x|); the
     // sample places L0 where ~25% more than k entries lie above, typically a
     // few dozen keys below the threshold.  A miss takes the radix path.
     constexpr int kWin = 1024;
-    constexpr int BPC = kCoarse / kSelThreads;   // coarse bins per thread
-    constexpr int BPW = kWin / kSelThreads;      // window bins per thread
+    constexpr int BPC = kCoarse / NT;   // coarse bins per thread
+    constexpr int BPW = kWin / NT;      // window bins per thread
     constexpr int kSampleEvery = 16;           // sample = every 16th step
     __shared__ uint32_t s_hist[kCoarse];
     __shared__ __attribute__((aligned(16))) uint32_t s_win[NB * kWin];
@@ -252,8 +254,8 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         }
         return;
     }
-    for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
-    for (int i = tid; i < NB * kWin / 4; i += kSelThreads)
+    for (int i = tid; i < kCoarse; i += NT) s_hist[i] = 0u;
+    for (int i = tid; i < NB * kWin / 4; i += NT)
         reinterpret_cast<uint4*>(s_win)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (tid < NW * kFineSlot) s_fine[tid] = 0u;
     if (tid < 4 + NB) s_res[tid] = 0u;
@@ -274,12 +276,12 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
         }
     };
     // Thread t owns the BP consecutive bins (BP = elements of h) of a table of
-    // BP * kSelThreads bins, the top ones first; returns the bin where the
+    // BP * NT bins, the top ones first; returns the bin where the
     // count from the top, started at `base`, reaches `target` (writes it to
     // *out; no write if never reached).
     auto find_bin = [&](const auto& h, uint32_t base, uint32_t target, uint32_t* out) {
         constexpr int BP = sizeof(h) / sizeof(h[0]);
-        const int b0 = (kSelThreads - 1 - tid) * BP;
+        const int b0 = (NT - 1 - tid) * BP;
         uint32_t sum = 0;
 #pragma unroll
         for (int q = 0; q < BP; ++q) sum += h[q];
@@ -336,7 +338,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     uint32_t L0 = 0;
     if (target <= total_samp) {
         uint32_t h[BPC];
-        const int b0 = (kSelThreads - 1 - tid) * BPC;
+        const int b0 = (NT - 1 - tid) * BPC;
 #pragma unroll
         for (int q = 0; q < BPC; ++q) h[q] = s_hist[b0 + q];
         find_bin(h, 0u, target, &s_res[0]);
@@ -394,7 +396,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     for (int w = 0; w < NW; ++w) above_tot += s_cnt[NW + w];
     {
         uint32_t h[BPW];
-        const int b0 = (kSelThreads - 1 - tid) * BPW;
+        const int b0 = (NT - 1 - tid) * BPW;
 #pragma unroll
         for (int q = 0; q < BPW; ++q) {
             h[q] = 0u;
@@ -409,7 +411,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     const uint32_t jstar = s_res[1];
     if (jstar != 0xffffffffu) {
         // exact threshold T = L0 + j*; per block: ties at T, count above T
-        const int b0 = (kSelThreads - 1 - tid) * BPW;
+        const int b0 = (NT - 1 - tid) * BPW;
         uint32_t gtp[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) gtp[b] = 0u;
@@ -455,7 +457,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     }
 
     // ---- fallback: radix select over all keys (4096 coarse bins, then 8 fine)
-    for (int i = tid; i < kCoarse; i += kSelThreads) s_hist[i] = 0u;
+    for (int i = tid; i < kCoarse; i += NT) s_hist[i] = 0u;
     __syncthreads();
     // (the fallback is rare: its passes take one step at a time, so that its
     // registers do not set the common path's register budget)
@@ -479,7 +481,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(CompressArgs a) {
     __syncthreads();
     {
         uint32_t h[BPC];
-        const int b0 = (kSelThreads - 1 - tid) * BPC;
+        const int b0 = (NT - 1 - tid) * BPC;
 #pragma unroll
         for (int q = 0; q < BPC; ++q) h[q] = s_hist[b0 + q];
         find_bin(h, 0u, kk, &s_res[2]);
@@ -1421,6 +1423,19 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     else run(BoolTag<false>{});
 }
 
+// Compute units of the current device, cached per device.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int D>
 constexpr int lowrank_rows_per_wg() { return 4 * 16 * kLrSteps; }
 
@@ -1429,7 +1444,13 @@ hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
     const unsigned M = (unsigned)a.out.M;
     if (a.out.k > 0 || RK > 0) {
         Timed t(kKSelect, st);
-        hipLaunchKernelGGL((select_kernel<D, 4>), dim3(M), dim3(kSelThreads), 0, st, a);
+        // 16 waves per matrix when the matrices are too few to give every CU
+        // more than two workgroups (their waves are then all a CU has to
+        // hide memory latency with), else 8
+        if ((int64_t)M <= 2 * (int64_t)cu_count())
+            hipLaunchKernelGGL((select_kernel<D, 4, 1024>), dim3(M), dim3(1024), 0, st, a);
+        else
+            hipLaunchKernelGGL((select_kernel<D, 4, 512>), dim3(M), dim3(512), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
