@@ -126,6 +126,52 @@ __device__ __forceinline__ float sum_rowgroups(float v) {
 constexpr int kAttnCsrCap = 2048;   // outliers of one piece staged in LDS
 constexpr int kAU = 4;              // token steps per batch of loads
 
+// out[b][hq][:] = merge over the pair's splits of (acc, max, sum), by the
+// kThreads threads of a workgroup; the splits are shared out over
+// kThreads / D threads per column.  s_m: kThreads / 64 floats, s_num and s_den:
+// kThreads floats each (LDS).
+template <int D, int G>
+__device__ __forceinline__ void merge_head(const AttnArgs& a, int pair, int bh, int h, float* s_m,
+                                           float* s_num, float* s_den) {
+    constexpr int NQ = kThreads / D;
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
+    const float* base = a.partial + ((size_t)pair * a.splits * G + h) * (D + 2);
+    const size_t stride = (size_t)G * (D + 2);   // between splits
+    float m = -INFINITY;
+    for (int s = tid; s < a.splits; s += kThreads) {
+        const float* part = base + s * stride;
+        if (part[D + 1] > 0.0f) m = fmaxf(m, part[D]);
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) s_m[wv] = m;
+    __syncthreads();
+    m = s_m[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, s_m[w]);
+    const int j = tid % D, q = tid / D;
+    float num = 0.0f, den = 0.0f;
+    for (int s = q; s < a.splits; s += NQ) {
+        const float* part = base + s * stride;
+        const float l = part[D + 1];
+        if (l > 0.0f) {
+            const float w = expf(part[D] - m);
+            num = fmaf(w, part[j], num);
+            den = fmaf(w, l, den);
+        }
+    }
+    s_num[tid] = num;
+    s_den[tid] = den;
+    __syncthreads();
+    if (q == 0) {
+        for (int qq = 1; qq < NQ; ++qq) {
+            num += s_num[qq * D + j];
+            den += s_den[qq * D + j];
+        }
+        a.out[(size_t)bh * D + j] = den > 0.0f ? num / den : 0.0f;
+    }
+}
+
 // One workgroup per (batch, kv-head, split of kTPS tokens).  Each token of a
 // compressed piece is read once per phase: 8 codes per lane (D/8 lanes per
 // token), the group's scale and zero, the token's A row; the piece's CSR rows
@@ -133,7 +179,9 @@ constexpr int kAU = 4;              // token steps per batch of loads
 // loads.  Phase 1 writes raw scores to LDS and adds the sparse term per row
 // (one thread per token, entries in CSR order); phase 2 folds each token's
 // sparse V entries into its dequantised values through a small per-wave LDS
-// tile that is scattered, read and cleared again.
+// tile that is scattered, read and cleared again.  When a pair has only one
+// split here (fuse_combine), its workgroup then merges all of the pair's
+// splits into out itself (no separate combine launch).
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TILE = 4 * RPS;
@@ -146,6 +194,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     __shared__ uint32_t s_cv[kAttnCsrCap];
     __shared__ __attribute__((aligned(16))) float s_tile[4 * RPS * D];
     __shared__ float s_pa[4 * G * kMaxRank];
+    __shared__ float s_mg[kThreads / 64 + 2 * kThreads];   // merge scratch (fuse_combine)
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
@@ -555,6 +604,20 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     if (tid < G) {
         part[tid * (D + 2) + D] = n > 0 ? s_stat[tid] : -INFINITY;
         part[tid * (D + 2) + D + 1] = n > 0 ? s_stat[G + tid] : 0.0f;
+    }
+    if (a.fuse_combine) {
+        // the pair's only split here: every other split was written by the
+        // prompt kernel, launched before on the same stream, and this one's
+        // by this workgroup (visible to it after the barrier)
+        __syncthreads();
+        float* s_m = s_mg;
+        float* s_num = s_mg + kThreads / 64;
+        float* s_den = s_num + kThreads;
+#pragma unroll 1
+        for (int h = 0; h < G; ++h) {
+            merge_head<D, G>(a, pair, b * a.Hq + hk * G + h, h, s_m, s_num, s_den);
+            __syncthreads();
+        }
     }
 }
 
@@ -981,54 +1044,15 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     }
 }
 
-// out[b][hq][:] = merge over splits of (acc, max, sum): 256 threads per
-// (b, hq); the splits are shared out over 256 / D lanes per column.
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
-    constexpr int NQ = kThreads / D;
     __shared__ float s_m[kThreads / 64];
     __shared__ float s_num[kThreads];
     __shared__ float s_den[kThreads];
     const int bh = (int)group_id_x();                 // b * Hq + hq
     const int b = bh / a.Hq, hq = bh % a.Hq;
     const int hk = hq / G, h = hq % G;
-    const int pair = b * a.Hkv + hk;
-    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
-    const float* base = a.partial + ((size_t)pair * a.splits * G + h) * (D + 2);
-    const size_t stride = (size_t)G * (D + 2);   // between splits
-    float m = -INFINITY;
-    for (int s = tid; s < a.splits; s += kThreads) {
-        const float* part = base + s * stride;
-        if (part[D + 1] > 0.0f) m = fmaxf(m, part[D]);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (lane == 0) s_m[wv] = m;
-    __syncthreads();
-    m = s_m[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, s_m[w]);
-    const int j = tid % D, q = tid / D;
-    float num = 0.0f, den = 0.0f;
-    for (int s = q; s < a.splits; s += NQ) {
-        const float* part = base + s * stride;
-        const float l = part[D + 1];
-        if (l > 0.0f) {
-            const float w = expf(part[D] - m);
-            num = fmaf(w, part[j], num);
-            den = fmaf(w, l, den);
-        }
-    }
-    s_num[tid] = num;
-    s_den[tid] = den;
-    __syncthreads();
-    if (q == 0) {
-        for (int qq = 1; qq < NQ; ++qq) {
-            num += s_num[qq * D + j];
-            den += s_den[qq * D + j];
-        }
-        a.out[(size_t)bh * D + j] = den > 0.0f ? num / den : 0.0f;
-    }
+    merge_head<D, G>(a, b * a.Hkv + hk, bh, h, s_m, s_num, s_den);
 }
 
 // Splits [0, split0) go to attn_prompt_kernel: the prompt's splits when every
@@ -1043,6 +1067,10 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
         D / a.prompt.p.group <= kFastGroups)
         a.split0 = min(a.splits, a.prompt.chunks * a.prompt.p.rows / kTPS);
     const unsigned pairs = (unsigned)(a.B * a.Hkv);
+    // one split of attn_split_kernel per pair and one query head per KV head:
+    // that workgroup also merges (with more heads it would merge them one
+    // after another, slower than the combine kernel's workgroup per head)
+    a.fuse_combine = (G == 1 && a.splits - a.split0 == 1) ? 1 : 0;
     hipError_t e;
     {
         Timed t(kKAttnSplit, st);
@@ -1058,7 +1086,7 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
                                0, st, a);
         e = hipGetLastError();
     }
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.fuse_combine) return e;
     {
         Timed t(kKAttnCombine, st);
         hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((unsigned)(a.B * a.Hq)), dim3(kThreads), 0, st, a);

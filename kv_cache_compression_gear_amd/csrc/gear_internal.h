@@ -169,6 +169,7 @@ struct AttnArgs {
     int32_t splits;
     int32_t tokens_per_split;
     int32_t split0;        // splits [0, split0) are whole prompt splits (fast kernel)
+    int32_t fuse_combine;  // 1: the one split of attn_split_kernel per pair also merges
 };
 size_t attn_workspace_bytes(int B, int Hkv, int Hq, int d, int64_t tokens, int* splits,
                             int* tokens_per_split);
