@@ -109,6 +109,27 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     const int32_t* rp = p.row_ptr + (size_t)mm * (rows + 1) + row0;
     const int32_t rpv0 = tid <= nrows ? rp[tid] : 0;
     const int32_t rpv1 = tid + kThreads <= nrows ? rp[tid + kThreads] : 0;
+    // the block's CSR entries, guessed before the row pointers arrive: a
+    // window around the block's share of k at a uniform density, 1.5 times
+    // that share plus 128 entries wide (whole multiples of kThreads, at most
+    // kCsrCap).  One round of loads instead of two when it covers the block's
+    // range; otherwise the entries are loaded again below.
+    const uint16_t* cm = p.col + (size_t)mm * p.k;
+    const uint16_t* vm = p.val + (size_t)mm * p.k;
+    constexpr int EPT = kCsrCap / kThreads;   // entries per thread, at most
+    const int share = (int)((int64_t)nrows * p.k / rows);
+    const int wsize = min(kCsrCap, (share * 3 / 2 + 128 + kThreads - 1) / kThreads * kThreads);
+    const int guess = (int)((int64_t)row0 * p.k / rows) - (wsize - share) / 2;
+    const int wbeg = max(min(guess, p.k - wsize), 0);
+    uint32_t went[EPT] = {};
+    if (p.k > 0) {   // workgroup-uniform; indices clamped to valid entries
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            if (j * kThreads >= wsize) break;   // workgroup-uniform
+            const int ic = min(wbeg + tid + j * kThreads, p.k - 1);
+            went[j] = (uint32_t)cm[ic] | ((uint32_t)vm[ic] << 16);
+        }
+    }
     {
         uint4* t4 = reinterpret_cast<uint4*>(s_s);
         for (int i = tid; i < ROWS_WG * D / 8; i += kThreads) t4[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -121,22 +142,29 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     if (tid <= nrows) s_rp[tid] = min(max(rpv0, 0), p.k);
     if (tid + kThreads <= nrows) s_rp[tid + kThreads] = min(max(rpv1, 0), p.k);
     __syncthreads();
-    // the block's CSR entries: one contiguous range, loaded coalesced
-    const uint16_t* cm = p.col + (size_t)mm * p.k;
-    const uint16_t* vm = p.val + (size_t)mm * p.k;
+    // the block's CSR entries: one contiguous range, from the guessed window
+    // when it covers the range, else loaded again (coalesced)
     const int beg = s_rp[0], cnt = max(s_rp[nrows] - beg, 0);
     const bool staged = cnt <= kCsrCap;
     if (staged) {
-        // all of the thread's loads in flight at once
-        uint32_t ent[kCsrCap / kThreads];
+        if (beg >= wbeg && beg + cnt <= wbeg + wsize) {   // workgroup-uniform
 #pragma unroll
-        for (int j = 0; j < kCsrCap / kThreads; ++j) {
-            const int i = tid + j * kThreads;
-            ent[j] = i < cnt ? ((uint32_t)cm[beg + i] | ((uint32_t)vm[beg + i] << 16)) : 0u;
+            for (int j = 0; j < EPT; ++j) {
+                const int i = wbeg + tid + j * kThreads - beg;
+                if (j * kThreads < wsize && i >= 0 && i < cnt) s_cv[i] = went[j];
+            }
+        } else {
+            // all of the thread's loads in flight at once
+            uint32_t ent[EPT];
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                const int i = tid + j * kThreads;
+                ent[j] = i < cnt ? ((uint32_t)cm[beg + i] | ((uint32_t)vm[beg + i] << 16)) : 0u;
+            }
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if (tid + j * kThreads < cnt) s_cv[tid + j * kThreads] = ent[j];
         }
-#pragma unroll
-        for (int j = 0; j < kCsrCap / kThreads; ++j)
-            if (tid + j * kThreads < cnt) s_cv[tid + j * kThreads] = ent[j];
         __syncthreads();
     }
     // into the dense tile: a row's entries shared out over TPR threads (all
