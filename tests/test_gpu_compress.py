@@ -122,6 +122,30 @@ def test_compress_parity_select_fallback():
     assert rep.ties <= 1e-6 * max(rep.entries, 1) + 0.5
 
 
+def test_decompress_csr_window_miss():
+    """All outliers in the last quarter of the rows: decompress's guessed CSR
+    window (a uniform density) misses those blocks' ranges and they load their
+    entries again."""
+    n, d = 1024, 128
+    p = P(4, 128, 15000, 4, 3)
+    _say(f"[compress parity] CSR window miss: n={n} d={d} {p}")
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn((2, n, d), generator=g, dtype=torch.float32)
+    x[:, 3 * n // 4:, :] *= 16.0
+    x = x.to(torch.float16).to("cuda").contiguous()
+    packed = gear.compress(x, p)
+    xhat = gear.decompress(packed)
+    torch.cuda.synchronize()
+    op = to_orc_params(p)
+    rep = Report()
+    for m in range(2):
+        xm = x[m].cpu().numpy().view(np.uint16)
+        ref = orc.compress_matrix(np.ascontiguousarray(xm), op)
+        check_matrix(xm, packed, m, ref, p, rep, xhat[m].float().cpu().numpy())
+    _say(f"    {rep.summary()}")
+    assert rep.ties <= 1e-6 * max(rep.entries, 1) + 0.5
+
+
 def test_compress_is_deterministic():
     _say("[compress] two calls give identical bytes")
     syn = KVSynth(1, 2, 128, 4, seed=3, device="cuda")
