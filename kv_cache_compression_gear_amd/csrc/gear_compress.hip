@@ -1444,14 +1444,13 @@ hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
     const unsigned M = (unsigned)a.out.M;
     if (a.out.k > 0 || RK > 0) {
         Timed t(kKSelect, st);
-        // 16 waves per matrix, 2 row steps per batch of loads, when the
-        // matrices are too few to give every CU more than two workgroups
-        // (their waves are then all a CU has to hide memory latency with);
-        // else 8 waves, 4 row steps per batch
+        // 16 waves per matrix when the matrices are too few to give every CU
+        // more than two workgroups (their waves are then all a CU has to
+        // hide memory latency with), else 8; batches of 2 row steps
         if ((int64_t)M <= 2 * (int64_t)cu_count())
             hipLaunchKernelGGL((select_kernel<D, 2, 1024>), dim3(M), dim3(1024), 0, st, a);
         else
-            hipLaunchKernelGGL((select_kernel<D, 4, 512>), dim3(M), dim3(512), 0, st, a);
+            hipLaunchKernelGGL((select_kernel<D, 2, 512>), dim3(M), dim3(512), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
