@@ -1158,15 +1158,18 @@ __device__ __forceinline__ void tie_rows(const uint32_t* sel, int rows, int& r_a
 template <bool B>
 struct BoolTag { static constexpr bool value = B; };
 
-// A = R Bf on the matrix cores with v_mfma_f32_16x16x4_f32: M = 16 token
-// rows, N = 16 (the r columns of Bf, zero beyond r), K = 4 per instruction.
-// Lane l holds row l % 16 and the CPL = D/4 consecutive columns starting at
-// CPL (l / 16); the j-th instruction contracts column CPL q + j of the four
-// lane groups q, so CPL instructions cover all D columns and no cross-lane sum
-// is needed.  The output lanes n = l % 16 < r hold A[row][n] for the rows
-// 4 (l / 16) + 0..3 of the step.  X goes from HBM straight into a per-wave
-// LDS tile (row-contiguous load instructions, 16-byte chunks XOR-swizzled by
-// row) and is read from there in that layout.
+// A = R Bf, 16 token rows per step of a wave.  Lane l holds row l % 16 and
+// the CPL = D/4 consecutive columns starting at CPL (l / 16).  At rank <= 4
+// (one quantization group per lane) each lane adds R Bf over its columns on
+// the VALU (Bf's rows from LDS) and the four lane groups of a row are summed
+// with permlane swaps.  Otherwise v_mfma_f32_16x16x4_f32 contracts them: M =
+// 16 token rows, N = 16 (the r columns of Bf, zero beyond r), K = 4 per
+// instruction; the j-th instruction contracts column CPL q + j of the four
+// lane groups q, so CPL instructions cover all D columns and no cross-lane
+// sum is needed, and the output lanes n = l % 16 < r hold A[row][n] for the
+// rows 4 (l / 16) + 0..3 of the step.  X goes from HBM straight into a
+// per-wave LDS tile (row-contiguous load instructions, 16-byte chunks
+// XOR-swizzled by row) and is read from there in that layout.
 // byte I of x as a float, one instruction (v_cvt_f32_ubyteI)
 template <int I>
 __device__ __forceinline__ float ubyte_f(uint32_t x) {
