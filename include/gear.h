@@ -210,7 +210,6 @@ gear_status gear_decode_attn(const gear_cache* cache, const void* q_f16, int32_t
 /* Current counters and section pointers (host call, nothing launched). */
 gear_status gear_cache_get_info(const gear_cache* cache, gear_cache_info* out);
 
-/* Status name, and the detail of this thread's last non-OK status. */
 /*
  * Kernel timing with HIP events, for profiling; off by default.  While it is
  * on, every kernel launch of the library is bracketed by two events recorded
@@ -219,11 +218,13 @@ gear_status gear_cache_get_info(const gear_cache* cache, gear_cache_info* out);
  * recorded events and returns, for the kernel named `kernel` -- one of
  * "select", "compress", "lowrank_a", "decompress", "attn_split",
  * "attn_combine", "buffer_append" -- the launches and their summed duration
- * in milliseconds since the measurement started.  It blocks; host-thread-safe.
+ * in milliseconds since the measurement started ("attn_combine" has none when
+ * the split kernel merges the splits itself).  It blocks; host-thread-safe.
  */
 gear_status gear_timing_enable(int on);
 gear_status gear_timing_read(const char* kernel, int64_t* launches, double* total_ms);
 
+/* Status name, and the detail of this thread's last non-OK status. */
 const char* gear_status_str(gear_status s);
 const char* gear_last_error(void);
 
