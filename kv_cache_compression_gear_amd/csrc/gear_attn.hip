@@ -691,7 +691,7 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     __shared__ __attribute__((aligned(16))) float s_gs[kTPS * kFastGroups];
     __shared__ __attribute__((aligned(16))) float s_gz[kTPS * kFastGroups];
     __shared__ __attribute__((aligned(16))) float s_a[kTPS * kMaxRank];
-    __shared__ float s_bkt[kMaxRank * D];              // B_K transposed: [c][j]
+    __shared__ __attribute__((aligned(16))) float s_bkt[kMaxRank * D];   // B_K transposed: [c][j]
     __shared__ __attribute__((aligned(16))) float s_bv[D * kMaxRank];
     __shared__ float s_qb[G * kMaxRank];
     __shared__ int32_t s_rk[kTPS + 1];
@@ -986,61 +986,73 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] += pz[h];
-    // low-rank part: acc += B_V (sum_t p_t A_t); the per-rank sums over the
-    // workgroup's tokens are added by one row group
+    float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
+    if (tid < G) {
+        part[tid * (D + 2) + D] = fmaxf(fmaxf(s_wm[tid], s_wm[G + tid]), fmaxf(s_wm[2 * G + tid], s_wm[3 * G + tid]));
+        part[tid * (D + 2) + D + 1] = s_ws[tid] + s_ws[G + tid] + s_ws[2 * G + tid] + s_ws[3 * G + tid];
+    }
+    // low-rank part: B_V (sum_t p_t A_t), from the per-rank sums of the waves
 #pragma unroll
     for (int h = 0; h < G; ++h) pa[h] = sum_rowgroups<LPR>(pa[h]);
     if (rl == 0 && colq < r) {
 #pragma unroll
         for (int h = 0; h < G; ++h) s_pa[(wv * G + h) * kMaxRank + colq] = pa[h];
     }
-    __syncthreads();
-    if (wv == 0 && rl == 0) {
-        for (int c = 0; c < r; ++c) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float tot = 0.0f;
-#pragma unroll
-                for (int w = 0; w < kFastWaves; ++w) tot += s_pa[(w * G + h) * kMaxRank + c];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(tot, s_bv[(colq * 8 + e) * r + c], acc[h][e]);
-            }
-        }
-    }
-    // reduce over the row groups of the wave, then over the waves: waves 4..7
-    // hand theirs to waves 0..3, which hand the sums to the store
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = sum_rowgroups<LPR>(acc[h][e]);
-    if (rl == 0 && wv >= 4) {
+    // the final sum for column j of head h: the waves' row sums, the low-rank
+    // term and the sparse V sums
+    auto emit = [&](const float* rows, int nrows) {
+        for (int i = tid; i < G * D; i += kFastThreads) {
+            const int h = i / D, j = i % D;
+            float lr = 0.0f;
+            for (int c = 0; c < r; ++c) {
+                float tot = 0.0f;
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+                for (int w = 0; w < kFastWaves; ++w) tot += s_pa[(w * G + h) * kMaxRank + c];
+                lr = fmaf(tot, s_bv[j * r + c], lr);
+            }
+            const float* vs = s_vs + h * D + j;   // row w at vs[w * G * D]
+            constexpr int RS = G * D;
+            float sp = 0.0f;
+            if (!VTILE) sp = (vs[0 * RS] + vs[1 * RS]) + (vs[2 * RS] + vs[3 * RS]);
+            if (!VTILE && kVsRows == 8) sp += (vs[4 * RS] + vs[5 * RS]) + (vs[6 * RS] + vs[7 * RS]);
+            float dn = 0.0f;
+            for (int w = 0; w < nrows; ++w) dn += rows[(w * G + h) * D + j];
+            part[h * (D + 2) + j] = dn + lr + sp;
+        }
+    };
+    if constexpr (G == 1) {
+        // B_K (read only before the V loop) holds the 8 waves' rows: one
+        // barrier, after which the V loop's LDS data is complete
+        static_assert(kFastWaves * G * D <= kMaxRank * D, "the wave rows fit where B_K was");
+        if (rl == 0) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_red[((wv - 4) * G + h) * D + colq * 8 + e] = acc[h][e];
-    }
-    __syncthreads();
-    if (rl == 0 && wv < 4) {
+            for (int e = 0; e < 8; ++e) s_bkt[wv * D + colq * 8 + e] = acc[0][e];
+        }
+        __syncthreads();
+        emit(s_bkt, kFastWaves);
+    } else {
+        // the rows go where the CSR entries were (read in the V loop): waves
+        // 4..7 hand theirs to waves 0..3
+        __syncthreads();
+        if (rl == 0 && wv >= 4) {
 #pragma unroll
-        for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s_red[(wv * G + h) * D + colq * 8 + e] += acc[h][e];
-    }
-    __syncthreads();
-    float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
-    for (int i = tid; i < G * D; i += kFastThreads) {
-        const int h = i / D, j = i % D;
-        const float* vs = s_vs + h * D + j;   // row w at vs[w * G * D]
-        constexpr int RS = G * D;
-        float sp = 0.0f;
-        if (!VTILE) sp = (vs[0 * RS] + vs[1 * RS]) + (vs[2 * RS] + vs[3 * RS]);
-        if (!VTILE && kVsRows == 8) sp += (vs[4 * RS] + vs[5 * RS]) + (vs[6 * RS] + vs[7 * RS]);
-        part[h * (D + 2) + j] = (s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j]) +
-                                (s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j]) + sp;
-    }
-    if (tid < G) {
-        part[tid * (D + 2) + D] = fmaxf(fmaxf(s_wm[tid], s_wm[G + tid]), fmaxf(s_wm[2 * G + tid], s_wm[3 * G + tid]));
-        part[tid * (D + 2) + D + 1] = s_ws[tid] + s_ws[G + tid] + s_ws[2 * G + tid] + s_ws[3 * G + tid];
+                for (int e = 0; e < 8; ++e) s_red[((wv - 4) * G + h) * D + colq * 8 + e] = acc[h][e];
+        }
+        __syncthreads();
+        if (rl == 0 && wv < 4) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_red[(wv * G + h) * D + colq * 8 + e] += acc[h][e];
+        }
+        __syncthreads();
+        emit(s_red, 4);
     }
 }
 
