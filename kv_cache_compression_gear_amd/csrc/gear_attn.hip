@@ -889,6 +889,8 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
             if (lane == 0) s_wm[wv * G + h] = m;
         }
     }
+    // (this barrier also ends the reads of K's CSR entries, whose LDS bytes
+    // take V's below)
     __syncthreads();
     if (tid < kTPS) {
 #pragma unroll
