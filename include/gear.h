@@ -28,10 +28,16 @@
  *     gear_cache object.
  *   - Every check (null or misaligned pointers, shapes, parameters, workspace
  *     and arena sizes, cache capacity) runs on the host before any launch.  A
- *     non-OK status means nothing was enqueued and no cache state changed;
- *     gear_last_error() then holds a message (thread-local).
- *   - GEAR_ERR_HIP reports a failed launch.  Device faults surface at the
- *     caller's next synchronisation.  No C++ exception crosses this ABI.
+ *     status other than GEAR_OK and GEAR_ERR_HIP means nothing was enqueued
+ *     and no cache state changed; gear_last_error() then holds a message
+ *     (thread-local).
+ *   - GEAR_ERR_HIP reports a failed kernel launch.  The launches of the same
+ *     call that came before it stay enqueued, so the outputs of that call are
+ *     undefined.  A cache whose call returned GEAR_ERR_HIP is marked failed:
+ *     every later call on it (load_prompt, append, decode_attn) returns
+ *     GEAR_ERR_INVALID_ARG without enqueuing anything, and the only use left
+ *     is gear_cache_destroy.  Device faults surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this ABI.
  *   - Calls on distinct caches may run from different threads; one cache is
  *     not thread-safe.
  *
@@ -132,6 +138,14 @@ gear_status gear_compress(const gear_params* p, const gear_shape* s, const void*
 /*
  * Decompress: packed -> out_f16 (the stack described by s), each entry
  * fl16(code*scale + zero + (A B^T)[t][j] + S[t][j]) with round to nearest even.
+ * Source: the app.cochat.ai GEAR page, "Cites" list, the Background sentence
+ * quoted under the PowerSGD entry (the composite approximation: a low-rank
+ * term for the coherent part of the quantization error plus a sparse term for
+ * the individual outliers, both on top of the dequantized matrix), and the
+ * allpcb Q&A, Q3 (the three components combined).  packed must be
+ * 256-byte aligned and hold the layout of (p, s); out_f16 16-byte aligned,
+ * num_mats * n_tokens * head_dim fp16 values.  Nothing is read outside the
+ * packed layout, nothing is written outside out_f16.
  */
 gear_status gear_decompress(const gear_params* p, const gear_shape* s, const void* packed,
                             void* out_f16, void* stream);
@@ -196,12 +210,19 @@ gear_status gear_append_tokens(gear_cache* cache, const void* k_new_f16, const v
 
 /*
  * Decode attention of one query token per sequence over everything cached
- * (prompt segments, fill segments, buffer), no mask:
+ * (prompt segments, fill segments, buffer), no mask.  Source: the allpcb
+ * Q&A, Q1 and Q4 (decoding is bound by reading the KV cache; the compressed
+ * cache cuts that traffic and raises decode throughput), and Q3 "Streaming
+ * strategy" (the most recent tokens are read from the small fp16 buffer).
+ * K^ and V^ are never formed in memory: the scores and the weighted sum are
+ * taken over codes, scales, zeros, A, B and the outliers directly.
  *   out[b][h] = sum_t softmax_t(sm_scale * q[b][h] . K^_t) V^_t
  * with K^, V^ of KV head floor(h * Hkv / q_heads).  q_f16 is [B][q_heads][d],
- * out_f32 is [B][q_heads][d].  q_heads must be a multiple of Hkv.  With no
- * cached tokens the output is zero.  q_f16 must be finite (NaN or infinity is
- * not detected; the output for it is unspecified).
+ * out_f32 is [B][q_heads][d]; both 16-byte aligned.  q_heads / Hkv must be 1,
+ * 2, 4 or 8.  With no cached tokens the output is zero.  q_f16 must be finite
+ * (NaN or infinity is not detected; the output for it is unspecified).
+ * workspace: >= gear_cache_workspace_bytes(config, q_heads), 256-byte aligned
+ * (split partials); it must not be shared by calls that may run concurrently.
  */
 gear_status gear_decode_attn(const gear_cache* cache, const void* q_f16, int32_t q_heads,
                              float sm_scale, float* out_f32, void* workspace,

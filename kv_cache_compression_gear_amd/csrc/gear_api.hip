@@ -1,9 +1,11 @@
 // gear_api.hip -- the C ABI of libgear.so: validation, packed layouts, the
 // streaming cache's host bookkeeping, and kernel launches.  Every check runs
-// before any launch; a non-OK status leaves device memory and cache state
-// untouched.
+// before any launch; a non-OK status other than GEAR_ERR_HIP leaves device
+// memory and cache state untouched.  A failed launch inside a cache call
+// marks that cache failed (later calls on it are refused).
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -34,6 +36,11 @@ gear_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+gear_status failed_cache() {
+    return fail(GEAR_ERR_INVALID_ARG,
+                "an earlier kernel launch on this cache failed; destroy the cache");
+}
 
 // Checks GEAR settings for matrices of `rows` tokens and head_dim d.
 gear_status check_params(const gear_params* p, int64_t rows, int d) {
@@ -172,8 +179,8 @@ double g_total_ms[kKernelCount];
 
 void timing_drop_locked() {
     for (const TimingRec& r : g_pending) {
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
     }
     g_pending.clear();
     for (int i = 0; i < kKernelCount; ++i) {
@@ -192,7 +199,7 @@ hipEvent_t timing_begin(hipStream_t st) {
     hipEvent_t e;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     if (hipEventRecord(e, st) != hipSuccess) {
-        hipEventDestroy(e);
+        (void)hipEventDestroy(e);
         return nullptr;
     }
     return e;
@@ -201,7 +208,7 @@ hipEvent_t timing_begin(hipStream_t st) {
 void timing_end(KernelId k, hipEvent_t start, hipStream_t st) {
     hipEvent_t e = timing_begin(st);
     if (!e) {
-        hipEventDestroy(start);
+        (void)hipEventDestroy(start);
         return;
     }
     std::lock_guard<std::mutex> lk(g_timing_mu);
@@ -222,6 +229,7 @@ struct gear_cache {
     int64_t appended;
     int buf_len;
     int num_fills;
+    bool failed;   // a launch of a cache call failed: the device state is unknown
 };
 
 namespace {
@@ -262,7 +270,11 @@ gear_status cache_layouts(const gear_cache_config* c, gear_layout* pl, gear_layo
 extern "C" {
 
 const char* gear_status_str(gear_status s) {
-    switch (s) {
+    // read as an int: a C caller may pass any int, and in C++ a value outside
+    // the enumerators' range may not be loaded as the enum type
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case GEAR_OK: return "GEAR_OK";
         case GEAR_ERR_INVALID_ARG: return "GEAR_ERR_INVALID_ARG";
         case GEAR_ERR_UNSUPPORTED: return "GEAR_ERR_UNSUPPORTED";
@@ -296,8 +308,8 @@ gear_status gear_timing_read(const char* kernel, int64_t* launches, double* tota
         if (e != hipSuccess) return hip_fail(e, "kernel timing event");
         g_launches[r.k] += 1;
         g_total_ms[r.k] += ms;
-        hipEventDestroy(r.start);
-        hipEventDestroy(r.stop);
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
     }
     g_pending.clear();
     *launches = g_launches[id];
@@ -410,6 +422,7 @@ gear_status gear_cache_create(const gear_cache_config* c, void* arena, size_t ar
     g->appended = 0;
     g->buf_len = 0;
     g->num_fills = 0;
+    g->failed = false;
     *out = g;
     return GEAR_OK;
 }
@@ -419,6 +432,7 @@ void gear_cache_destroy(gear_cache* cache) { delete cache; }
 gear_status gear_cache_load_prompt(gear_cache* g, const void* k_f16, const void* v_f16,
                                    void* workspace, size_t workspace_bytes, void* stream) {
     if (!g) return fail(GEAR_ERR_INVALID_ARG, "cache is NULL");
+    if (g->failed) return failed_cache();
     const gear_cache_config& c = g->cfg;
     if (g->prompt_loaded || g->appended > 0)
         return fail(GEAR_ERR_INVALID_ARG, "the prompt can only be loaded into an empty cache");
@@ -435,6 +449,7 @@ gear_status gear_cache_load_prompt(gear_cache* g, const void* k_f16, const void*
                                   g->arena + g->off_prompt, workspace, workspace_bytes,
                                   static_cast<hipStream_t>(stream));
     if (st == GEAR_OK) g->prompt_loaded = true;
+    if (st == GEAR_ERR_HIP) g->failed = true;
     return st;
 }
 
@@ -442,6 +457,7 @@ gear_status gear_append_tokens(gear_cache* g, const void* k_new_f16, const void*
                                int32_t n_new, void* workspace, size_t workspace_bytes,
                                void* stream) {
     if (!g) return fail(GEAR_ERR_INVALID_ARG, "cache is NULL");
+    if (g->failed) return failed_cache();
     const gear_cache_config& c = g->cfg;
     if (n_new < 0) return fail(GEAR_ERR_INVALID_ARG, "n_new < 0");
     if (n_new == 0) return GEAR_OK;
@@ -473,7 +489,10 @@ gear_status gear_append_tokens(gear_cache* g, const void* k_new_f16, const void*
                                             static_cast<const uint16_t*>(v_new_f16), buf, c.batch,
                                             c.kv_heads, c.head_dim, c.buf_tokens, g->buf_len, take,
                                             n_new, done, st);
-        if (e != hipSuccess) return hip_fail(e, "buffer append launch");
+        if (e != hipSuccess) {
+            g->failed = true;
+            return hip_fail(e, "buffer append launch");
+        }
         g->buf_len += take;
         g->appended += take;
         done += take;
@@ -481,7 +500,10 @@ gear_status gear_append_tokens(gear_cache* g, const void* k_new_f16, const void*
             uint8_t* dst = g->arena + g->off_fills + (size_t)g->num_fills * g->fill_stride;
             gear_status s2 = run_compress(&c.fill, g->fill_layout, c.head_dim, buf, buf, 2 * mats_half,
                                           dst, workspace, workspace_bytes, st);
-            if (s2 != GEAR_OK) return s2;
+            if (s2 != GEAR_OK) {   // checked above: only a failed launch gets here
+                g->failed = true;
+                return s2;
+            }
             g->num_fills += 1;
             g->buf_len = 0;
         }
@@ -493,6 +515,7 @@ gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_h
                              float sm_scale, float* out_f32, void* workspace,
                              size_t workspace_bytes, void* stream) {
     if (!g) return fail(GEAR_ERR_INVALID_ARG, "cache is NULL");
+    if (g->failed) return failed_cache();
     const gear_cache_config& c = g->cfg;
     if (q_heads < c.kv_heads || q_heads % c.kv_heads != 0)
         return fail(GEAR_ERR_INVALID_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads,
@@ -501,8 +524,9 @@ gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_h
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(GEAR_ERR_UNSUPPORTED, "q_heads / kv_heads must be 1, 2, 4 or 8 (got %d)", G);
     if (!q_f16 || !out_f32 || !workspace) return fail(GEAR_ERR_INVALID_ARG, "NULL device pointer");
-    if (!aligned(q_f16, 2) || !aligned(out_f32, 4) || !aligned(workspace, kAlign))
-        return fail(GEAR_ERR_INVALID_ARG, "misaligned pointer");
+    if (!aligned(q_f16, 16) || !aligned(out_f32, 16) || !aligned(workspace, kAlign))
+        return fail(GEAR_ERR_INVALID_ARG,
+                    "q_f16 and out_f32 must be 16-byte, workspace 256-byte aligned");
     if (c.prompt_tokens > 0 && !g->prompt_loaded)
         return fail(GEAR_ERR_INVALID_ARG, "load the prompt before decoding");
     const int64_t tokens = (int64_t)(c.prompt_tokens) + g->appended;

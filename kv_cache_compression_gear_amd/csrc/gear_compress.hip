@@ -946,7 +946,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 near_tie |= fabsf(R[e]) > hs;
             }
             if (near_tie) {
-                // round the exact quotient
+                // rint of the correctly rounded fp32 quotient (as the oracle takes it)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     cf[e] = rintf(t[e] / sc);

@@ -168,3 +168,46 @@ def test_timing_registry_on_the_host():
         assert n.value == 0 and ms.value == 0.0
     assert lib.gear_timing_enable(0) == 0
     assert lib.gear_timing_read(None, ctypes.byref(n), ctypes.byref(ms)) == 1
+
+
+def test_decode_attn_requires_16_byte_aligned_query_and_output():
+    lib = gear.lib()
+    c = _cfg(prompt_tokens=0, max_new=3, B=1, H=1)
+    n = lib.gear_cache_arena_bytes(ctypes.byref(c))
+    h = ctypes.c_void_p()
+    assert lib.gear_cache_create(ctypes.byref(c), ctypes.c_void_p(0x10000000), n, ctypes.byref(h)) == 0
+    try:
+        fake = ctypes.c_void_p(0x20000000)
+        for q, out in ((0x20000008, 0x20000000), (0x20000002, 0x20000000), (0x20000000, 0x20000004)):
+            st = lib.gear_decode_attn(h, ctypes.c_void_p(q), 1, ctypes.c_float(0.1),
+                                      ctypes.c_void_p(out), fake, 1 << 30, None)
+            assert st == 1, lib.gear_last_error()
+            assert b"16-byte" in lib.gear_last_error()
+    finally:
+        lib.gear_cache_destroy(h)
+
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="needs a host with no GPU: the launch must fail")
+def test_failed_launch_marks_the_cache_failed():
+    """With no GPU the buffer-append launch fails: the call reports
+    GEAR_ERR_HIP and every later call on that cache is refused with
+    GEAR_ERR_INVALID_ARG before anything is enqueued."""
+    lib = gear.lib()
+    c = _cfg(prompt_tokens=0, max_new=8, B=1, H=1)
+    n = lib.gear_cache_arena_bytes(ctypes.byref(c))
+    h = ctypes.c_void_p()
+    assert lib.gear_cache_create(ctypes.byref(c), ctypes.c_void_p(0x10000000), n, ctypes.byref(h)) == 0
+    try:
+        fake = ctypes.c_void_p(0x20000000)
+        assert lib.gear_append_tokens(h, fake, fake, 1, fake, 1 << 30, None) == 4
+        assert lib.gear_append_tokens(h, fake, fake, 1, fake, 1 << 30, None) == 1
+        assert b"destroy the cache" in lib.gear_last_error()
+        assert lib.gear_decode_attn(h, fake, 1, ctypes.c_float(0.1), fake, fake, 1 << 30, None) == 1
+        assert lib.gear_cache_load_prompt(h, fake, fake, fake, 1 << 30, None) == 1
+    finally:
+        lib.gear_cache_destroy(h)

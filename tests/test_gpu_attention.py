@@ -174,18 +174,18 @@ def test_streaming_full_gqa_workload_sampled():
             _attn_check(out[sel], ref, what=f"step {s}")
 
 
-def test_decode_attention_full_7b_layer_sampled():
-    """The benchmark's decode step at full size: 8 x 32 heads, 4096-token
-    prompt, one appended token, one query per head (the whole-split prompt
-    kernel with staged outliers, plus the buffer tail); batches {0, 7} x heads
-    0..3 against the oracle (heads attend independently at one query head per
-    KV head)."""
-    w = WORKLOADS["7b_layer"]
+def _full_decode_sampled(name, bsel, hsel):
+    """One decode step of a full-size workload (the whole compressed prompt,
+    one appended token, one query per head, MHA), sampled batches x heads
+    against the oracle (heads attend independently at one query head per KV
+    head)."""
+    w = WORKLOADS[name]
     B, H, n, d = w.batch, w.heads, w.seq, w.head_dim
     Hq = w.q_heads or H
     assert Hq == H
-    _say(f"[attention full] 7b_layer B={B} H={H} prompt={n}")
-    pp = P(w.bits, w.group, w.outlier_ppm, w.rank, w.power_iters)
+    _say(f"[attention full] {name} B={B} H={H} prompt={n} chunk={w.chunk_tokens} b={w.bits} "
+         f"g={w.group} r={w.rank}")
+    pp = P(w.bits, w.group, w.outlier_ppm, w.rank, w.power_iters, w.chunk_tokens)
     fp = P(w.bits, w.group, w.outlier_ppm, w.fill_rank, w.power_iters)
     syn = w.kv_synth("cuda")
     k, v = syn.prompt(n)
@@ -196,9 +196,28 @@ def test_decode_attention_full_7b_layer_sampled():
     cache.append(kn, vn)
     out = cache.decode_attn(q)
     torch.cuda.synchronize()
-    bsel, hs = [0, B - 1], slice(0, 4)
-    oc = orc.OracleCache(len(bsel), 4, d, to_orc_params(pp), to_orc_params(fp), w.buf_tokens)
-    oc.load_prompt(k[bsel][:, hs].cpu().numpy(), v[bsel][:, hs].cpu().numpy())
-    oc.append(kn[bsel][:, hs].cpu().numpy(), vn[bsel][:, hs].cpu().numpy())
-    ref = oc.decode_attention(q[bsel][:, hs].cpu().numpy())
-    _attn_check(out[bsel][:, hs], ref, what="7b_layer sampled")
+    oc = orc.OracleCache(len(bsel), len(hsel), d, to_orc_params(pp), to_orc_params(fp),
+                         w.buf_tokens)
+    oc.load_prompt(k[bsel][:, hsel].cpu().numpy(), v[bsel][:, hsel].cpu().numpy())
+    oc.append(kn[bsel][:, hsel].cpu().numpy(), vn[bsel][:, hsel].cpu().numpy())
+    ref = oc.decode_attention(q[bsel][:, hsel].cpu().numpy())
+    _attn_check(out[bsel][:, hsel], ref, what=f"{name} sampled")
+
+
+def test_decode_attention_full_7b_layer_sampled():
+    """8 x 32 heads, 4096-token prompt (whole-split prompt kernel at one query
+    head per KV head with staged outliers, plus the buffer tail)."""
+    _full_decode_sampled("7b_layer", [0, 7], [0, 1, 2, 3])
+
+
+def test_decode_attention_full_2bit_sampled():
+    """16 x 32 heads, 2048-token prompt, 2-bit codes, two groups of 64 per
+    token, rank 8, one query head per KV head: the prompt kernel's 2-bit MHA
+    variant."""
+    _full_decode_sampled("2bit", [0, 15], [0, 17, 31])
+
+
+def test_decode_attention_full_long_ctx_sampled():
+    """1 x 32 heads, 32,768-token prompt compressed in 64 chunks of 512
+    tokens: 128 prompt splits per head merged by log-sum-exp."""
+    _full_decode_sampled("long_ctx", [0], [0, 31])

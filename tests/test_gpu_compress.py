@@ -1,8 +1,9 @@
 """GPU parity of gear_compress / gear_decompress against the CPU oracle.
 
 Small cases run the oracle on every matrix; they span several workgroup tiles,
-multi-workgroup teams (4096- and 2048-token matrices), ragged tails, chunking
-and the degenerate settings (k = 0, k = n*d, r = 0, n < 64).  Full-size cases
+long matrices (4096 and 2048 tokens: many 64-row slabs per workgroup), ragged
+tails, chunking and the degenerate settings (k = 0, k = n*d, r = 0, n < 64,
+residuals whose rank is below r, zero and constant matrices).  Full-size cases
 run the same launch configuration the benchmark times and check sampled
 matrices against the oracle.
 """
@@ -167,3 +168,61 @@ def test_empty_stack_is_a_no_op():
     out = gear.decompress(packed)
     torch.cuda.synchronize()
     assert out.shape == (0, 64, 128)
+
+
+def _run_x(name, x16, p):
+    """Compress + decompress a given fp16 stack [M, n, d] and check every
+    matrix against the oracle."""
+    M, n, d = x16.shape
+    _say(f"[compress parity] {name}: M={M} n={n} d={d} {p}")
+    x = torch.from_numpy(np.ascontiguousarray(x16)).view(torch.float16).to("cuda").contiguous()
+    packed = gear.compress(x, p)
+    xhat = gear.decompress(packed)
+    torch.cuda.synchronize()
+    op = to_orc_params(p)
+    rep = Report()
+    for m in range(M):
+        xm = np.ascontiguousarray(x16[m])
+        ref = orc.compress_matrix(xm, op)
+        check_matrix(xm, packed, m, ref, p, rep, xhat[m].float().cpu().numpy())
+    _say(f"    {rep.summary()}")
+    assert rep.ties <= 1e-6 * max(rep.entries, 1) + 0.5
+
+
+def _f16_bits(a):
+    return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("n,p", [
+    (512, P(4, 128, 0, 4, 3)),
+    (4096, P(4, 128, 0, 4, 3)),
+    (2048, P(2, 64, 0, 8, 4)),
+    (64, P(4, 128, 0, 2, 3)),
+])
+def test_residual_rank_below_r_identical_rows(n, p):
+    """Every token row the same and no outliers: R = 1 rho^T has rank 1 < r.
+    The oracle's Gram-Schmidt drops the dead columns; the GPU builds C = R^T R
+    in fp32, so its later pivots are rounding noise, not zero.  L must still
+    be R (the one live direction) within the bar."""
+    rng = np.random.default_rng(31)
+    rows = [rng.standard_normal(128) * 3.0, rng.standard_normal(128) * 0.01]
+    x = np.stack([np.tile(r, (n, 1)) for r in rows])
+    _run_x(f"identical rows n={n}", _f16_bits(x), p)
+
+
+@pytest.mark.parametrize("eps", [1e-3, 1e-2])
+def test_residual_near_duplicate_rows(eps):
+    """Rows = one base row + small noise: a residual with one dominant
+    direction and a long tail of tiny singular values."""
+    rng = np.random.default_rng(32)
+    base = rng.standard_normal((2, 1, 128)) * 3.0
+    x = base + eps * rng.standard_normal((2, 1024, 128))
+    _run_x(f"near-duplicate rows eps={eps}", _f16_bits(x), P(4, 128, 0, 4, 3))
+
+
+def test_zero_and_constant_matrices():
+    """A zero matrix (R = 0: L must be exactly 0) and a constant one with
+    outliers (ties everywhere: the lowest flat indices are taken)."""
+    x = np.zeros((2, 256, 128))
+    x[1] = 1.5
+    _run_x("zero and constant", _f16_bits(x), P(4, 64, 20000, 4, 3))

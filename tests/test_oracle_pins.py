@@ -379,3 +379,83 @@ def test_stream_appends_equal_bulk_compression():
     K, V = cache.kv(1, 0)
     assert K.shape == (128, 64)
     assert np.array_equal(K[64:], bulk.xhat)
+
+
+# ---------------------------------------------------------------- bookkeeping of the cache model
+
+def _textbook_attention(K, V, q, scale):
+    s = scale * (K @ q)
+    w = np.exp(s - s.max())
+    return (w / w.sum()) @ V
+
+
+def test_gqa_query_head_reads_consecutive_kv_head():
+    """Query head hq reads KV head floor(hq / (Hq / Hkv)).  Three KV heads and
+    six query heads: the consecutive grouping (0,0,1,1,2,2) and an interleaved
+    one (hq mod 3) disagree on four of the six heads, and each KV head's
+    values are offset by a distinct constant, so a wrong mapping moves the
+    output by at least 1 in every entry."""
+    rng = _rng(21)
+    B, H, Hq, d, n = 2, 3, 6, 32, 9
+    p = orc.Params(bits=4, group=32, outlier_ppm=0, rank=0, power_iters=0)
+    cache = orc.OracleCache(B, H, d, p, p, buf_tokens=64)
+    ks = _f16(rng.standard_normal((n, B, H, d)))
+    vs = _f16(rng.standard_normal((n, B, H, d)) * 0.1 + 4.0 * np.arange(H)[None, None, :, None])
+    for t in range(n):
+        cache.append(ks[t], vs[t])
+    q = _f16(rng.standard_normal((B, Hq, d)))
+    out = cache.decode_attention(q)
+    scale = 1.0 / np.sqrt(d)
+    for b in range(B):
+        for hq in range(Hq):
+            h = hq // (Hq // H)
+            K = ks[:, b, h].astype(np.float64)
+            V = vs[:, b, h].astype(np.float64)
+            exp = _textbook_attention(K, V, q[b, hq].astype(np.float64), scale)
+            assert np.allclose(out[b, hq], exp, rtol=1e-12, atol=1e-12)
+            assert np.all(np.abs(out[b, hq] - 4.0 * h) < 1.0)
+
+
+def test_chunked_compress_is_matrix_major_chunk_minor():
+    """compress() with chunk_tokens cuts each matrix into row chunks and lists
+    them matrix-major, chunk-minor.  Every chunk here is a distinct constant
+    (no outliers, so each group is constant: scale 0, X^ = the constant
+    exactly), so each result names the chunk it came from."""
+    M, C, ct, d = 3, 4, 16, 64
+    val = lambda m, c: 0.5 * (m * C + c + 1)
+    x = np.zeros((M, C * ct, d), np.float16)
+    for m in range(M):
+        for c in range(C):
+            x[m, c * ct:(c + 1) * ct] = val(m, c)
+    p = orc.Params(bits=4, group=32, outlier_ppm=0, rank=2, power_iters=2, chunk_tokens=ct)
+    res = orc.compress(x, p)
+    assert len(res) == M * C
+    for m in range(M):
+        for c in range(C):
+            r = res[m * C + c]
+            assert r.xhat.shape == (ct, d)
+            assert np.all(r.xhat == val(m, c))
+
+
+def test_chunked_prompt_segments_in_token_order():
+    """load_prompt of a chunked prompt: matrix index (tensor * B + b) * H + h,
+    chunk c of it holds tokens [c * ct, (c + 1) * ct); K^ and V^ of (b, h)
+    list the chunks in token order."""
+    B, H, C, ct, d = 2, 2, 3, 8, 64
+    val = lambda t, b, h, c: 0.25 * (((t * B + b) * H + h) * C + c + 1)
+    k = np.zeros((B, H, C * ct, d), np.float16)
+    v = np.zeros((B, H, C * ct, d), np.float16)
+    for b in range(B):
+        for h in range(H):
+            for c in range(C):
+                k[b, h, c * ct:(c + 1) * ct] = val(0, b, h, c)
+                v[b, h, c * ct:(c + 1) * ct] = val(1, b, h, c)
+    p = orc.Params(bits=2, group=64, outlier_ppm=0, rank=1, power_iters=1, chunk_tokens=ct)
+    cache = orc.OracleCache(B, H, d, p, p, buf_tokens=64)
+    cache.load_prompt(k, v)
+    for b in range(B):
+        for h in range(H):
+            K, V = cache.kv(b, h)
+            for c in range(C):
+                assert np.all(K[c * ct:(c + 1) * ct] == val(0, b, h, c))
+                assert np.all(V[c * ct:(c + 1) * ct] == val(1, b, h, c))
