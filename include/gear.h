@@ -136,6 +136,23 @@ gear_status gear_compress(const gear_params* p, const gear_shape* s, const void*
                           void* stream);
 
 /*
+ * Compress without any workspace or allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same inputs, outputs and results as
+ * gear_compress; the per-call scratch (the workspace of gear_compress) is a
+ * static device array of GEAR_NOALLOC_SCRATCH_BYTES that each GPU holds for
+ * the life of the process.  GEAR_ERR_WORKSPACE (nothing enqueued) when
+ * gear_compress_workspace_bytes(p, s) exceeds it.  The first call on a device
+ * looks up the array's address there (GEAR_ERR_HIP if that fails).  All calls
+ * on one GPU share its array: calls that may overlap on one GPU (other
+ * streams, other host threads) race and must be ordered by the caller.  No
+ * part of the array needs clearing between calls.
+ */
+#define GEAR_NOALLOC_SCRATCH_BYTES (16u << 20)
+gear_status gear_compress_noalloc(const gear_params* p, const gear_shape* s, const void* x_f16,
+                                  void* packed, void* stream);
+
+/*
  * Decompress: packed -> out_f16 (the stack described by s), each entry
  * fl16(code*scale + zero + (A B^T)[t][j] + S[t][j]) with round to nearest even.
  * Source: the app.cochat.ai GEAR page, "Cites" list, the Background sentence

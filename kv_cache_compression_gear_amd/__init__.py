@@ -69,7 +69,7 @@ class _CacheInfo(ctypes.Structure):
 
 # Every symbol include/gear.h declares (checked by the tests).
 EXPORTS = ["gear_packed_layout", "gear_packed_bytes", "gear_compress_workspace_bytes",
-           "gear_compress", "gear_decompress",
+           "gear_compress", "gear_compress_noalloc", "gear_decompress",
            "gear_cache_arena_bytes", "gear_cache_workspace_bytes", "gear_cache_create",
            "gear_cache_destroy", "gear_cache_load_prompt", "gear_append_tokens",
            "gear_decode_attn", "gear_cache_get_info", "gear_timing_enable", "gear_timing_read",
@@ -101,6 +101,8 @@ def lib():
         L.gear_compress_workspace_bytes.argtypes = [pp, ps]
         L.gear_compress.restype = S
         L.gear_compress.argtypes = [pp, ps, P, P, P, sz, P]
+        L.gear_compress_noalloc.restype = S
+        L.gear_compress_noalloc.argtypes = [pp, ps, P, P, P]
         L.gear_decompress.restype = S
         L.gear_decompress.argtypes = [pp, ps, P, P, P]
         L.gear_cache_arena_bytes.restype = sz
@@ -261,6 +263,17 @@ def compress(x: torch.Tensor, p: Params, out: Packed | None = None,
                                 device=x.device)
     _check(lib().gear_compress(ctypes.byref(p._c()), ctypes.byref(_shape(M, n, d)), _ptr(x),
                                _ptr(out.buf), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def compress_noalloc(x: torch.Tensor, p: Params, out: Packed) -> Packed:
+    """gear_compress_noalloc: like compress(), into a caller-provided Packed,
+    with the library's static device scratch instead of a workspace."""
+    _check_input(x)
+    n, d = x.shape[-2], x.shape[-1]
+    M = x.numel() // (n * d)
+    _check(lib().gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(_shape(M, n, d)), _ptr(x),
+                                       _ptr(out.buf), _stream()))
     return out
 
 

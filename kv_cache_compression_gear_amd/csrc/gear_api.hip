@@ -159,6 +159,43 @@ gear_status run_compress(const gear_params* p, const gear_layout& L, int d, cons
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// Static scratch of gear_compress_noalloc: the per-matrix selection results
+// and the d x r projection that gear_compress keeps in the caller's
+// workspace.  Each GPU holds its own copy for the life of the process.  Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in): the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current, and is what the kernels get.
+static __device__ __align__(256) unsigned char scratch[GEAR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's scratch address, looked up on its first use.
+gear_status scratch_of_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(GEAR_ERR_UNSUPPORTED, "device %d is beyond this library's %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
+        if (!ptr || !aligned(ptr, kAlign))
+            return fail(GEAR_ERR_HIP, "static scratch at an unexpected address %p", ptr);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return GEAR_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // Kernel timing
 
 namespace {
@@ -348,6 +385,30 @@ gear_status gear_compress(const gear_params* p, const gear_shape* s, const void*
     const int64_t half = s->num_mats * (s->n_tokens / L.rows);
     return run_compress(p, L, s->head_dim, x_f16, x_f16, half, packed, workspace, workspace_bytes,
                         static_cast<hipStream_t>(stream));
+}
+
+gear_status gear_compress_noalloc(const gear_params* p, const gear_shape* s, const void* x_f16,
+                                  void* packed, void* stream) {
+    gear_layout L;
+    gear_status st = compute_layout(p, s, &L);
+    if (st != GEAR_OK) return st;
+    if (L.num_compressed > 0 && (!x_f16 || !packed))
+        return fail(GEAR_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned(x_f16, 16) || !aligned(packed, kAlign))
+        return fail(GEAR_ERR_INVALID_ARG, "x_f16 must be 16-byte, packed 256-byte aligned");
+    const size_t need = plan_compress(p, L, s->head_dim).ws_bytes;
+    if (need > (size_t)GEAR_NOALLOC_SCRATCH_BYTES)
+        return fail(GEAR_ERR_WORKSPACE,
+                    "this call needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use gear_compress with a workspace, or fewer matrices per call)",
+                    need, (size_t)GEAR_NOALLOC_SCRATCH_BYTES);
+    if (L.num_compressed == 0) return GEAR_OK;
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != GEAR_OK) return st;
+    const int64_t half = s->num_mats * (s->n_tokens / L.rows);
+    return run_compress(p, L, s->head_dim, x_f16, x_f16, half, packed, ws,
+                        (size_t)GEAR_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
 }
 
 gear_status gear_decompress(const gear_params* p, const gear_shape* s, const void* packed,

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     lib = gear.lib()
     names = _declared()
-    assert len(names) == 17
+    assert len(names) == 18
     assert sorted(gear.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -211,3 +211,22 @@ def test_failed_launch_marks_the_cache_failed():
         assert lib.gear_cache_load_prompt(h, fake, fake, fake, 1 << 30, None) == 1
     finally:
         lib.gear_cache_destroy(h)
+
+
+def test_noalloc_compress_rejects_more_than_its_static_scratch():
+    """gear_compress_noalloc refuses, on the host, a call whose scratch need
+    exceeds the static array (4224 bytes per 64 x 128 matrix at rank 8)."""
+    lib = gear.lib()
+    p = gear.Params(4, 128, 20000, 8, 3)
+    fake = ctypes.c_void_p(0x10000000)
+    for M, expect in ((5000, 5), (0, 0)):
+        s = gear._shape(M, 64, 128)
+        need = lib.gear_compress_workspace_bytes(ctypes.byref(p._c()), ctypes.byref(s))
+        assert (need > (16 << 20)) == (expect == 5)
+        st = lib.gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(s), fake, fake, None)
+        assert st == expect, lib.gear_last_error()
+    s = gear._shape(5000, 64, 128)
+    assert lib.gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(s), fake, fake, None) == 5
+    assert b"static scratch" in lib.gear_last_error()
+    assert lib.gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(s), ctypes.c_void_p(0x10000008),
+                                     fake, None) == 1
