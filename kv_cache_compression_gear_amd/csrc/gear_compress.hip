@@ -704,6 +704,40 @@ __device__ __forceinline__ int residual_exponent(float bound) {
     return 14 - E;
 }
 
+// Exponent of a slab that holds only zeros: larger than any finite slab's
+// (whose keys are at least the smallest fp16 subnormal, exponent 14 + 23), so
+// that it never lowers the running minimum.
+constexpr int kExNone = 40;
+
+// Largest key (|x| bit pattern) in the rows of xr, over the whole wave, as a
+// wave-uniform value: keys two at a time with packed 16-bit max, then DPP
+// within rows of 16 lanes and the four rows' maxima read out.
+template <int SS>
+__device__ __forceinline__ uint32_t wave_max_key(const uint4 (&xr)[SS]) {
+    typedef unsigned short u2v __attribute__((ext_vector_type(2)));
+    u2v m2 = {0, 0};
+#pragma unroll
+    for (int u = 0; u < SS; ++u) {
+        const uint32_t w[4] = {xr[u].x, xr[u].y, xr[u].z, xr[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u2v, w[i] & 0x7fff7fffu));
+    }
+    uint32_t m = max((uint32_t)m2[0], (uint32_t)m2[1]);
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+    m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)m, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)m, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)m, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)m, 48);
+    return max(max(a, b), max(c, d));
+}
+
+// 2^e as an fp32 bit pattern, for |e| <= 126
+__device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23); }
+
 // GL: lanes per quantization group when fixed at compile time (D/8: a group
 // is a whole token row), 0 for the group size of the call.
 template <int D, int RK, int GL>
@@ -726,6 +760,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     __shared__ double s_w[LR ? (NH - 1) * D * RKX : 1];
     __shared__ double s_g[RKX * RKX];
     __shared__ double s_m[RKX * RKX];
+    __shared__ uint32_t s_ex[2][kCompressWaves];   // per slab: each wave's largest key
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
@@ -774,10 +809,18 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     // both 16-bit halves hold thrk (thrk in [-1, 0x7fff], so thrk - key fits
     // an int16 and is negative exactly for the outliers)
     const uint32_t thr2 = ((uint32_t)thrk & 0xffffu) * 0x10001u;
-    if (LR) bound = h2f(sel[kSelBound]);
-    const int ex = LR ? residual_exponent(bound) : 0;
-    const float sx = ldexpf(1.0f, ex), rsx = ldexpf(1.0f, -ex);
-    const float m1 = -(sx * rsx);   // -1, opaque to the compiler: keeps fma_mix below
+    // R is formed in units of 2^ex so that fp16 covers it.  With outliers the
+    // exponent comes from the selection's bound on the non-outliers; without
+    // them (no selection pass is run) from each 64-row slab's largest key,
+    // made known one slab ahead through s_ex: the running exponent only
+    // decreases, and when it does the Gram accumulators are rescaled by the
+    // exact power of two.  Codes, scales and zeros do not depend on it.
+    constexpr bool kSlabExp = true;
+    const bool slab_ex = LR && kSlabExp && kk == 0;
+    if (LR && !slab_ex) bound = h2f(sel[kSelBound]);
+    int ex = LR && !slab_ex ? residual_exponent(bound) : slab_ex ? kExNone : 0;
+    float sx = pow2f(ex), rsx = pow2f(-ex);
+    float m1 = -(sx * rsx);   // -1, opaque to the compiler: keeps fma_mix below
 
     int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     uint16_t* cm = o.col + (size_t)mm * kk;
@@ -800,8 +843,26 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
         }
     };
 
-    auto do_slab = [&](const uint4 (&xr)[SS], int sl) {
+    auto do_slab = [&](const uint4 (&xr)[SS], const uint4 (&xn)[SS], int sl) {
         unsigned char* slab = s_big + (sl & 1) * 2 * kPlane;
+        if (slab_ex) {   // wave-uniform
+            const uint4 e0 = *reinterpret_cast<const uint4*>(&s_ex[sl & 1][0]);
+            const uint4 e1 = *reinterpret_cast<const uint4*>(&s_ex[sl & 1][4]);
+            const uint32_t key = __builtin_amdgcn_readfirstlane(
+                max(max(max(e0.x, e0.y), max(e0.z, e0.w)), max(max(e1.x, e1.y), max(e1.z, e1.w))));
+            const int exs = key == 0u ? kExNone : residual_exponent(h2f(key));
+            if (exs < ex) {
+                const float f = pow2f(2 * (exs - ex));   // >= 2^-80: exact
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[b][v] *= f;
+                ex = exs;
+                sx = pow2f(ex);
+                rsx = pow2f(-ex);
+                m1 = -(sx * rsx);
+            }
+        }
         uint32_t dm[SS][4], om[SS];
         // ---- outlier mask: dm = x with the outliers set to +0, om bit e set
         // for column 8 colq + e
@@ -996,6 +1057,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             }
         }
         if (LR) {
+            if (slab_ex && lane == 0) s_ex[(sl + 1) & 1][wv] = wave_max_key<SS>(xn);
             __syncthreads();
             slab_mma<D>(slab, wv, lane, acc);
         }
@@ -1004,12 +1066,17 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     {
         uint4 xa[SS], xb[SS];
         load_slab(xa, 0);
+        if (slab_ex) {   // the first slab's bound
+            const uint32_t k0 = wave_max_key<SS>(xa);
+            if (lane == 0) s_ex[0][wv] = k0;
+            __syncthreads();
+        }
         for (int sl = 0; sl < nslab; sl += 2) {
             load_slab(xb, sl + 1);
-            do_slab(xa, sl);
+            do_slab(xa, xb, sl);
             if (sl + 1 < nslab) {
                 load_slab(xa, sl + 2);
-                do_slab(xb, sl + 1);
+                do_slab(xb, xa, sl + 1);
             }
         }
     }
@@ -1445,7 +1512,7 @@ constexpr int lowrank_rows_per_wg() { return 4 * 16 * kLrSteps; }
 template <int D, int RK>
 hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
     const unsigned M = (unsigned)a.out.M;
-    if (a.out.k > 0 || RK > 0) {
+    if (a.out.k > 0) {   // without outliers the compress kernel bounds R itself
         Timed t(kKSelect, st);
         // 16 waves per matrix when the matrices are too few to give every CU
         // more than two workgroups (their waves are then all a CU has to

@@ -226,3 +226,38 @@ def test_zero_and_constant_matrices():
     x = np.zeros((2, 256, 128))
     x[1] = 1.5
     _run_x("zero and constant", _f16_bits(x), P(4, 64, 20000, 4, 3))
+
+
+def _full_gear_l(name, sample):
+    """A full-size workload at s = 0 (GEAR-L: quantization + low rank, no
+    outliers and no selection pass)."""
+    w = WORKLOADS[name]
+    p = P(w.bits, w.group, 0, w.rank, w.power_iters, w.chunk_tokens)
+    return _run_case(f"{name} GEAR-L (s=0)", w.batch, w.heads, w.seq, w.head_dim, p,
+                     w.k_outlier_channels, w.k_outlier_mult, device_gen="cuda", sample=sample)
+
+
+def test_gear_l_full_7b_layer_sampled():
+    _full_gear_l("7b_layer", [0, 255, 256, 511])
+
+
+def test_gear_l_full_2bit_sampled():
+    _full_gear_l("2bit", [0, 511, 512, 1023])
+
+
+def test_gear_l_exponent_falls_mid_matrix():
+    """Without outliers the residual's scaling comes from each 64-row slab's
+    largest |x| and only decreases: magnitudes growing down the rows (the
+    exponent falls at almost every slab), 1000 zero rows before the data,
+    and one large slab between small ones."""
+    rng = np.random.default_rng(33)
+    n, d = 4096, 128
+    z = rng.standard_normal((3, n, d))
+    x = np.empty_like(z)
+    x[0] = z[0] * np.exp2(np.arange(n) / 512.0)[:, None] * 1e-3
+    x[1] = z[1]
+    x[1, :1000] = 0.0
+    x[2] = z[2] * 1e-3
+    x[2, 2048:2112] = z[2, 2048:2112] * 300.0
+    _run_x("GEAR-L falling exponent", _f16_bits(x), P(4, 128, 0, 4, 3))
+    _run_x("GEAR-L falling exponent, 2-bit rank 8", _f16_bits(x), P(2, 64, 0, 8, 2))
