@@ -1,7 +1,8 @@
 """Benchmark of the GEAR hot path on one MI355X.
 
-One step = one pass of the whole path over one 7B-shaped attention layer
-(batch 8, 32 heads, 4096 tokens, head_dim 128; K and V, fp16 = 536,870,912 B):
+Headline step (the `value`): one pass of the whole path over one 7B-shaped
+attention layer (batch 8, 32 heads, 4096 tokens, head_dim 128; K and V, fp16 =
+536,870,912 B):
   gear_compress    outlier top-k + CSR, 4-bit group quantization, rank-4 fit
                    (3 power iterations) of all 512 K/V matrices
   gear_decompress  reconstruction of all 512 matrices to fp16
@@ -14,18 +15,25 @@ bytes per step / step time (GB/s).  Prints one JSON line.
 
 The K timed steps run uninstrumented; K further steps then run with the
 library's per-kernel HIP events on (gear_timing_*) and per-phase events, which
-give `phases_ms`, `kernels_ms` and the `roofline` object: the kernel with the
-largest share of a step, its launch time measured live on the launch stream.
-`traffic` is its measured HBM bytes per launch from
-the committed rocprofv3 counter summary under profiles/, when that summary was
-taken from the current kernel sources (else null).  Next to it, the CPU
-oracle is timed on a bounded sample of the same workload (`cpu_baseline`).
-A second block times the streaming GQA decode workload (batch 64, 32 query /
-8 KV heads, 2048-token prompt, 256 decode steps).
+give `phases_ms`, `kernels_ms`, `roofline` (the kernel with the largest share
+of a step, its launch time measured live on the launch stream) and
+`compress_phase` (the three compress launches as one unit).  Measured HBM
+bytes and SQ counters come from the committed rocprofv3 summaries under
+profiles/ while they were taken from the current kernel sources (else null);
+the counters also name the binding resource (`bound`).
+
+Beside the headline, the same line carries (all timed in this run):
+  configs            compress / decompress (and one decode step) of the other
+                     workloads: tiny, 2-bit, long context in 512-token chunks,
+                     and GEAR-L (no outliers) at the 7B-layer and 2-bit shapes
+  stream_gqa_decode  the streaming GQA workload (batch 64, 32 query / 8 KV
+                     heads, 2048-token prompt, 256 append + decode steps)
+  cpu_baseline       the CPU oracle on a bounded sample of the headline layer
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--no-cpu-baseline]
-                    [--no-stream] [--copy-calibration]
-    python bench.py --summarize-pmc counter_collection.csv   (profile helper)
+                    [--no-stream] [--no-configs] [--workload 7b_layer]
+    python bench.py --make-profiles OUTDIR [--workload W]   (rocprofv3 passes
+                    and every summary table under OUTDIR; runs on the GPU machine)
 """
 from __future__ import annotations
 
@@ -34,7 +42,9 @@ import csv
 import hashlib
 import json
 import os
+import platform
 import re
+import subprocess
 import sys
 import time
 from collections import defaultdict
@@ -43,22 +53,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# 256 CUs x 4 SIMDs x 16 lanes per cycle (a wave64 VALU instruction takes 4
+# cycles) x 2.4 GHz: ordinary (non-packed) VALU lane-operations per second
+VALU_PEAK_TLANE_OPS = 256 * 64 * 2.4e9 / 1e12
+SIMDS = 1024
+XCDS = 8
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "kv_cache_compression_gear_amd", "csrc")
 COPY_BYTES = 256 << 20          # plain copy used to calibrate the byte counters
-# kernel -> source file it is built from
+COPY_KERNEL = "copyBuffer"      # the runtime's blit kernel behind torch's device copy
+COPY_GRID = str(COPY_BYTES // 2048)   # its grid for the 256 MiB calibration copy
+METRIC = "GEAR compress+decompress GB/s (fp16 KV in) & decode tok/s; % of HBM peak"
+
+# kernel (name used by gear_timing_read, plus attn_prompt) -> source file
 KERNEL_SOURCE = {"select": "gear_compress.hip", "compress": "gear_compress.hip",
                  "lowrank_a": "gear_compress.hip", "decompress": "gear_decompress.hip",
                  "attn_prompt": "gear_attn.hip", "attn_split": "gear_attn.hip",
                  "attn_combine": "gear_attn.hip", "buffer_append": "gear_attn.hip"}
-# device symbol of each kernel (for rocprofv3 summaries)
-# ("attn_prompt" and "attn_split" are timed together by the library, as
-# "attn_split": the decode attention over all splits)
+# device symbol of each kernel ("attn_prompt" and "attn_split" are timed
+# together by the library, as "attn_split": the decode attention over all splits)
 KERNEL_SYMBOL = {"select": "select_kernel", "compress": "compress_kernel",
                  "lowrank_a": "lowrank_a_kernel", "decompress": "decompress_kernel",
                  "attn_prompt": "attn_prompt_kernel", "attn_split": "attn_split_kernel",
                  "attn_combine": "attn_combine_kernel", "buffer_append": "buffer_append_kernel"}
+SQ_PASSES = [
+    ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES",
+     "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
+    ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_WAIT_ANY", "SQ_WAVES",
+     "SQ_INSTS_VMEM_RD", "SQ_INSTS_BRANCH", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS",
+     "GRBM_GUI_ACTIVE"],
+]
 
+
+# --------------------------------------------------------------------------
+# Profile summaries (rocprofv3 output -> the text files under profiles/)
+# --------------------------------------------------------------------------
 
 def source_digest(kernel: str) -> str:
     """sha256 (first 16 hex digits) over the code of the kernel's source and of
@@ -74,42 +103,23 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel: str, workload: str):
-    """Measured HBM bytes per launch from profiles/<symbol>_<workload>_traffic.txt,
-    or None if absent or taken from other kernel sources."""
-    path = os.path.join(PROFILES, f"{KERNEL_SYMBOL[kernel]}_{workload}_traffic.txt")
-    if not os.path.exists(path):
-        return None
-    kv = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-    if kv.get("source_sha256") != source_digest(kernel):
-        return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
-
-
-COPY_KERNEL = "copyBuffer"      # the runtime's blit kernel behind torch's device copy
-COPY_GRID = str(COPY_BYTES // 2048)   # its grid for the 256 MiB calibration copy
+def _kernel_key(name: str):
+    # the symbol as a whole identifier: compress_kernel is not decompress_kernel
+    for k, sym in KERNEL_SYMBOL.items():
+        if re.search(r"(?<![A-Za-z0-9_])" + sym + r"(?![A-Za-z0-9_])", name):
+            return k
+    return None
 
 
 def summarize_pmc(path: str):
     """Per-kernel mean of each counter in a rocprofv3 counter_collection.csv;
-    the 256 MiB calibration copy of --copy-calibration is listed as 'copy'."""
+    the 256 MiB calibration copy is listed as 'copy'."""
     vals = defaultdict(lambda: defaultdict(list))
     with open(path) as f:
         for row in csv.DictReader(f):
             name = row["Kernel_Name"]
-            key = None
-            for k, sym in KERNEL_SYMBOL.items():
-                if sym in name:
-                    key = k
-            if key is None and COPY_KERNEL in name and row["Grid_Size"] == COPY_GRID:
+            key = _kernel_key(name)
+            if key is None and COPY_KERNEL in name and row.get("Grid_Size") == COPY_GRID:
                 key = "copy"
             if key is None:
                 continue
@@ -117,52 +127,257 @@ def summarize_pmc(path: str):
     return {k: {c: (sum(v) / len(v), len(v)) for c, v in d.items()} for k, d in vals.items()}
 
 
-def traffic_summary(fetch_csv: str, write_csv: str, kernel: str, workload: str) -> str:
-    """The traffic file read by read_traffic(): FETCH_SIZE and WRITE_SIZE (KiB
-    per dispatch) of `kernel`, each divided by what the same counter reads per
-    byte of the plain calibration copy."""
-    f = summarize_pmc(fetch_csv)
-    w = summarize_pmc(write_csv)
+def _trace_rows(path: str):
+    rows = []
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            s = row.get("Start_Timestamp") or row.get("Start") or row.get("BeginNs")
+            e = row.get("End_Timestamp") or row.get("End") or row.get("EndNs")
+            rows.append((row["Kernel_Name"], int(s), int(e)))
+    rows.sort(key=lambda r: r[1])
+    return rows
+
+
+def _short(name: str) -> str:
+    m = re.search(r"(\w+_kernel)(<[^()]*>)?", name)
+    if not m:
+        return name[:48]
+    return (m.group(1) + (m.group(2) or "")).replace(" ", "")
+
+
+def kernel_stats_table(trace_csv: str, last: int, bench_json: dict | None, header: str) -> str:
+    """Per kernel instantiation: calls, mean / min / max duration over the
+    whole run and the mean of its last `last` launches (the instrumented pass
+    of the headline step, which comes last in the run), beside the HIP-event
+    means the run's own JSON line reported."""
+    per = defaultdict(list)
+    for name, s, e in _trace_rows(trace_csv):
+        if _kernel_key(name) is not None:      # this library's kernels only
+            per[_short(name)].append((e - s) / 1e3)
+    bench_k = (bench_json or {}).get("kernels_ms", {})
+    # the library's timing covers the instantiation the headline step runs
+    # most (the fill compression of the streaming cache is another one)
+    main_inst = {}
+    for k, d in per.items():
+        key = _kernel_key(k)
+        if key not in main_inst or len(d) > len(per[main_inst[key]]):
+            main_inst[key] = k
+    lines = [header.rstrip("\n"), "# Times in microseconds.",
+             f"{'kernel':44s} {'calls':>6s} {'avg_us':>8s} {'min_us':>8s} {'max_us':>8s} "
+             f"{'last' + str(last) + '_us':>9s} {'bench_us':>9s}"]
+    for k, d in sorted(per.items(), key=lambda kv: -sum(kv[1][-last:])):
+        key = _kernel_key(k)
+        b = bench_k.get(key) if main_inst.get(key) == k else None
+        lines.append(f"{k:44s} {len(d):6d} {sum(d) / len(d):8.1f} {min(d):8.1f} {max(d):8.1f} "
+                     f"{sum(d[-last:]) / len(d[-last:]):9.1f} {'' if b is None else f'{b * 1e3:9.1f}'}")
+    if bench_json:
+        lines.append(f"# same run: value {bench_json['value']} GB/s, ms_per_step "
+                     f"{bench_json['ms_per_step']}, roofline {bench_json['roofline']['kernel']} "
+                     f"launch {bench_json['roofline']['launch_ms']} ms")
+    lines.append("# (bench_us: attn_prompt_kernel and attn_split_kernel are timed together as "
+                 "attn_split by the library)")
+    return "\n".join(lines) + "\n"
+
+
+def hbm_table(fetch_csv: str, write_csv: str, header: str) -> str:
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of every kernel, each
+    divided by what the same counter reads per byte of the plain calibration
+    copy; with each kernel's source digest (bench.py uses the bytes only while
+    the digest matches the current sources)."""
+    f, w = summarize_pmc(fetch_csv), summarize_pmc(write_csv)
     kib = COPY_BYTES / 1024
     ff = f["copy"]["FETCH_SIZE"][0] / kib
     wf = w["copy"]["WRITE_SIZE"][0] / kib
-    fk, nf = f[kernel]["FETCH_SIZE"]
-    wk, nw = w[kernel]["WRITE_SIZE"]
-    fetch_b = fk * 1024 / ff
-    write_b = wk * 1024 / wf
-    return "\n".join([
-        f"# HBM traffic per launch of {KERNEL_SYMBOL[kernel]}, workload {workload}",
-        f"kernel: {KERNEL_SYMBOL[kernel]}",
-        f"fetch_size_kib_per_dispatch: {fk:.1f}   ({nf} dispatches)",
-        f"write_size_kib_per_dispatch: {wk:.1f}   ({nw} dispatches)",
-        f"copy_fetch_size_kib: {f['copy']['FETCH_SIZE'][0]:.1f}   (plain copy of {COPY_BYTES} bytes)",
-        f"copy_write_size_kib: {w['copy']['WRITE_SIZE'][0]:.1f}",
-        f"fetch_factor: {ff:.5f}",
-        f"write_factor: {wf:.5f}",
-        f"hbm_fetch_bytes_per_launch: {fetch_b:.0f}",
-        f"hbm_write_bytes_per_launch: {write_b:.0f}",
-        f"hbm_bytes_per_launch: {fetch_b + write_b:.0f}",
-        f"source_sha256: {source_digest(kernel)}",
-    ]) + "\n"
+    lines = [header.rstrip("\n"),
+             f"# calibration: plain copy of {COPY_BYTES} bytes reads FETCH_SIZE "
+             f"{f['copy']['FETCH_SIZE'][0]:.1f} KiB (fetch_factor {ff:.5f}), WRITE_SIZE "
+             f"{w['copy']['WRITE_SIZE'][0]:.1f} KiB (write_factor {wf:.5f}); bytes = KiB x 1024 / factor",
+             f"{'kernel':16s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'read_B':>12s} {'write_B':>12s} "
+             f"{'total_B':>12s} {'dispatches':>10s}  source_sha256"]
+    for k in KERNEL_SYMBOL:
+        if k not in f or k not in w:
+            continue
+        fk, nf = f[k]["FETCH_SIZE"]
+        wk, _ = w[k]["WRITE_SIZE"]
+        rb, wb = fk * 1024 / ff, wk * 1024 / wf
+        lines.append(f"{k:16s} {fk:12.1f} {wk:12.1f} {rb:12.0f} {wb:12.0f} {rb + wb:12.0f} "
+                     f"{nf:10d}  {source_digest(k)}")
+    return "\n".join(lines) + "\n"
+
+
+def sq_table(p1_csv: str, p2_csv: str, entries: dict, header: str) -> str:
+    """SQ counters per dispatch (means) and derived columns: valu% = VALU
+    instructions x 4 cycles over the dispatch's SIMD-cycles (1024 SIMDs x
+    GRBM_GUI_ACTIVE / 8 XCDs); mfma% = SQ_VALU_MFMA_BUSY_CYCLES over the same;
+    coexec% = MFMA cycles with VALU issuing too; lane_ops/entry = VALU
+    instructions x 64 / matrix entries the launch covers."""
+    a, b = summarize_pmc(p1_csv), summarize_pmc(p2_csv)
+    cols = SQ_PASSES[0][:-1] + SQ_PASSES[1][:-1] + ["GRBM_GUI_ACTIVE"]
+    lines = [header.rstrip("\n"),
+             f"{'kernel':14s} " + " ".join(f"{c.replace('SQ_', ''):>14s}" for c in cols)]
+    derived = [f"{'kernel':14s} {'valu%':>7s} {'mfma%':>7s} {'coexec%':>8s} {'lane_ops/entry':>15s} "
+               f"{'lds_confl/inst':>15s}  source_sha256"]
+    for k in KERNEL_SYMBOL:
+        if k not in a or k not in b:
+            continue
+        v = {**{c: a[k][c][0] for c in a[k]}, **{c: b[k][c][0] for c in b[k] if c != "GRBM_GUI_ACTIVE"}}
+        lines.append(f"{k:14s} " + " ".join(f"{v.get(c, float('nan')):14.4g}" for c in cols))
+        simd_cycles = SIMDS * v["GRBM_GUI_ACTIVE"] / XCDS
+        valu = 100 * v["SQ_INSTS_VALU"] * 4 / simd_cycles
+        mfma = 100 * v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / simd_cycles
+        co = (100 * v.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / v["SQ_VALU_MFMA_BUSY_CYCLES"]
+              if v.get("SQ_VALU_MFMA_BUSY_CYCLES") else 0.0)
+        ent = entries.get(k)
+        lpe = f"{v['SQ_INSTS_VALU'] * 64 / ent:15.2f}" if ent else f"{'':15s}"
+        lds = v.get("SQ_LDS_BANK_CONFLICT", 0) / max(v.get("SQ_INSTS_LDS", 1), 1)
+        derived.append(f"{k:14s} {valu:7.1f} {mfma:7.1f} {co:8.1f} {lpe} {lds:15.2f}  {source_digest(k)}")
+    return "\n".join(lines + [""] + derived) + "\n"
+
+
+def read_profile_row(kind: str, workload: str, kernel: str):
+    """The row of `kernel` in profiles/gear_kernels_<workload>_<kind>.txt as a
+    dict of floats, or None if absent or taken from other kernel sources."""
+    path = os.path.join(PROFILES, f"gear_kernels_{workload}_{kind}.txt")
+    if not os.path.exists(path):
+        return None
+    hdr = None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            parts = line.split()
+            if parts[0] == "kernel":
+                # only the tables that carry each row's source digest
+                hdr = parts if parts[-1] == "source_sha256" else None
+                continue
+            if hdr and parts[0] == kernel and len(parts) == len(hdr):
+                if parts[-1] != source_digest(kernel):
+                    return None
+                out = {}
+                for h, p in zip(hdr[1:-1], parts[1:-1]):
+                    try:
+                        out[h] = float(p)
+                    except ValueError:
+                        pass
+                return out
+    return None
+
+
+def _entries_of(workload: str) -> dict:
+    """Matrix entries one launch of each kernel covers, in the headline step
+    of `workload` (for lane-ops per entry)."""
+    from kv_cache_compression_gear_amd.synth import WORKLOADS
+    w = WORKLOADS[workload]
+    n = 2 * w.batch * w.heads * w.seq * w.head_dim
+    return {"select": n, "compress": n, "lowrank_a": n, "decompress": n, "attn_prompt": n}
+
+
+def make_profiles(outdir: str, workload: str, keep_raw: bool = False) -> int:
+    """rocprofv3 passes over the headline step of `workload` (kernel trace,
+    FETCH_SIZE, WRITE_SIZE, two SQ counter sets), then the summary tables,
+    written to OUTDIR/profiles/.  This process never touches the GPU: each
+    pass is a child process, rocprofv3 with the program after `--`."""
+    os.makedirs(os.path.join(outdir, "profiles"), exist_ok=True)
+    me = os.path.abspath(__file__)
+    step = ["python3", me, "--workload", workload, "--no-cpu-baseline", "--no-stream",
+            "--no-configs"]
+    short = step + ["--steps", "3", "--warmup", "1"]
+    env = dict(os.environ, TMPDIR="/tmp")
+    passes = [("kt", ["--kernel-trace", "--stats"], step, 300),
+              ("pf", ["--pmc", "FETCH_SIZE"], short + ["--copy-calibration"], 120),
+              ("pw", ["--pmc", "WRITE_SIZE"], short + ["--copy-calibration"], 120),
+              ("p1", ["--pmc", *SQ_PASSES[0]], short, 120),
+              ("p2", ["--pmc", *SQ_PASSES[1]], short, 120)]
+    cmds = {}
+    for tag, opts, prog, limit in passes:
+        d = os.path.join(outdir, tag)
+        cmd = ["timeout", "-s", "KILL", str(limit), "rocprofv3", *opts, "-d", d, "-o", "run",
+               "--output-format", "csv", "--", *prog]
+        cmds[tag] = " ".join(cmd).replace(outdir, "<out>").replace(os.path.dirname(me), "<repo>")
+        print(f"[make-profiles] {tag}: {cmds[tag]}", flush=True)
+        with open(os.path.join(outdir, f"{tag}.log"), "w") as log:
+            r = subprocess.run(cmd, cwd="/tmp", env=env, stdout=log, stderr=subprocess.STDOUT)
+        print(f"[make-profiles] {tag}: exit {r.returncode}", flush=True)
+        if r.returncode != 0:
+            # rocprofv3 can end with a segmentation fault after a complete run
+            # (results written); anything else stops here
+            if not (r.returncode in (139, -11) and _csv(d, "kernel_trace" if tag == "kt"
+                                                        else "counter_collection")):
+                return r.returncode
+    bench_json = None
+    with open(os.path.join(outdir, "kt.log")) as f:
+        for line in f:
+            if line.startswith("{\"metric\""):
+                bench_json = json.loads(line)
+    mk = f"python3 <repo>/bench.py --make-profiles <out> --workload {workload}"
+    common = (f"# One MI355X (gfx950), ROCm 7.2; workload {workload} (the headline step of "
+              f"bench.py --workload {workload}).\n# Made by `{mk}` (committed code), which ran, "
+              f"from /tmp with TMPDIR=/tmp:\n")
+    out = os.path.join(outdir, "profiles")
+    with open(os.path.join(out, f"gear_kernels_{workload}_kernel_stats.txt"), "w") as f:
+        f.write(kernel_stats_table(_csv(os.path.join(outdir, "kt"), "kernel_trace"),
+                                   bench_json["steps"] if bench_json else 20, bench_json,
+                                   common + f"#   {cmds['kt']}\n"))
+    with open(os.path.join(out, f"gear_kernels_{workload}_hbm_bytes.txt"), "w") as f:
+        f.write(hbm_table(_csv(os.path.join(outdir, "pf"), "counter_collection"),
+                          _csv(os.path.join(outdir, "pw"), "counter_collection"),
+                          common + f"#   {cmds['pf']}\n#   {cmds['pw']}\n"))
+    with open(os.path.join(out, f"gear_kernels_{workload}_sq_counters.txt"), "w") as f:
+        f.write(sq_table(_csv(os.path.join(outdir, "p1"), "counter_collection"),
+                         _csv(os.path.join(outdir, "p2"), "counter_collection"),
+                         _entries_of(workload),
+                         common + f"#   {cmds['p1']}\n#   {cmds['p2']}\n"
+                         "# Means per dispatch over the run's dispatches of each kernel.\n"))
+    if not keep_raw:   # raw traces and counter files: large, and summarised above
+        import shutil
+        for tag, *_ in passes:
+            shutil.rmtree(os.path.join(outdir, tag), ignore_errors=True)
+    print(f"[make-profiles] summaries in {out}", flush=True)
+    return 0
+
+
+def _csv(d: str, kind: str):
+    for root, _, files in os.walk(d):
+        for fn in files:
+            if fn.endswith(f"{kind}.csv"):
+                return os.path.join(root, fn)
+    return None
+
+
+# --------------------------------------------------------------------------
+# Timed parts
+# --------------------------------------------------------------------------
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
 
 
 def _cpu_baseline(w, x_sample, p, n_mats_total):
     """The C oracle (as it stands) on a bounded sample of the same workload:
     compress + reconstruct of a number of the layer's matrices, one host thread
-    per matrix."""
+    per matrix, on at most 16 threads (one GPU's share of a GPU host)."""
     from concurrent.futures import ThreadPoolExecutor
 
     from oracle import oracle as orc
 
     op = orc.Params(p.bits, p.group, p.outlier_ppm, p.rank, p.power_iters, p.chunk_tokens, p.seed)
     mats = [x_sample[i] for i in range(x_sample.shape[0])]
-    threads = max(1, min(len(mats), len(os.sched_getaffinity(0)), 16))
+    host_cpus = len(os.sched_getaffinity(0))
+    threads = max(1, min(len(mats), host_cpus, 16))
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda m: orc.compress_matrix(m, op), mats))
     dt = time.perf_counter() - t0
     nbytes = sum(m.nbytes for m in mats)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "host_cpus": host_cpus, "cpu_model": _cpu_model(),
             "sample": f"{len(mats)} of the {n_mats_total} K/V matrices ({w.seq}x{w.head_dim} fp16): "
                       f"compress + reconstruct (no decode attention), {dt:.2f} s wall on "
                       f"{threads} host threads"}
@@ -172,10 +387,107 @@ def _packed_bytes(pk) -> int:
     return sum(s.numel() * s.element_size() for s in pk.sections())
 
 
+def _median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def _codec_config(gear, torch, w, p, label, reps=10, decode=False):
+    """Compress and decompress of one whole workload (inputs resident), median
+    of `reps` timed calls after 3 warm-up calls, per-kernel means from a second
+    pass with the library's HIP events; optionally one decode step (append +
+    attention) over a cache holding the same compressed prompt."""
+    B, H, n, d = w.batch, w.heads, w.seq, w.head_dim
+    syn = w.kv_synth("cuda")
+    k, v = syn.prompt(n)
+    x = torch.cat([k.reshape(B * H, n, d), v.reshape(B * H, n, d)]).contiguous()
+    M = x.shape[0]
+    L = gear.packed_layout(p, M, n, d)
+    packed = gear.Packed(torch.empty(L.total_bytes, dtype=torch.uint8, device="cuda"), p, M, n, d, L)
+    ws = torch.empty(gear.compress_workspace_bytes(p, M, n, d), dtype=torch.uint8, device="cuda")
+    xhat = torch.empty_like(x)
+    for _ in range(3):
+        gear.compress(x, p, out=packed, workspace=ws)
+        gear.decompress(packed, out=xhat)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record()
+        gear.compress(x, p, out=packed, workspace=ws)
+        e[1].record()
+        gear.decompress(packed, out=xhat)
+        e[2].record()
+    torch.cuda.synchronize()
+    c_ms = _median([e[0].elapsed_time(e[1]) for e in ev])
+    d_ms = _median([e[1].elapsed_time(e[2]) for e in ev])
+    gear.timing_enable(True)
+    for _ in range(reps):
+        gear.compress(x, p, out=packed, workspace=ws)
+        gear.decompress(packed, out=xhat)
+    torch.cuda.synchronize()
+    kt = gear.timing_read()
+    gear.timing_enable(False)
+    fp16 = x.numel() * 2
+    pb = _packed_bytes(packed)
+    algo = fp16 + pb
+    rec = {"workload": label, "matrices": M * (n // (p.chunk_tokens or n)),
+           "compress_ms": round(c_ms, 4), "decompress_ms": round(d_ms, 4),
+           "compress_GBps_fp16": round(fp16 / (c_ms * 1e-3) / 1e9, 1),
+           "decompress_GBps_fp16": round(fp16 / (d_ms * 1e-3) / 1e9, 1),
+           "algorithmic_bytes": algo,
+           "compress_hbm_frac": round(algo / (c_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "decompress_hbm_frac": round(algo / (d_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "kernels_ms": {k2: round(t / c, 4) for k2, (c, t) in kt.items()}}
+    del xhat, ws
+    if decode:
+        Hq = w.q_heads or H
+        fp = gear.Params(w.bits, w.group, w.outlier_ppm, w.fill_rank, w.power_iters)
+        cache = gear.Cache(B, H, d, p, fp, n, buf_tokens=w.buf_tokens, max_new_tokens=1, q_heads=Hq)
+        cache.load_prompt(k.contiguous(), v.contiguous())
+        kn, vn = syn.step()
+        q = syn.queries(Hq)
+        cache.append(kn, vn)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            cache.decode_attn(q, out=out)
+        torch.cuda.synchronize()
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        e0[0].record()
+        for i in range(reps):
+            cache.decode_attn(q, out=out)
+            e0[i + 1].record()
+        torch.cuda.synchronize()
+        a_ms = _median([e0[i].elapsed_time(e0[i + 1]) for i in range(reps)])
+        cb = _packed_bytes(cache.prompt_packed()) + B * H * 2 * d * 2 + q.numel() * 2 + out.numel() * 4
+        rec.update({"decode_attn_ms": round(a_ms, 4), "decode_tok_s": round(B / (a_ms * 1e-3), 1),
+                    "decode_algorithmic_bytes": cb,
+                    "decode_hbm_frac": round(cb / (a_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)})
+        del cache
+    del x, k, v, packed
+    torch.cuda.synchronize()
+    return rec
+
+
+def _configs(gear, torch, WORKLOADS):
+    out = {}
+    for name, s0, decode in (("tiny", False, True), ("2bit", False, True), ("long_ctx", False, True),
+                             ("7b_layer", True, False), ("2bit", True, False)):
+        w = WORKLOADS[name]
+        ppm = 0 if s0 else w.outlier_ppm
+        p = gear.Params(w.bits, w.group, ppm, w.rank, w.power_iters, w.chunk_tokens)
+        key = f"{name}_gear_l" if s0 else name
+        label = (f"{name}{' GEAR-L' if s0 else ''}: batch {w.batch}, {w.heads} heads, {w.seq} tokens, "
+                 f"head_dim {w.head_dim}, b={w.bits} g={w.group} s={ppm / 1e4:g}% r={w.rank} "
+                 f"t={w.power_iters}" + (f", chunks of {w.chunk_tokens}" if w.chunk_tokens else ""))
+        print(f"[bench] config {key}", file=sys.stderr, flush=True)
+        out[key] = _codec_config(gear, torch, w, p, label, decode=decode)
+    return out
+
+
 def _stream_decode(gear, WORKLOADS, torch):
     """Streaming GQA decode: append + decode attention for 256 steps, timed
     uninstrumented; the same steps on a second cache (same prompt) give the
-    per-kernel breakdown."""
+    per-kernel breakdown and the attention's bytes per step."""
     w = WORKLOADS["stream_gqa"]
     B, H, n, d, Hq = w.batch, w.heads, w.seq, w.head_dim, w.q_heads
     p = gear.Params(w.bits, w.group, w.outlier_ppm, w.rank, w.power_iters)
@@ -220,13 +532,52 @@ def _stream_decode(gear, WORKLOADS, torch):
     kt = gear.timing_read()
     gear.timing_enable(False)
     attn_ms = sum(kt.get(k2, (0, 0.0))[1] for k2 in ("attn_split", "attn_combine"))
-    return {"workload": f"stream_gqa: batch {B}, {Hq} query / {H} KV heads, prompt {n} tokens, "
-                        f"{steps} decode steps, fp16 buffer {w.buf_tokens} tokens compressed "
-                        f"on fill at rank {w.fill_rank}",
-            "tok_s": round(B * steps / dt, 1),
-            "attn_only_tok_s": round(B * steps / (attn_ms * 1e-3), 1) if attn_ms > 0 else None,
-            "ms_total": round(dt * 1e3, 3),
-            "kernels_ms": {k2: round(v2[1] / v2[0], 4) for k2, v2 in kt.items()}}
+    # what the attention reads and writes over the run: the packed prompt every
+    # step, the fills compressed so far, the fp16 buffer rows, q and out
+    prompt_b = _packed_bytes(caches[1].prompt_packed())
+    fill_b = _packed_bytes(caches[1].fill_packed(0))
+    row_b = B * H * 2 * d * 2
+    total_b = 0
+    for s in range(1, steps + 1):
+        total_b += prompt_b + (s // w.buf_tokens) * fill_b + (s % w.buf_tokens) * row_b
+        total_b += qs[0].numel() * 2 + out.numel() * 4
+    rec = {"workload": f"stream_gqa: batch {B}, {Hq} query / {H} KV heads, prompt {n} tokens, "
+                       f"{steps} decode steps, fp16 buffer {w.buf_tokens} tokens compressed "
+                       f"on fill at rank {w.fill_rank}",
+           "tok_s": round(B * steps / dt, 1),
+           "attn_only_tok_s": round(B * steps / (attn_ms * 1e-3), 1) if attn_ms > 0 else None,
+           "ms_total": round(dt * 1e3, 3),
+           "attn_algorithmic_bytes_per_step": round(total_b / steps),
+           "attn_hbm_frac": round(total_b / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if attn_ms else None,
+           "kernels_ms": {k2: round(v2[1] / v2[0], 4) for k2, v2 in kt.items()}}
+    del caches
+    torch.cuda.synchronize()
+    return rec
+
+
+def _bound_from_counters(kernel: str, workload: str, launch_ms: float, algo_bytes: float):
+    """The binding resource of `kernel` from the committed counters: VALU
+    issue (instructions x 4 cycles over the launch's SIMD-cycles, as measured)
+    against HBM (measured bytes over the launch time at 8 TB/s)."""
+    sq = read_profile_row("sq_counters", workload, kernel)
+    hb = read_profile_row("hbm_bytes", workload, kernel)
+    if sq is None:
+        return None
+    lane_ops = None
+    p = os.path.join(PROFILES, f"gear_kernels_{workload}_sq_counters.txt")
+    with open(p) as f:
+        txt = f.read()
+    m = re.search(rf"^{kernel}\s+((?:[-\d.e+]+\s+)+)", txt, flags=re.M)
+    if m:
+        lane_ops = float(m.group(1).split()[0]) * 64       # first column: SQ_INSTS_VALU
+    valu_frac = sq.get("valu%", 0.0) / 100.0
+    hbm_frac = (hb["total_B"] / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS) if hb else None
+    return {"valu_busy_frac": round(valu_frac, 4),
+            "hbm_busy_frac": None if hbm_frac is None else round(hbm_frac, 4),
+            "lane_ops_per_launch": lane_ops,
+            "lane_ops_per_entry": sq.get("lane_ops/entry"),
+            "traffic": None if hb is None else hb["total_B"],
+            "bound": "alu" if hbm_frac is None or valu_frac > hbm_frac else "hbm"}
 
 
 def main():
@@ -238,25 +589,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
-    ap.add_argument("--summarize-pmc", metavar="CSV",
-                    help="print per-kernel counter means of a rocprofv3 counter_collection.csv")
-    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="print the traffic file of --kernel from FETCH_SIZE / WRITE_SIZE runs")
-    ap.add_argument("--kernel", default="compress")
+    ap.add_argument("--make-profiles", metavar="OUTDIR",
+                    help="run the rocprofv3 passes and write the summary tables under OUTDIR")
+    ap.add_argument("--keep-raw", action="store_true",
+                    help="with --make-profiles: keep the raw rocprofv3 output")
     args = ap.parse_args()
-    if args.traffic_summary:
-        print(traffic_summary(*args.traffic_summary, args.kernel, args.workload), end="")
-        return
-    if args.summarize_pmc:
-        for k, d in sorted(summarize_pmc(args.summarize_pmc).items()):
-            for c, (mean, cnt) in sorted(d.items()):
-                print(f"{k:16s} {c:12s} dispatches={cnt:4d} mean={mean:.6g}")
-        return
+    if args.make_profiles:
+        sys.exit(make_profiles(os.path.abspath(args.make_profiles), args.workload, args.keep_raw))
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the GEAR path has no cross-GPU step "
-              f"(--gpus {args.gpus} requested)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only: the GEAR path has no cross-GPU step and this "
+              f"build measures one GPU (--gpus {args.gpus} requested)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -266,6 +611,11 @@ def main():
     from kv_cache_compression_gear_amd.synth import WORKLOADS
 
     torch.cuda.set_device(0)
+    # the other workloads first, so that the headline step's instrumented pass
+    # is the last launch of each of its kernels in a profiler trace
+    configs = None if args.no_configs else _configs(gear, torch, WORKLOADS)
+    stream = None if args.no_stream else _stream_decode(gear, WORKLOADS, torch)
+
     w = WORKLOADS[args.workload]
     B, H, n, d = w.batch, w.heads, w.seq, w.head_dim
     Hq = w.q_heads or H
@@ -355,14 +705,54 @@ def main():
     dom = max(((k2, n2 * t2) for k2, (n2, t2) in kern.items() if k2 in algo), key=lambda z: z[1])[0]
     launch_ms = kern[dom][1]
     achieved = algo[dom] / (launch_ms * 1e-3) / 1e9
-    traffic = read_traffic(dom, args.workload)
+    cnt = _bound_from_counters(dom, args.workload, launch_ms, algo[dom])
+    entries = M * n * d
+    if cnt and cnt["bound"] == "alu" and cnt["lane_ops_per_launch"]:
+        ach = cnt["lane_ops_per_launch"] / (launch_ms * 1e-3) / 1e12
+        roofline = {"kernel": KERNEL_SYMBOL[dom], "bound": "alu", "achieved": round(ach, 2),
+                    "peak": round(VALU_PEAK_TLANE_OPS, 2), "unit": "Tlane-op/s",
+                    "frac": round(ach / VALU_PEAK_TLANE_OPS, 4), "traffic": cnt["traffic"],
+                    "basis": "VALU lane-ops issued per launch (SQ_INSTS_VALU x 64, committed counters) "
+                             "/ live launch time",
+                    "lane_ops_per_entry": cnt["lane_ops_per_entry"],
+                    "hbm_achieved": round(achieved, 1), "hbm_peak": HBM_PEAK_GBPS,
+                    "hbm_frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "algorithmic_bytes": algo[dom], "launch_ms": round(launch_ms, 4)}
+    else:
+        roofline = {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                    "traffic": None if cnt is None else cnt["traffic"],
+                    "valu_busy_frac": None if cnt is None else cnt["valu_busy_frac"],
+                    "algorithmic_bytes": algo[dom], "launch_ms": round(launch_ms, 4)}
+
+    # the compress phase as one unit: fp16 in + packed out, over its three launches
+    phase_algo = fp16_bytes + packed_bytes
+    ph_traffic, ph_ops, ph_ok = 0.0, 0.0, True
+    for k2 in ("select", "compress", "lowrank_a"):
+        if k2 not in kern:
+            continue
+        hb = read_profile_row("hbm_bytes", args.workload, k2)
+        sq = read_profile_row("sq_counters", args.workload, k2)
+        if hb is None or sq is None or sq.get("lane_ops/entry") is None:
+            ph_ok = False
+            continue
+        ph_traffic += hb["total_B"]
+        ph_ops += sq["lane_ops/entry"]
+    compress_phase = {"kernels": [KERNEL_SYMBOL[k2] for k2 in ("select", "compress", "lowrank_a")
+                                  if k2 in kern],
+                      "algorithmic_bytes": phase_algo, "ms": round(comp_ms, 4),
+                      "achieved": round(phase_algo / (comp_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                      "unit": "GB/s", "frac": round(phase_algo / (comp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "traffic": round(ph_traffic) if ph_ok else None,
+                      "traffic_ratio": round(ph_traffic / phase_algo, 3) if ph_ok else None,
+                      "lane_ops_per_entry": round(ph_ops, 2) if ph_ok else None,
+                      "valu_lane_op_budget_per_entry_at_60pct_hbm":
+                          round(VALU_PEAK_TLANE_OPS * 1e12 / (0.6 * HBM_PEAK_GBPS * 1e9 / (phase_algo / entries)), 2)}
 
     cpu = None
     if not args.no_cpu_baseline:
         sample = x[: min(args.cpu_sample, M)].cpu().numpy().view(np.uint16)
         cpu = _cpu_baseline(w, sample, p, M)
-
-    stream = None if args.no_stream else _stream_decode(gear, WORKLOADS, torch)
 
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -372,7 +762,7 @@ def main():
         torch.cuda.synchronize()
 
     rec = {
-        "metric": "GEAR compress+decompress GB/s (fp16 KV in) & decode tok/s; % of HBM peak",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -395,13 +785,14 @@ def main():
         "decompress_GBps_fp16": round(fp16_bytes / (decomp_ms * 1e-3) / 1e9, 1),
         "decompress_hbm_frac": round((packed_bytes + fp16_bytes) / (decomp_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "decode_tok_s": round(B / (dec_ms * 1e-3), 1),
-        "roofline": {"kernel": KERNEL_SYMBOL[dom], "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic),
-                     "algorithmic_bytes": algo[dom], "launch_ms": round(launch_ms, 4)},
+        "roofline": roofline,
+        "compress_phase": compress_phase,
         "cpu_baseline": cpu,
+        "configs": configs,
         "stream_gqa_decode": stream,
     }
+    del cache, packed, xhat, ws, x
+    torch.cuda.synchronize()
     print(json.dumps(rec), flush=True)
 
 
