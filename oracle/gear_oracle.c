@@ -204,6 +204,129 @@ void orc_dequantize(const uint8_t *code, const float *scale, const float *zero,
         }
 }
 
+/*
+ * KIVI-style key quantization ([CITES], the KIVI entry and the sentence quoted
+ * under it, Method: when GEAR is combined with KIVI the streaming buffer must
+ * hold at least one group; the "Cited by" quote of the same page: KIVI
+ * quantizes keys per channel and values per token).
+ *
+ * reading: a group is `group` consecutive tokens of one channel (column j);
+ * min, max, scale, zero-point, rounding and clamping exactly as in
+ * orc_quantize.  scale and zero are laid out [n/group][d] (group index, then
+ * channel); n must be a multiple of group.
+ */
+void orc_quantize_channel(const float *D, int64_t n, int64_t d, int bits, int group,
+                          uint8_t *code, float *scale, float *zero)
+{
+    const int qmax = (1 << bits) - 1;
+    for (int64_t gi = 0; gi < n / group; ++gi) {
+        for (int64_t j = 0; j < d; ++j) {
+            const float *v = D + gi * group * d + j;   /* v[i * d]: token gi*group + i */
+            float mn = v[0], mx = v[0];
+            for (int i = 1; i < group; ++i) {
+                if (v[i * d] < mn) mn = v[i * d];
+                if (v[i * d] > mx) mx = v[i * d];
+            }
+            float diff = mx - mn;
+            float sc = diff / (float)qmax;
+            scale[gi * d + j] = sc + 0.0f;
+            zero[gi * d + j] = mn + 0.0f;
+            for (int i = 0; i < group; ++i) {
+                int c = 0;
+                if (sc != 0.0f) {
+                    float q = (v[i * d] - mn) / sc;
+                    float r = rintf(q);
+                    if (r < 0.0f) r = 0.0f;
+                    if (r > (float)qmax) r = (float)qmax;
+                    c = (int)r;
+                }
+                code[(gi * group + i) * d + j] = (uint8_t)c;
+            }
+        }
+    }
+}
+
+/* deq = code*scale + zero for the per-channel layout, in fp64. */
+void orc_dequantize_channel(const uint8_t *code, const float *scale, const float *zero,
+                            int64_t n, int64_t d, int group, double *deq)
+{
+    for (int64_t t = 0; t < n; ++t)
+        for (int64_t j = 0; j < d; ++j) {
+            int64_t gi = (t / group) * d + j;
+            deq[t * d + j] = (double)code[t * d + j] * (double)scale[gi] + (double)zero[gi];
+        }
+}
+
+/*
+ * ZipCache's channel-separable tokenwise quantization ("ZipCache: Accurate and
+ * Efficient KV Cache Quantization with Salient Token Identification",
+ * abstract): the channel dimension is separated out of the quantization
+ * parameters, which are then per token.
+ *
+ * reading: channel j of X is divided by a power of two 2^e_j, the smallest one
+ * not below the channel's largest |x| (e_j = 0 for an all-zero channel), so
+ * that the normalized entries lie in [-1, 1] and the division is exact up to
+ * fp16 rounding of subnormal results; GEAR (outliers, quantization with one
+ * group per token, low-rank fit) then runs on the normalized matrix, and the
+ * reconstruction multiplies channel j back by 2^e_j.
+ */
+
+/* e_j for every channel of x (n x d fp16 bits). */
+void orc_channel_exponents(const uint16_t *x, int64_t n, int64_t d, int32_t *e)
+{
+    for (int64_t j = 0; j < d; ++j) {
+        double m = 0.0;
+        for (int64_t t = 0; t < n; ++t) {
+            double v = fabs(orc_half_to_double(x[t * d + j]));
+            if (v > m) m = v;
+        }
+        int32_t k = 0;
+        if (m > 0.0) {
+            int ex;
+            double f = frexp(m, &ex);          /* m = f 2^ex, f in [0.5, 1) */
+            k = (f == 0.5) ? ex - 1 : ex;      /* smallest k with 2^k >= m */
+        }
+        e[j] = k;
+    }
+}
+
+/* The binary16 bit pattern nearest to a finite double (ties to even),
+ * subnormals included; values beyond the largest finite half become
+ * infinity. */
+uint16_t orc_double_to_half(double v)
+{
+    uint16_t sign = (uint16_t)(signbit(v) ? 0x8000u : 0u);
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int ex;
+    frexp(a, &ex);                    /* a in [2^(ex-1), 2^ex) */
+    int e = ex - 1;                   /* unbiased exponent of a */
+    if (e < -14) e = -14;             /* subnormal range: fixed quantum 2^-24 */
+    double q = ldexp(1.0, e - 10);    /* spacing of halves around a */
+    double m = a / q;                 /* exact: a scaled by a power of two */
+    double r = nearbyint(m);          /* ties to even (default rounding mode) */
+    double h = r * q;
+    if (h >= 65520.0)                 /* rounds above the largest finite half */
+        return (uint16_t)(sign | 0x7c00u);
+    /* h = r 2^(e-10) with r <= 2048: encode */
+    if (h < ldexp(1.0, -14))          /* subnormal (or rounded up to the min normal) */
+        return (uint16_t)(sign | (uint16_t)(h / ldexp(1.0, -24)));
+    int hex;
+    double hf = frexp(h, &hex);       /* h = hf 2^hex, hf in [0.5, 1) */
+    uint16_t mant = (uint16_t)((hf * 2.0 - 1.0) * 1024.0);
+    return (uint16_t)(sign | (uint16_t)((hex - 1 + 15) << 10) | mant);
+}
+
+/* xt = fl16(x * 2^-e_j), channel by channel. */
+void orc_channel_normalize(const uint16_t *x, int64_t n, int64_t d, const int32_t *e,
+                           uint16_t *xt)
+{
+    for (int64_t t = 0; t < n; ++t)
+        for (int64_t j = 0; j < d; ++j)
+            xt[t * d + j] = orc_double_to_half(ldexp(orc_half_to_double(x[t * d + j]), -e[j]));
+}
+
 /* ------------------------------------------------------------------------ */
 /* Step 3: low-rank approximation of the quantization residual               */
 /* ------------------------------------------------------------------------ */
@@ -322,11 +445,15 @@ void orc_low_rank_product(const double *A, const double *B, int64_t n, int64_t d
  *   L        n*d doubles (the low-rank term)
  *   xhat     n*d doubles (D^ + L + S, the reconstruction)
  */
-void orc_compress_matrix(const uint16_t *x, int64_t n, int64_t d, int bits,
-                         int group, int32_t ppm, int r, int iters, uint64_t seed,
-                         uint8_t *packed, float *scale, float *zero,
-                         int32_t *row_ptr, uint16_t *col, uint16_t *val,
-                         double *A, double *B, double *L, double *xhat)
+/* mode 0: groups of `group` columns of a token (scale/zero [n][d/group]);
+ * mode 1: groups of `group` tokens of a channel (KIVI keys; scale/zero
+ * [n/group][d]).  Both hold n*d/group parameters. */
+void orc_compress_matrix_mode(const uint16_t *x, int64_t n, int64_t d, int bits,
+                              int group, int mode, int32_t ppm, int r, int iters,
+                              uint64_t seed, uint8_t *packed, float *scale,
+                              float *zero, int32_t *row_ptr, uint16_t *col,
+                              uint16_t *val, double *A, double *B, double *L,
+                              double *xhat)
 {
     const int64_t nd = n * d, ng = d / group;
     const int64_t k = orc_num_outliers(n, d, ppm);
@@ -348,8 +475,13 @@ void orc_compress_matrix(const uint16_t *x, int64_t n, int64_t d, int bits,
         Dm[i] = mask[i] ? 0.0f : (float)orc_half_to_double(x[i]);
 
     /* Q = quantize(D); D^ = deq(Q). */
-    orc_quantize(Dm, n, d, bits, group, code, sc, zr);
-    orc_dequantize(code, sc, zr, n, d, group, deq);
+    if (mode == 1) {
+        orc_quantize_channel(Dm, n, d, bits, group, code, sc, zr);
+        orc_dequantize_channel(code, sc, zr, n, d, group, deq);
+    } else {
+        orc_quantize(Dm, n, d, bits, group, code, sc, zr);
+        orc_dequantize(code, sc, zr, n, d, group, deq);
+    }
 
     /* R = X - S - D^ = D - D^; L = rank-r fit of R. */
     for (int64_t i = 0; i < nd; ++i)
@@ -373,6 +505,17 @@ void orc_compress_matrix(const uint16_t *x, int64_t n, int64_t d, int bits,
 
     free(mask); free(Dm); free(code); free(sc); free(zr); free(deq);
     free(R); free(Lw); free(Aw); free(Bw); free(B0);
+}
+
+/* GEAR's own quantizer (groups along head_dim). */
+void orc_compress_matrix(const uint16_t *x, int64_t n, int64_t d, int bits,
+                         int group, int32_t ppm, int r, int iters, uint64_t seed,
+                         uint8_t *packed, float *scale, float *zero,
+                         int32_t *row_ptr, uint16_t *col, uint16_t *val,
+                         double *A, double *B, double *L, double *xhat)
+{
+    orc_compress_matrix_mode(x, n, d, bits, group, 0, ppm, r, iters, seed, packed, scale,
+                             zero, row_ptr, col, val, A, B, L, xhat);
 }
 
 /* ------------------------------------------------------------------------ */

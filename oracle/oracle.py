@@ -67,6 +67,15 @@ def lib():
                                           ctypes.c_int, ctypes.c_int, u64,
                                           P, P, P, P, P, P, P, P, P, P]
         L.orc_attention.argtypes = [P, P, i64, i64, P, ctypes.c_double, P]
+        L.orc_quantize_channel.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, P, P, P]
+        L.orc_dequantize_channel.argtypes = [P, P, P, i64, i64, ctypes.c_int, P]
+        L.orc_compress_matrix_mode.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               i32, ctypes.c_int, ctypes.c_int, u64,
+                                               P, P, P, P, P, P, P, P, P, P]
+        L.orc_channel_exponents.argtypes = [P, i64, i64, P]
+        L.orc_double_to_half.restype = ctypes.c_uint16
+        L.orc_double_to_half.argtypes = [ctypes.c_double]
+        L.orc_channel_normalize.argtypes = [P, i64, i64, P, P]
         _lib = L
     return _lib
 
@@ -117,6 +126,51 @@ def pack_codes(code: np.ndarray, bits: int) -> np.ndarray:
     n, d = code.shape
     out = np.zeros((n, d * bits // 8), np.uint8)
     lib().orc_pack_codes(_p(code), n, d, bits, _p(out))
+    return out
+
+
+def quantize_channel(D: np.ndarray, bits: int, group: int):
+    """Per-channel quantization (groups of `group` tokens of one column):
+    (codes uint8 [n,d], scale [n/group, d], zero [n/group, d])."""
+    D = np.ascontiguousarray(D, dtype=np.float32)
+    n, d = D.shape
+    code = np.zeros((n, d), np.uint8)
+    scale = np.zeros((n // group, d), np.float32)
+    zero = np.zeros((n // group, d), np.float32)
+    lib().orc_quantize_channel(_p(D), n, d, bits, group, _p(code), _p(scale), _p(zero))
+    return code, scale, zero
+
+
+def dequantize_channel(code, scale, zero, group: int) -> np.ndarray:
+    code = np.ascontiguousarray(code, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    zero = np.ascontiguousarray(zero, dtype=np.float32)
+    n, d = code.shape
+    out = np.zeros((n, d), np.float64)
+    lib().orc_dequantize_channel(_p(code), _p(scale), _p(zero), n, d, group, _p(out))
+    return out
+
+
+def channel_exponents(x) -> np.ndarray:
+    """e_j: the smallest power of two not below channel j's largest |x|."""
+    xb = _bits16(x)
+    n, d = xb.shape
+    e = np.zeros(d, np.int32)
+    lib().orc_channel_exponents(_p(xb), n, d, _p(e))
+    return e
+
+
+def double_to_half(v: float) -> int:
+    return int(lib().orc_double_to_half(float(v)))
+
+
+def channel_normalize(x, e) -> np.ndarray:
+    """fl16(x * 2^-e_j) as fp16 bits."""
+    xb = _bits16(x)
+    n, d = xb.shape
+    e = np.ascontiguousarray(e, dtype=np.int32)
+    out = np.zeros((n, d), np.uint16)
+    lib().orc_channel_normalize(_p(xb), n, d, _p(e), _p(out))
     return out
 
 
@@ -181,10 +235,18 @@ def attention(K: np.ndarray, V: np.ndarray, q: np.ndarray, scale: float) -> np.n
 # Whole-matrix compression
 # --------------------------------------------------------------------------
 
+QUANT_GROUP, QUANT_KIVI, QUANT_ZIPCACHE = 0, 1, 2
+ROLE_KEYS, ROLE_VALUES = 0, 1
+
+
 @dataclass(frozen=True)
 class Params:
-    """GEAR settings: b-bit codes, group size g along head_dim, outlier share
-    in parts per million, rank r, power iterations t, chunking, B0 seed."""
+    """GEAR settings: b-bit codes, group size g, outlier share in parts per
+    million, rank r, power iterations t, chunking, B0 seed, and the
+    quantization backbone: GEAR's own (groups of g head_dim columns of a
+    token), KIVI (keys: groups of g tokens of a channel; values as GEAR's) or
+    ZipCache (channels separated out by powers of two, then one group per
+    token)."""
     bits: int = 4
     group: int = 128
     outlier_ppm: int = 20000
@@ -192,6 +254,7 @@ class Params:
     power_iters: int = 3
     chunk_tokens: int = 0
     seed: int = 0
+    quant: int = QUANT_GROUP
 
 
 @dataclass
@@ -207,17 +270,34 @@ class Compressed:
     B: np.ndarray        # float64 [d, r]
     L: np.ndarray        # float64 [n, d]
     xhat: np.ndarray     # float64 [n, d]
+    chan: np.ndarray | None = None   # ZipCache: float32 [d] channel factors 2^e_j
 
 
-def compress_matrix(x, p: Params) -> Compressed:
+def compress_matrix(x, p: Params, role: int = ROLE_KEYS) -> Compressed:
+    """One n x d matrix.  role says whether it holds keys or values (only
+    the KIVI backbone treats them differently)."""
     xb = _bits16(x)
     n, d = xb.shape
+    if p.quant == QUANT_ZIPCACHE:
+        # the channels separated out, GEAR with one group per token on the rest
+        assert p.group == d, "ZipCache's quantization is tokenwise: group = head_dim"
+        e = channel_exponents(xb)
+        xt = channel_normalize(xb, e)
+        c = compress_matrix(xt, Params(**{**p.__dict__, "quant": QUANT_GROUP}), role)
+        f = np.ldexp(1.0, e)
+        c.chan = f.astype(np.float32)
+        c.xhat = c.xhat * f[None, :]
+        return c
+    mode = 1 if (p.quant == QUANT_KIVI and role == ROLE_KEYS) else 0
+    if mode == 1:
+        assert n % p.group == 0, "KIVI keys: tokens per matrix must be a multiple of the group"
     k = num_outliers(n, d, p.outlier_ppm)
     r = p.rank
+    pshape = (n // p.group, d) if mode == 1 else (n, d // p.group)
     out = Compressed(
         packed=np.zeros((n, d * p.bits // 8), np.uint8),
-        scale=np.zeros((n, d // p.group), np.float32),
-        zero=np.zeros((n, d // p.group), np.float32),
+        scale=np.zeros(pshape, np.float32),
+        zero=np.zeros(pshape, np.float32),
         row_ptr=np.zeros(n + 1, np.int32),
         col=np.zeros(max(k, 1), np.uint16),
         val=np.zeros(max(k, 1), np.uint16),
@@ -226,8 +306,8 @@ def compress_matrix(x, p: Params) -> Compressed:
         L=np.zeros((n, d), np.float64),
         xhat=np.zeros((n, d), np.float64),
     )
-    lib().orc_compress_matrix(
-        _p(xb), n, d, p.bits, p.group, p.outlier_ppm, r, p.power_iters, p.seed,
+    lib().orc_compress_matrix_mode(
+        _p(xb), n, d, p.bits, p.group, mode, p.outlier_ppm, r, p.power_iters, p.seed,
         _p(out.packed), _p(out.scale), _p(out.zero), _p(out.row_ptr),
         _p(out.col), _p(out.val), _p(out.A), _p(out.B), _p(out.L), _p(out.xhat))
     out.col, out.val = out.col[:k], out.val[:k]
@@ -235,18 +315,20 @@ def compress_matrix(x, p: Params) -> Compressed:
     return out
 
 
-def compress(x, p: Params) -> list:
+def compress(x, p: Params, role: int = ROLE_KEYS, roles=None) -> list:
     """Compress a stack of matrices x [M, n, d].  With chunk_tokens > 0 each
     matrix is cut into n/chunk_tokens row chunks, compressed independently;
-    the result is ordered matrix-major, chunk-minor."""
+    the result is ordered matrix-major, chunk-minor.  roles (optional) gives
+    each matrix's role, else every matrix has `role`."""
     xb = _bits16(x)
     M, n, d = xb.shape
     ct = p.chunk_tokens or n
     assert n % ct == 0
     res = []
     for m in range(M):
+        rm = role if roles is None else roles[m]
         for c in range(n // ct):
-            res.append(compress_matrix(xb[m, c * ct:(c + 1) * ct], p))
+            res.append(compress_matrix(xb[m, c * ct:(c + 1) * ct], p, rm))
     return res
 
 
@@ -291,7 +373,7 @@ class OracleCache:
         kb, vb = _bits16(k), _bits16(v)
         B, H, n, d = kb.shape
         x = np.concatenate([kb.reshape(B * H, n, d), vb.reshape(B * H, n, d)])
-        segs = compress(x, self.prompt_p)
+        segs = compress(x, self.prompt_p, roles=[ROLE_KEYS] * (B * H) + [ROLE_VALUES] * (B * H))
         C = len(segs) // (2 * B * H)
         for t in range(2):
             for b in range(B):
@@ -310,7 +392,8 @@ class OracleCache:
             B, H, nb, d = self.buf_k.shape
             x = np.concatenate([self.buf_k.reshape(B * H, nb, d),
                                 self.buf_v.reshape(B * H, nb, d)])
-            segs = compress(x, Params(**{**self.fill_p.__dict__, "chunk_tokens": 0}))
+            segs = compress(x, Params(**{**self.fill_p.__dict__, "chunk_tokens": 0}),
+                            roles=[ROLE_KEYS] * (B * H) + [ROLE_VALUES] * (B * H))
             self.fill_inputs.append(x)
             for t in range(2):
                 for b in range(B):

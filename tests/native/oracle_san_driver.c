@@ -21,6 +21,15 @@ void orc_compress_matrix(const uint16_t *x, int64_t n, int64_t d, int bits, int 
                          uint16_t *val, double *A, double *B, double *L, double *xhat);
 void orc_attention(const double *K, const double *V, int64_t ntok, int64_t d,
                    const double *q, double scale, double *out);
+void orc_compress_matrix_mode(const uint16_t *x, int64_t n, int64_t d, int bits, int group,
+                              int mode, int32_t ppm, int r, int iters, uint64_t seed,
+                              uint8_t *packed, float *scale, float *zero, int32_t *row_ptr,
+                              uint16_t *col, uint16_t *val, double *A, double *B, double *L,
+                              double *xhat);
+void orc_channel_exponents(const uint16_t *x, int64_t n, int64_t d, int32_t *e);
+uint16_t orc_double_to_half(double v);
+void orc_channel_normalize(const uint16_t *x, int64_t n, int64_t d, const int32_t *e,
+                           uint16_t *xt);
 
 static uint64_t rng_state = 88172645463325252ull;
 static uint64_t next_u64(void)
@@ -40,7 +49,7 @@ static uint16_t rand_half(void)
 }
 
 static int run_case(int64_t n, int64_t d, int bits, int group, int32_t ppm, int r, int iters,
-                    int fill)
+                    int fill, int mode)
 {
     const int64_t k = orc_num_outliers(n, d, ppm);
     uint16_t *x = malloc(sizeof(uint16_t) * n * d);
@@ -56,9 +65,18 @@ static int run_case(int64_t n, int64_t d, int bits, int group, int32_t ppm, int 
     double *B = malloc(sizeof(double) * d * (r > 0 ? r : 1));
     double *L = malloc(sizeof(double) * n * d);
     double *xhat = malloc(sizeof(double) * n * d);
-    orc_compress_matrix(x, n, d, bits, group, ppm, r, iters, 7, packed, scale, zero, row_ptr,
-                        col, val, A, B, L, xhat);
+    orc_compress_matrix_mode(x, n, d, bits, group, mode, ppm, r, iters, 7, packed, scale, zero,
+                             row_ptr, col, val, A, B, L, xhat);
     int bad = row_ptr[n] != (int32_t)k;
+    if (mode == 0) {   /* the ZipCache steps on the same input */
+        int32_t *e = malloc(sizeof(int32_t) * d);
+        uint16_t *xt = malloc(sizeof(uint16_t) * n * d);
+        orc_channel_exponents(x, n, d, e);
+        orc_channel_normalize(x, n, d, e, xt);
+        for (int64_t i = 0; i < n * d; ++i) bad |= (xt[i] & 0x7fffu) > 0x3c00u;   /* |x~| <= 1 */
+        free(e);
+        free(xt);
+    }
     for (int64_t i = 0; i < n * d; ++i) bad |= !isfinite(xhat[i]);
     free(x); free(packed); free(scale); free(zero); free(row_ptr); free(col); free(val);
     free(A); free(B); free(L); free(xhat);
@@ -69,15 +87,18 @@ int main(void)
 {
     int bad = 0;
     for (uint32_t h = 0; h < 0x7c00u; h += 7) bad |= !isfinite(orc_half_to_double((uint16_t)h));
-    bad |= run_case(256, 64, 4, 64, 20000, 4, 3, 0);
-    bad |= run_case(37, 64, 2, 16, 30000, 1, 1, 0);
-    bad |= run_case(100, 128, 4, 32, 20000, 3, 2, 0);
-    bad |= run_case(64, 128, 2, 8, 1000000, 2, 2, 0);    /* every entry an outlier */
-    bad |= run_case(64, 64, 4, 64, 0, 0, 0, 0);          /* plain quantization */
-    bad |= run_case(16, 8 * 8, 4, 8, 50000, 8, 4, 0);
-    bad |= run_case(8, 64, 4, 64, 20000, 8, 2, 0);       /* r = n (full rank) */
-    bad |= run_case(32, 64, 4, 32, 20000, 4, 3, 1);      /* zero matrix */
-    bad |= run_case(32, 64, 2, 64, 20000, 4, 3, 2);      /* constant matrix */
+    bad |= run_case(256, 64, 4, 64, 20000, 4, 3, 0, 0);
+    bad |= run_case(37, 64, 2, 16, 30000, 1, 1, 0, 0);
+    bad |= run_case(100, 128, 4, 32, 20000, 3, 2, 0, 0);
+    bad |= run_case(64, 128, 2, 8, 1000000, 2, 2, 0, 0);    /* every entry an outlier */
+    bad |= run_case(64, 64, 4, 64, 0, 0, 0, 0, 0);          /* plain quantization */
+    bad |= run_case(16, 8 * 8, 4, 8, 50000, 8, 4, 0, 0);
+    bad |= run_case(8, 64, 4, 64, 20000, 8, 2, 0, 0);       /* r = n (full rank) */
+    bad |= run_case(32, 64, 4, 32, 20000, 4, 3, 1, 0);      /* zero matrix */
+    bad |= run_case(32, 64, 2, 64, 20000, 4, 3, 2, 0);      /* constant matrix */
+    bad |= run_case(128, 64, 4, 32, 20000, 4, 3, 0, 1);     /* per-channel (KIVI keys) */
+    bad |= run_case(64, 128, 2, 64, 0, 2, 2, 0, 1);
+    for (double v = 1e-9; v < 1e6; v *= 1.37) bad |= orc_double_to_half(v) == 0x7e00u;
     {
         double P[12] = {1, 2, 3, 2, 4, 6, 0, 0, 0, 1, 0, 1};   /* dependent and zero columns */
         orc_mgs(P, 4, 3);

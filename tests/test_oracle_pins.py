@@ -7,6 +7,7 @@ wrong sign or index, a transposed operand, an off-by-one iteration count)
 fails it.
 """
 import itertools
+import math
 import os
 
 import numpy as np
@@ -459,3 +460,140 @@ def test_chunked_prompt_segments_in_token_order():
             for c in range(C):
                 assert np.all(K[c * ct:(c + 1) * ct] == val(0, b, h, c))
                 assert np.all(V[c * ct:(c + 1) * ct] == val(1, b, h, c))
+
+
+# ---------------------------------------------------------------- KIVI keys: per-channel groups
+
+def test_channel_quantizer_hand_worked_example():
+    """tests/golden/quant_channel_worked.txt: a 4 x 2 matrix quantized per
+    channel with groups of 4 tokens at 2 bits, worked by hand."""
+    rows = {}
+    with open(os.path.join(GOLDEN, "quant_channel_worked.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                k, *v = line.split()
+                rows[k] = v
+    D = np.array([[0, -1, 0, 5], [2, 0, 0, 5], [4, 1.5, 0, 5], [6, 2, 0, 5]], np.float32)
+    code, scale, zero = orc.quantize_channel(D, 2, 4)
+    assert code.ravel().tolist() == [int(v) for v in rows["codes"]]
+    assert scale.ravel().tolist() == [float(v) for v in rows["scale"]]
+    assert zero.ravel().tolist() == [float(v) for v in rows["zero"]]
+    assert orc.pack_codes(code, 2).ravel().tolist() == [int(v, 16) for v in rows["packed"]]
+    deq = orc.dequantize_channel(code, scale, zero, 4)
+    assert deq.ravel().tolist() == [float(v) for v in rows["deq"]]
+
+
+@pytest.mark.parametrize("bits,group", [(2, 4), (4, 8), (4, 64), (2, 32)])
+def test_channel_quantizer_is_the_group_quantizer_on_the_transpose(bits, group):
+    """Groups of g tokens of one channel are groups of g columns of one row of
+    D^T: codes, scales and zeros must be the transposes of the (pinned)
+    group quantizer's on D^T."""
+    rng = _rng(40 + group)
+    n, d = 128, 64
+    D = (rng.standard_normal((n, d)) * np.exp(rng.standard_normal(d))).astype(np.float32)
+    D[rng.random((n, d)) < 0.05] = 0.0
+    c1, s1, z1 = orc.quantize_channel(D, bits, group)
+    c2, s2, z2 = orc.quantize(np.ascontiguousarray(D.T), bits, group)
+    assert np.array_equal(c1, c2.T)
+    assert np.array_equal(s1.view(np.uint32), s2.T.view(np.uint32))
+    assert np.array_equal(z1.view(np.uint32), z2.T.view(np.uint32))
+    deq = orc.dequantize_channel(c1, s1, z1, group)
+    assert np.array_equal(deq, orc.dequantize(c2, s2, z2, group).T)
+
+
+def test_kivi_keys_and_values_in_one_compression():
+    """With the KIVI backbone a key matrix is quantized per channel and a
+    value matrix per token (as GEAR's own); everything else is unchanged."""
+    rng = _rng(41)
+    x = _f16(rng.standard_normal((128, 64)) * 2.0)
+    pk = orc.Params(bits=4, group=32, outlier_ppm=20000, rank=2, power_iters=2, quant=orc.QUANT_KIVI)
+    pg = orc.Params(bits=4, group=32, outlier_ppm=20000, rank=2, power_iters=2)
+    kv = orc.compress_matrix(x, pk, orc.ROLE_VALUES)
+    gv = orc.compress_matrix(x, pg)
+    assert np.array_equal(kv.packed, gv.packed) and np.array_equal(kv.L, gv.L)
+    kk = orc.compress_matrix(x, pk, orc.ROLE_KEYS)
+    assert kk.scale.shape == (128 // 32, 64)
+    assert np.array_equal(kk.row_ptr, gv.row_ptr) and np.array_equal(kk.val, gv.val)
+    # the reconstruction is the per-channel dequantization + L + S
+    mask = orc.select_outliers(x, len(kk.col))
+    xs = x.astype(np.float64)
+    D = np.where(mask, 0.0, xs).astype(np.float32)
+    code, sc, zr = orc.quantize_channel(D, 4, 32)
+    deq = orc.dequantize_channel(code, sc, zr, 32)
+    assert np.allclose(kk.xhat, deq + kk.L + np.where(mask, xs, 0.0), atol=1e-12)
+    # plain per-channel quantization error bound (s = 0, r = 0)
+    p0 = orc.Params(bits=4, group=32, outlier_ppm=0, rank=0, power_iters=0, quant=orc.QUANT_KIVI)
+    c0 = orc.compress_matrix(x, p0, orc.ROLE_KEYS)
+    half = np.repeat(c0.scale.astype(np.float64), 32, axis=0) / 2
+    assert np.all(np.abs(c0.xhat - xs) <= half + 1e-6 * np.abs(xs) + 1e-12)
+
+
+# ---------------------------------------------------------------- ZipCache: channels separated out
+
+def test_double_to_half_rounds_like_numpy():
+    """The oracle's fp16 rounding (ties to even, subnormals, overflow) against
+    numpy's conversion, on random doubles of every magnitude, exact ties and
+    the edges of the format."""
+    rng = _rng(42)
+    mags = np.ldexp(rng.random(20000) + 0.5, rng.integers(-30, 17, 20000))
+    vals = list(mags * np.where(rng.random(20000) < 0.5, -1, 1))
+    h = np.arange(0, 0x7bff, 37, dtype=np.uint16).view(np.float16).astype(np.float64)
+    nxt = np.arange(1, 0x7c00, 37, dtype=np.uint16).view(np.float16).astype(np.float64)
+    vals += list((h + nxt) / 2)                      # exact ties
+    vals += [0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 65504.0, 65519.99, 65520.0, 1e6,
+             2.0 ** -14 - 2.0 ** -25, 2.0 ** -14 - 2.0 ** -26]
+    with np.errstate(over="ignore"):      # 1e6 and 65520 become infinity, as they must
+        for v in vals:
+            assert orc.double_to_half(v) == int(np.array(v).astype(np.float16).view(np.uint16)), v
+
+
+def test_channel_exponents_and_normalization():
+    rng = _rng(43)
+    n, d = 50, 16
+    x = rng.standard_normal((n, d)) * np.ldexp(1.0, rng.integers(-12, 12, d))[None, :]
+    x[:, 3] = 0.0                                   # an all-zero channel
+    x[7, 5] = 4.0                                   # a channel whose max is a power of two
+    x[:, 5] = np.clip(x[:, 5], -4.0, 4.0)
+    x16 = _f16(x)
+    e = orc.channel_exponents(x16)
+    for j in range(d):
+        m = float(np.max(np.abs(x16[:, j].astype(np.float64))))
+        if m == 0.0:
+            assert e[j] == 0
+        else:
+            k = math.ceil(math.log2(m))
+            assert 2.0 ** k >= m > 2.0 ** (k - 1)
+            assert e[j] == k
+    assert e[5] == 2
+    xt = orc.channel_normalize(x16, e)
+    want = (x16.astype(np.float64) * np.ldexp(1.0, -e)[None, :]).astype(np.float16)
+    assert np.array_equal(xt, want.view(np.uint16))
+    assert np.all(np.abs(xt.view(np.float16).astype(np.float64)) <= 1.0)
+
+
+def test_zipcache_is_gear_tokenwise_on_the_normalized_matrix():
+    """With every channel maximum in (1/2, 1] the factors are 1 and the
+    ZipCache backbone is GEAR with one group per token; scaling a channel by
+    2^k leaves every stored section unchanged and scales that channel of X^
+    by 2^k."""
+    rng = _rng(44)
+    n, d = 96, 64
+    x = rng.uniform(-1.0, 1.0, (n, d))
+    x = np.sign(x) * np.maximum(np.abs(x), 2.0 ** -7)   # no subnormal after a 2^-6 scaling
+    x[0, :] = 1.0                                   # every channel max exactly 1
+    x16 = _f16(x)
+    pz = orc.Params(bits=4, group=64, outlier_ppm=20000, rank=3, power_iters=2, quant=orc.QUANT_ZIPCACHE)
+    pg = orc.Params(bits=4, group=64, outlier_ppm=20000, rank=3, power_iters=2)
+    z = orc.compress_matrix(x16, pz)
+    g = orc.compress_matrix(x16, pg)
+    assert np.all(z.chan == 1.0)
+    for f in ("packed", "scale", "zero", "row_ptr", "col", "val"):
+        assert np.array_equal(getattr(z, f), getattr(g, f)), f
+    assert np.array_equal(z.xhat, g.xhat)
+    k = rng.integers(-6, 7, d)
+    xs = _f16(x16.astype(np.float64) * np.ldexp(1.0, k)[None, :])
+    zs = orc.compress_matrix(xs, pz)
+    assert np.array_equal(zs.chan, np.ldexp(1.0, k).astype(np.float32))
+    for f in ("packed", "scale", "zero", "row_ptr", "col", "val", "A", "B"):
+        assert np.array_equal(getattr(zs, f), getattr(z, f)), f
+    assert np.allclose(zs.xhat, z.xhat * np.ldexp(1.0, k)[None, :], rtol=0, atol=0)
