@@ -42,8 +42,9 @@
  *     not thread-safe.
  *
  * Limits of this implementation: head_dim 64 or 128; bits 2 or 4; group in
- * {8,16,32,64,128} dividing head_dim; rank <= 8 (and <= tokens per matrix);
- * power_iters >= 1 when rank > 0 and <= 64.
+ * {8,16,32,64,128} dividing head_dim (KIVI keys: 16..128 dividing the tokens
+ * per matrix); rank <= 8 (and <= tokens per matrix); power_iters >= 1 when
+ * rank > 0 and <= 64.
  */
 #ifndef GEAR_H
 #define GEAR_H
@@ -64,6 +65,32 @@ typedef enum {
     GEAR_ERR_WORKSPACE = 5     /* workspace too small */
 } gear_status;
 
+/*
+ * Quantization backbone (the Q step; outliers and the low-rank fit are the
+ * same for all):
+ *   GEAR_QUANT_GROUP     GEAR's own: groups of `group` consecutive head_dim
+ *                        columns of one token, for keys and values.
+ *   GEAR_QUANT_KIVI      KIVI's (app.cochat.ai GEAR page, "Cites" list, the
+ *                        KIVI entry, and the "Cited by" quote that KIVI
+ *                        quantizes keys per channel and values per token):
+ *                        keys in groups of `group` consecutive tokens of one
+ *                        channel, values as GEAR_QUANT_GROUP.  Keys need
+ *                        outlier_ppm = 0 in this library (GEAR-L with a KIVI
+ *                        backbone) and tokens per matrix divisible by group.
+ *   GEAR_QUANT_ZIPCACHE  ZipCache's channel-separable tokenwise quantization
+ *                        ("ZipCache: Accurate and Efficient KV Cache
+ *                        Quantization with Salient Token Identification",
+ *                        abstract): channel j is divided by 2^e_j, the
+ *                        smallest power of two not below its largest |x|
+ *                        (e_j = 0 for an all-zero channel; the normalized
+ *                        entries rounded to fp16, to nearest even), GEAR runs
+ *                        on the normalized matrix with one group per token
+ *                        (group must equal head_dim), and the reconstruction
+ *                        multiplies channel j back by 2^e_j.  The factors are
+ *                        stored in the packed `chan` section.
+ */
+typedef enum { GEAR_QUANT_GROUP = 0, GEAR_QUANT_KIVI = 1, GEAR_QUANT_ZIPCACHE = 2 } gear_quant;
+
 /* GEAR settings.  Outlier share s = outlier_ppm / 1e6; k = floor(n*d*s). */
 typedef struct {
     int32_t bits;          /* b: 2 or 4 */
@@ -76,7 +103,18 @@ typedef struct {
                               n_tokens) */
     uint64_t seed;         /* B0[j][c] = top 24 bits of splitmix64 output
                               (j*r + c + 1) from state `seed`, * 2^-23 - 1 */
+    int32_t quant;         /* gear_quant */
+    int32_t reserved;      /* must be 0 */
 } gear_params;
+
+/* What the matrices of a stack hold (only the KIVI backbone treats keys and
+   values differently). */
+typedef enum {
+    GEAR_ROLE_KEYS = 0,
+    GEAR_ROLE_VALUES = 1,
+    GEAR_ROLE_KEYS_THEN_VALUES = 2   /* num_mats even: the first half keys, the
+                                        second half values (a cache segment) */
+} gear_role;
 
 /* A stack of num_mats matrices, each n_tokens x head_dim fp16, row-major,
    contiguous: element (m, t, j) at ((m * n_tokens + t) * head_dim + j). */
@@ -84,6 +122,8 @@ typedef struct {
     int64_t num_mats;
     int32_t n_tokens;
     int32_t head_dim;
+    int32_t role;          /* gear_role */
+    int32_t reserved;      /* must be 0 */
 } gear_shape;
 
 /*
@@ -93,22 +133,25 @@ typedef struct {
  *   codes   u8  [M][rows][head_dim*bits/8]  code of column j of a token at
  *                                           byte j*bits/8, bit (j*bits)%8,
  *                                           least significant bits first
- *   scale   f32 [M][rows][head_dim/group]
- *   zero    f32 [M][rows][head_dim/group]   (= group minimum)
+ *   scale   f32 [M][rows][head_dim/group]   (KIVI keys: [M][rows/group][head_dim])
+ *   zero    f32 [M][rows][head_dim/group]   (= group minimum; layout as scale)
  *   row_ptr i32 [M][rows+1]                 CSR of S, offsets into col/val of
  *                                           the same matrix; row_ptr[rows] = k
  *   col     u16 [M][k]                      ascending within a token
  *   val     f16 [M][k]                      the original entries, exact
  *   A       f32 [M][rows][rank]
  *   B       f32 [M][head_dim][rank]         L = A B^T
- * Offsets are relative to the buffer start; the buffer holds no pointers, so
- * it may be copied or saved as plain bytes.
+ *   chan    f32 [M][head_dim]               ZipCache: channel factors 2^e_j
+ *                                           (empty for the other backbones)
+ * With ZipCache, codes, scales, zeros, outlier values, A and B describe the
+ * normalized matrix.  Offsets are relative to the buffer start; the buffer
+ * holds no pointers, so it may be copied or saved as plain bytes.
  */
 typedef struct {
     int64_t num_compressed;  /* M */
     int32_t rows;            /* tokens per compressed matrix */
     int32_t k;               /* outliers per compressed matrix */
-    size_t off_codes, off_scale, off_zero, off_row_ptr, off_col, off_val, off_a, off_b;
+    size_t off_codes, off_scale, off_zero, off_row_ptr, off_col, off_val, off_a, off_b, off_chan;
     size_t total_bytes;
 } gear_layout;
 
@@ -118,7 +161,8 @@ gear_status gear_packed_layout(const gear_params* p, const gear_shape* s, gear_l
 /* Bytes of the packed buffer; 0 if the settings are rejected. */
 size_t gear_packed_bytes(const gear_params* p, const gear_shape* s);
 
-/* Bytes of device workspace gear_compress needs; 0 if rejected. */
+/* Bytes of device workspace gear_compress needs; 0 if rejected (ZipCache
+   adds room for the normalized copy of the stack). */
 size_t gear_compress_workspace_bytes(const gear_params* p, const gear_shape* s);
 
 /*
@@ -173,7 +217,10 @@ gear_status gear_decompress(const gear_params* p, const gear_shape* s, const voi
 
 typedef struct {
     gear_params prompt;       /* settings for the prompt (chunk_tokens allowed) */
-    gear_params fill;         /* settings for each full buffer (chunk_tokens ignored) */
+    gear_params fill;         /* settings for each full buffer (chunk_tokens ignored);
+                                 same backbone (quant) as the prompt.  With the
+                                 KIVI backbone buf_tokens must be a multiple of
+                                 the key group: the buffer holds whole groups */
     int32_t batch;            /* B */
     int32_t kv_heads;         /* Hkv */
     int32_t head_dim;         /* d */

@@ -32,16 +32,21 @@ class GearError(RuntimeError):
         self.status = status
 
 
+# quantization backbones (gear_quant) and roles of a stack (gear_role)
+QUANT_GROUP, QUANT_KIVI, QUANT_ZIPCACHE = 0, 1, 2
+ROLE_KEYS, ROLE_VALUES, ROLE_KEYS_THEN_VALUES = 0, 1, 2
+
+
 class _Params(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("outlier_ppm", ctypes.c_int32), ("rank", ctypes.c_int32),
                 ("power_iters", ctypes.c_int32), ("chunk_tokens", ctypes.c_int32),
-                ("seed", ctypes.c_uint64)]
+                ("seed", ctypes.c_uint64), ("quant", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _Shape(ctypes.Structure):
     _fields_ = [("num_mats", ctypes.c_int64), ("n_tokens", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32)]
+                ("head_dim", ctypes.c_int32), ("role", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class _Layout(ctypes.Structure):
@@ -49,7 +54,7 @@ class _Layout(ctypes.Structure):
                 ("off_codes", ctypes.c_size_t), ("off_scale", ctypes.c_size_t),
                 ("off_zero", ctypes.c_size_t), ("off_row_ptr", ctypes.c_size_t),
                 ("off_col", ctypes.c_size_t), ("off_val", ctypes.c_size_t),
-                ("off_a", ctypes.c_size_t), ("off_b", ctypes.c_size_t),
+                ("off_a", ctypes.c_size_t), ("off_b", ctypes.c_size_t), ("off_chan", ctypes.c_size_t),
                 ("total_bytes", ctypes.c_size_t)]
 
 
@@ -77,7 +82,7 @@ EXPORTS = ["gear_packed_layout", "gear_packed_bytes", "gear_compress_workspace_b
 
 # Kernel names accepted by gear_timing_read.
 KERNELS = ["select", "compress", "lowrank_a", "decompress", "attn_split", "attn_combine",
-           "buffer_append"]
+           "buffer_append", "channel"]
 
 _lib = None
 
@@ -149,8 +154,9 @@ def _ptr(t: torch.Tensor):
 
 @dataclass(frozen=True)
 class Params:
-    """GEAR settings (bits b, group g along head_dim, outlier share in ppm,
-    rank r, power-iteration steps t, optional token chunking, B0 seed)."""
+    """GEAR settings (bits b, group g, outlier share in ppm, rank r,
+    power-iteration steps t, optional token chunking, B0 seed, quantization
+    backbone: QUANT_GROUP (GEAR's own), QUANT_KIVI, QUANT_ZIPCACHE)."""
     bits: int = 4
     group: int = 128
     outlier_ppm: int = 20000
@@ -158,44 +164,56 @@ class Params:
     power_iters: int = 3
     chunk_tokens: int = 0
     seed: int = 0
+    quant: int = QUANT_GROUP
 
     def _c(self) -> _Params:
         return _Params(self.bits, self.group, self.outlier_ppm, self.rank, self.power_iters,
-                       self.chunk_tokens, self.seed)
+                       self.chunk_tokens, self.seed, self.quant, 0)
 
 
-def _shape(num_mats: int, n: int, d: int) -> _Shape:
-    return _Shape(num_mats, n, d)
+def _shape(num_mats: int, n: int, d: int, role: int = ROLE_KEYS) -> _Shape:
+    return _Shape(num_mats, n, d, role, 0)
 
 
-def packed_layout(p: Params, num_mats: int, n_tokens: int, head_dim: int) -> _Layout:
+def packed_layout(p: Params, num_mats: int, n_tokens: int, head_dim: int,
+                  role: int = ROLE_KEYS) -> _Layout:
     L = _Layout()
-    _check(lib().gear_packed_layout(ctypes.byref(p._c()), ctypes.byref(_shape(num_mats, n_tokens, head_dim)),
-                                    ctypes.byref(L)))
+    _check(lib().gear_packed_layout(ctypes.byref(p._c()),
+                                    ctypes.byref(_shape(num_mats, n_tokens, head_dim, role)), ctypes.byref(L)))
     return L
 
 
-def compress_workspace_bytes(p: Params, num_mats: int, n_tokens: int, head_dim: int) -> int:
+def compress_workspace_bytes(p: Params, num_mats: int, n_tokens: int, head_dim: int,
+                             role: int = ROLE_KEYS) -> int:
     n = lib().gear_compress_workspace_bytes(ctypes.byref(p._c()),
-                                            ctypes.byref(_shape(num_mats, n_tokens, head_dim)))
+                                            ctypes.byref(_shape(num_mats, n_tokens, head_dim, role)))
     if n == 0:
         _check(1)
     return n
 
 
 class Packed:
-    """A compressed stack: one uint8 device buffer plus typed section views."""
+    """A compressed stack: one uint8 device buffer plus typed section views.
+    role: which matrices hold keys (only the KIVI backbone cares)."""
 
     def __init__(self, buf: torch.Tensor, p: Params, num_mats: int, n_tokens: int, head_dim: int,
-                 layout: _Layout):
+                 layout: _Layout, role: int = ROLE_KEYS):
         self.buf, self.params = buf, p
         self.num_mats, self.n_tokens, self.head_dim = num_mats, n_tokens, head_dim
         self.layout = layout
+        self.role = role
 
     def sections(self):
-        """The eight sections, in layout order (alignment padding excluded)."""
-        return [self.codes(), self.scale(), self.zero(), self.row_ptr(), self.col(), self.val(),
-                self.A(), self.B()]
+        """The sections, in layout order (alignment padding excluded)."""
+        out = [self.codes(), self.scale(), self.zero(), self.row_ptr(), self.col(), self.val(),
+               self.A(), self.B()]
+        if self.params.quant == QUANT_ZIPCACHE:
+            out.append(self.chan())
+        return out
+
+    def chan(self):
+        """ZipCache channel factors [M, d] (float32)."""
+        return self._sec(self.layout.off_chan, self.M * self.head_dim, torch.float32).view(self.M, self.head_dim)
 
     def _sec(self, off: int, count: int, dtype: torch.dtype) -> torch.Tensor:
         nbytes = count * torch.tensor([], dtype=dtype).element_size()
@@ -250,18 +268,18 @@ def _check_input(x: torch.Tensor):
 
 
 def compress(x: torch.Tensor, p: Params, out: Packed | None = None,
-             workspace: torch.Tensor | None = None) -> Packed:
+             workspace: torch.Tensor | None = None, role: int = ROLE_KEYS) -> Packed:
     """x: fp16 [M, n, d] (or [..., n, d]) on the GPU -> Packed."""
     _check_input(x)
     n, d = x.shape[-2], x.shape[-1]
     M = x.numel() // (n * d)
-    L = packed_layout(p, M, n, d)
+    L = packed_layout(p, M, n, d, role)
     if out is None:
-        out = Packed(torch.empty(L.total_bytes, dtype=torch.uint8, device=x.device), p, M, n, d, L)
+        out = Packed(torch.empty(L.total_bytes, dtype=torch.uint8, device=x.device), p, M, n, d, L, role)
     if workspace is None:
-        workspace = torch.empty(max(compress_workspace_bytes(p, M, n, d), 256), dtype=torch.uint8,
+        workspace = torch.empty(max(compress_workspace_bytes(p, M, n, d, role), 256), dtype=torch.uint8,
                                 device=x.device)
-    _check(lib().gear_compress(ctypes.byref(p._c()), ctypes.byref(_shape(M, n, d)), _ptr(x),
+    _check(lib().gear_compress(ctypes.byref(p._c()), ctypes.byref(_shape(M, n, d, role)), _ptr(x),
                                _ptr(out.buf), _ptr(workspace), workspace.numel(), _stream()))
     return out
 
@@ -272,8 +290,8 @@ def compress_noalloc(x: torch.Tensor, p: Params, out: Packed) -> Packed:
     _check_input(x)
     n, d = x.shape[-2], x.shape[-1]
     M = x.numel() // (n * d)
-    _check(lib().gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(_shape(M, n, d)), _ptr(x),
-                                       _ptr(out.buf), _stream()))
+    _check(lib().gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(_shape(M, n, d, out.role)),
+                                       _ptr(x), _ptr(out.buf), _stream()))
     return out
 
 
@@ -298,7 +316,7 @@ def decompress(packed: Packed, out: torch.Tensor | None = None) -> torch.Tensor:
     if out is None:
         out = torch.empty((M, n, d), dtype=torch.float16, device=packed.buf.device)
     _check_input(out)
-    _check(lib().gear_decompress(ctypes.byref(packed.params._c()), ctypes.byref(_shape(M, n, d)),
+    _check(lib().gear_decompress(ctypes.byref(packed.params._c()), ctypes.byref(_shape(M, n, d, packed.role)),
                                  _ptr(packed.buf), _ptr(out), _stream()))
     return out
 
@@ -370,14 +388,14 @@ class Cache:
     def prompt_packed(self) -> Packed:
         c = self.cfg
         M = 2 * c.batch * c.kv_heads
-        L = packed_layout(self.prompt_params, M, c.prompt_tokens, c.head_dim)
+        L = packed_layout(self.prompt_params, M, c.prompt_tokens, c.head_dim, ROLE_KEYS_THEN_VALUES)
         return Packed(self._view(self.info().prompt_packed, L.total_bytes), self.prompt_params, M,
-                      c.prompt_tokens, c.head_dim, L)
+                      c.prompt_tokens, c.head_dim, L, ROLE_KEYS_THEN_VALUES)
 
     def fill_packed(self, f: int) -> Packed:
         c, inf = self.cfg, self.info()
         M = 2 * c.batch * c.kv_heads
         fp = Params(**{**self.fill_params.__dict__, "chunk_tokens": 0})
-        L = packed_layout(fp, M, c.buf_tokens, c.head_dim)
+        L = packed_layout(fp, M, c.buf_tokens, c.head_dim, ROLE_KEYS_THEN_VALUES)
         return Packed(self._view(inf.fill_packed + f * inf.fill_stride, L.total_bytes), fp, M,
-                      c.buf_tokens, c.head_dim, L)
+                      c.buf_tokens, c.head_dim, L, ROLE_KEYS_THEN_VALUES)

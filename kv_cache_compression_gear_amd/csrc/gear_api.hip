@@ -75,7 +75,32 @@ gear_status check_params(const gear_params* p, int64_t rows, int d) {
     if (mrows > (1 << 24))
         return fail(GEAR_ERR_UNSUPPORTED, "%lld tokens per matrix is above this library's limit of %d",
                     (long long)mrows, 1 << 24);
+    if (p->reserved != 0) return fail(GEAR_ERR_INVALID_ARG, "params.reserved must be 0");
+    if (p->quant < GEAR_QUANT_GROUP || p->quant > GEAR_QUANT_ZIPCACHE)
+        return fail(GEAR_ERR_INVALID_ARG, "unknown quantization backbone %d", p->quant);
+    if (p->quant == GEAR_QUANT_ZIPCACHE && p->group != d)
+        return fail(GEAR_ERR_INVALID_ARG,
+                    "ZipCache quantizes tokenwise: group must equal head_dim (%d, got %d)", d, p->group);
     return GEAR_OK;
+}
+
+// Keys quantized per channel (KIVI backbone): the extra conditions.
+gear_status check_channel_keys(const gear_params* p, int64_t mrows) {
+    if (p->group < 16)
+        return fail(GEAR_ERR_UNSUPPORTED, "KIVI key groups must be 16..128 tokens (got %d)", p->group);
+    if (mrows % p->group != 0)
+        return fail(GEAR_ERR_INVALID_ARG, "KIVI keys: %lld tokens per matrix is not a multiple of the group %d",
+                    (long long)mrows, p->group);
+    if (p->outlier_ppm != 0)
+        return fail(GEAR_ERR_UNSUPPORTED,
+                    "KIVI keys are supported without outliers only (outlier_ppm = 0: GEAR-L)");
+    return GEAR_OK;
+}
+
+// Leading matrices of a stack quantized per channel.
+int64_t channel_mats(const gear_params* p, int64_t M, int role) {
+    if (p->quant != GEAR_QUANT_KIVI) return 0;
+    return role == GEAR_ROLE_KEYS ? M : role == GEAR_ROLE_KEYS_THEN_VALUES ? M / 2 : 0;
 }
 
 gear_status compute_layout(const gear_params* p, const gear_shape* s, gear_layout* L) {
@@ -83,7 +108,16 @@ gear_status compute_layout(const gear_params* p, const gear_shape* s, gear_layou
     if (s->num_mats < 0) return fail(GEAR_ERR_INVALID_ARG, "num_mats < 0");
     gear_status st = check_params(p, s->n_tokens, s->head_dim);
     if (st != GEAR_OK) return st;
+    if (s->reserved != 0) return fail(GEAR_ERR_INVALID_ARG, "shape.reserved must be 0");
+    if (s->role < GEAR_ROLE_KEYS || s->role > GEAR_ROLE_KEYS_THEN_VALUES)
+        return fail(GEAR_ERR_INVALID_ARG, "unknown role %d", s->role);
+    if (s->role == GEAR_ROLE_KEYS_THEN_VALUES && s->num_mats % 2 != 0)
+        return fail(GEAR_ERR_INVALID_ARG, "a keys-then-values stack needs an even num_mats");
     const int64_t rows = p->chunk_tokens > 0 ? p->chunk_tokens : s->n_tokens;
+    if (channel_mats(p, s->num_mats, s->role) > 0) {
+        st = check_channel_keys(p, rows);
+        if (st != GEAR_OK) return st;
+    }
     const int64_t M = s->num_mats * (s->n_tokens / rows);
     const int64_t d = s->head_dim;
     const int64_t k = rows * d * (int64_t)p->outlier_ppm / 1000000;
@@ -99,14 +133,17 @@ gear_status compute_layout(const gear_params* p, const gear_shape* s, gear_layou
     L->off_val = off; off = align_up(off + (size_t)(M * k) * 2);
     L->off_a = off; off = align_up(off + (size_t)(M * rows * p->rank) * 4);
     L->off_b = off; off = align_up(off + (size_t)(M * d * p->rank) * 4);
+    L->off_chan = off; off = align_up(off + (p->quant == GEAR_QUANT_ZIPCACHE ? (size_t)(M * d) * 4 : 0));
     L->total_bytes = off;
     return GEAR_OK;
 }
 
-Packed make_packed(const gear_params* p, const gear_layout& L, int d, void* base) {
+Packed make_packed(const gear_params* p, const gear_layout& L, int d, void* base, int role) {
     uint8_t* b = static_cast<uint8_t*>(base);
     Packed k;
     k.M = L.num_compressed;
+    k.ch_mats = channel_mats(p, L.num_compressed, role);
+    k.chan = p->quant == GEAR_QUANT_ZIPCACHE ? reinterpret_cast<float*>(b + L.off_chan) : nullptr;
     k.rows = L.rows;
     k.d = d;
     k.bits = p->bits;
@@ -128,13 +165,19 @@ struct CompressPlan {
     size_t ws_bytes;
 };
 
+// The compress workspace: selection results and the projection for A, then
+// (ZipCache) the normalized copy of the stack.
 CompressPlan plan_compress(const gear_params* p, const gear_layout& L, int d) {
-    return CompressPlan{compress_workspace(L.num_compressed, d, p->rank)};
+    size_t n = compress_workspace(L.num_compressed, d, p->rank);
+    if (p->quant == GEAR_QUANT_ZIPCACHE)
+        n = align_up(n) + align_up((size_t)L.num_compressed * L.rows * d * 2);
+    return CompressPlan{n};
 }
 
-// Compress matrices [0, m_split) from x and [m_split, M) from x2.
+// Compress matrices [0, m_split) from x and [m_split, M) from x2; role as in
+// gear_shape (which matrices are keys).
 gear_status run_compress(const gear_params* p, const gear_layout& L, int d, const void* x,
-                         const void* x2, int64_t m_split, void* packed, void* ws,
+                         const void* x2, int64_t m_split, int role, void* packed, void* ws,
                          size_t ws_bytes, hipStream_t st) {
     const CompressPlan pl = plan_compress(p, L, d);
     if (ws_bytes < pl.ws_bytes)
@@ -145,13 +188,36 @@ gear_status run_compress(const gear_params* p, const gear_layout& L, int d, cons
     a.x = static_cast<const uint16_t*>(x);
     a.x2 = static_cast<const uint16_t*>(x2);
     a.m_split = m_split;
-    a.out = make_packed(p, L, d, packed);
+    a.m0 = 0;
+    a.m1 = L.num_compressed;
+    a.chan_q = 0;
+    a.out = make_packed(p, L, d, packed, role);
     a.iters = p->power_iters;
     a.seed = p->seed;
     a.sel = static_cast<uint32_t*>(ws);
+    const size_t base_ws = align_up(compress_workspace(L.num_compressed, d, p->rank));
     a.bf = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) +
                                     align_up((size_t)L.num_compressed * kSelStride * 4));
-    hipError_t e = launch_compress(a, st);
+    hipError_t e = hipSuccess;
+    if (p->quant == GEAR_QUANT_ZIPCACHE) {
+        // channel factors, then the normalized stack, which the GEAR steps read
+        uint16_t* xt = reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(ws) + base_ws);
+        e = launch_channel_normalize(a, xt, st);
+        if (e != hipSuccess) return hip_fail(e, "channel normalization launch");
+        a.x = a.x2 = xt;
+        a.m_split = L.num_compressed;
+    }
+    const int64_t kc = a.out.ch_mats;
+    if (kc > 0) {   // KIVI keys: per-channel parameters, then the compression
+        CompressArgs ak = a;
+        ak.m1 = kc;
+        ak.chan_q = 1;
+        e = launch_channel_params(ak, st);
+        if (e == hipSuccess) e = launch_compress(ak, st);
+        if (e != hipSuccess) return hip_fail(e, "compress launch (keys per channel)");
+        a.m0 = kc;
+    }
+    if (a.m0 < a.m1) e = launch_compress(a, st);
     if (e != hipSuccess) return hip_fail(e, "compress launch");
     return GEAR_OK;
 }
@@ -201,7 +267,8 @@ gear_status scratch_of_current_device(void** out) {
 namespace {
 
 const char* const kKernelNames[kKernelCount] = {
-    "select", "compress", "lowrank_a", "decompress", "attn_split", "attn_combine", "buffer_append"};
+    "select", "compress", "lowrank_a", "decompress", "attn_split", "attn_combine", "buffer_append",
+    "channel"};
 
 struct TimingRec {
     KernelId k;
@@ -281,7 +348,7 @@ gear_status cache_layouts(const gear_cache_config* c, gear_layout* pl, gear_layo
     const int64_t mats = 2LL * c->batch * c->kv_heads;
     size_t off = 0;
     if (c->prompt_tokens > 0) {
-        gear_shape s{mats, c->prompt_tokens, c->head_dim};
+        gear_shape s{mats, c->prompt_tokens, c->head_dim, GEAR_ROLE_KEYS_THEN_VALUES, 0};
         gear_status st = compute_layout(&c->prompt, &s, pl);
         if (st != GEAR_OK) return st;
         off = pl->total_bytes;
@@ -290,7 +357,13 @@ gear_status cache_layouts(const gear_cache_config* c, gear_layout* pl, gear_layo
     }
     gear_params fp = c->fill;
     fp.chunk_tokens = 0;
-    gear_shape fs{mats, c->buf_tokens, c->head_dim};
+    if (c->prompt_tokens > 0 && fp.quant != c->prompt.quant)
+        return fail(GEAR_ERR_INVALID_ARG, "prompt and fill settings must use the same backbone");
+    if (fp.quant == GEAR_QUANT_KIVI && c->buf_tokens % fp.group != 0)
+        return fail(GEAR_ERR_INVALID_ARG,
+                    "KIVI backbone: the buffer (%d tokens) must hold whole key groups of %d tokens",
+                    c->buf_tokens, fp.group);
+    gear_shape fs{mats, c->buf_tokens, c->head_dim, GEAR_ROLE_KEYS_THEN_VALUES, 0};
     gear_status st = compute_layout(&fp, &fs, fl);
     if (st != GEAR_OK) return st;
     *max_fills = c->max_new_tokens / c->buf_tokens;
@@ -382,9 +455,9 @@ gear_status gear_compress(const gear_params* p, const gear_shape* s, const void*
         return fail(GEAR_ERR_INVALID_ARG, "NULL device pointer");
     if (!aligned(x_f16, 16) || !aligned(packed, kAlign) || !aligned(workspace, kAlign))
         return fail(GEAR_ERR_INVALID_ARG, "x_f16 must be 16-byte, packed/workspace 256-byte aligned");
-    const int64_t half = s->num_mats * (s->n_tokens / L.rows);
-    return run_compress(p, L, s->head_dim, x_f16, x_f16, half, packed, workspace, workspace_bytes,
-                        static_cast<hipStream_t>(stream));
+    const int64_t all = s->num_mats * (s->n_tokens / L.rows);
+    return run_compress(p, L, s->head_dim, x_f16, x_f16, all, s->role, packed, workspace,
+                        workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 gear_status gear_compress_noalloc(const gear_params* p, const gear_shape* s, const void* x_f16,
@@ -406,8 +479,8 @@ gear_status gear_compress_noalloc(const gear_params* p, const gear_shape* s, con
     void* ws = nullptr;
     st = scratch_of_current_device(&ws);
     if (st != GEAR_OK) return st;
-    const int64_t half = s->num_mats * (s->n_tokens / L.rows);
-    return run_compress(p, L, s->head_dim, x_f16, x_f16, half, packed, ws,
+    const int64_t all = s->num_mats * (s->n_tokens / L.rows);
+    return run_compress(p, L, s->head_dim, x_f16, x_f16, all, s->role, packed, ws,
                         (size_t)GEAR_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
 }
 
@@ -420,7 +493,7 @@ gear_status gear_decompress(const gear_params* p, const gear_shape* s, const voi
         return fail(GEAR_ERR_INVALID_ARG, "NULL device pointer");
     if (!aligned(packed, kAlign) || !aligned(out_f16, 16))
         return fail(GEAR_ERR_INVALID_ARG, "packed must be 256-byte, out_f16 16-byte aligned");
-    Packed k = make_packed(p, L, s->head_dim, const_cast<void*>(packed));
+    Packed k = make_packed(p, L, s->head_dim, const_cast<void*>(packed), s->role);
     hipError_t e = launch_decompress(k, static_cast<uint16_t*>(out_f16), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decompress launch");
     return GEAR_OK;
@@ -507,8 +580,8 @@ gear_status gear_cache_load_prompt(gear_cache* g, const void* k_f16, const void*
         return fail(GEAR_ERR_INVALID_ARG, "k/v must be 16-byte, workspace 256-byte aligned");
     const int64_t half = (int64_t)c.batch * c.kv_heads * (c.prompt_tokens / g->prompt_layout.rows);
     gear_status st = run_compress(&c.prompt, g->prompt_layout, c.head_dim, k_f16, v_f16, half,
-                                  g->arena + g->off_prompt, workspace, workspace_bytes,
-                                  static_cast<hipStream_t>(stream));
+                                  GEAR_ROLE_KEYS_THEN_VALUES, g->arena + g->off_prompt, workspace,
+                                  workspace_bytes, static_cast<hipStream_t>(stream));
     if (st == GEAR_OK) g->prompt_loaded = true;
     if (st == GEAR_ERR_HIP) g->failed = true;
     return st;
@@ -560,7 +633,7 @@ gear_status gear_append_tokens(gear_cache* g, const void* k_new_f16, const void*
         if (g->buf_len == c.buf_tokens) {
             uint8_t* dst = g->arena + g->off_fills + (size_t)g->num_fills * g->fill_stride;
             gear_status s2 = run_compress(&c.fill, g->fill_layout, c.head_dim, buf, buf, 2 * mats_half,
-                                          dst, workspace, workspace_bytes, st);
+                                          GEAR_ROLE_KEYS_THEN_VALUES, dst, workspace, workspace_bytes, st);
             if (s2 != GEAR_OK) {   // checked above: only a failed launch gets here
                 g->failed = true;
                 return s2;
@@ -607,11 +680,12 @@ gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_h
     a.prompt.count = c.prompt_tokens > 0 ? 1 : 0;
     a.prompt.chunks = c.prompt_tokens > 0 ? c.prompt_tokens / g->prompt_layout.rows : 0;
     a.prompt.stride = 0;
+    const int kv = GEAR_ROLE_KEYS_THEN_VALUES;
     if (c.prompt_tokens > 0)
-        a.prompt.p = make_packed(&c.prompt, g->prompt_layout, c.head_dim, g->arena + g->off_prompt);
+        a.prompt.p = make_packed(&c.prompt, g->prompt_layout, c.head_dim, g->arena + g->off_prompt, kv);
     else
-        a.prompt.p = make_packed(&c.fill, g->fill_layout, c.head_dim, g->arena + g->off_fills);
-    a.fills.p = make_packed(&c.fill, g->fill_layout, c.head_dim, g->arena + g->off_fills);
+        a.prompt.p = make_packed(&c.fill, g->fill_layout, c.head_dim, g->arena + g->off_fills, kv);
+    a.fills.p = make_packed(&c.fill, g->fill_layout, c.head_dim, g->arena + g->off_fills, kv);
     a.fills.chunks = 1;
     a.fills.count = g->num_fills;
     a.fills.stride = g->fill_stride;

@@ -260,6 +260,17 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             const Packed& p = pc.p;
             const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
             const uint32_t cmask = (1u << bits) - 1u;
+            // keys per channel (KIVI), channel factors (ZipCache): uniform
+            const bool chk = pc.mk < p.ch_mats;
+            float fk[8], qsf[G];   // the key factors of the lane's columns; sum of q fk
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fk[e] = p.chan ? p.chan[(size_t)pc.mk * D + colq * 8 + e] : 1.0f;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                qsf[h] = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qsf[h] = fmaf(q[h][e], fk[e], qsf[h]);
+            }
             stage_csr(p, pc.mk, pc.row0, pc.len);
             if (r > 0 && wv == 0) {
                 // B^T q: one token row of lanes spans all D columns
@@ -270,7 +281,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     if (rl == 0) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float bv = p.B[((size_t)pc.mk * D + colq * 8 + e) * r + c];
+                            const float bv = p.B[((size_t)pc.mk * D + colq * 8 + e) * r + c] * fk[e];
 #pragma unroll
                             for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], bv, part[h]);
                         }
@@ -323,17 +334,34 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     float part[G];
 #pragma unroll
                     for (int h = 0; h < G; ++h) part[h] = 0.0f;
+                    if (chk) {
+                        // each column's scale and zero, in the token's group
+                        const int tk = min(tok, pc.len - 1);
+                        const float* gs = p.scale + ((size_t)pc.mk * (p.rows / p.group) +
+                                                     (size_t)(pc.row0 + tk) / p.group) * D + colq * 8;
+                        const float* gz = p.zero + (gs - p.scale);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float cf = (float)((word[bf][u] >> (e * bits)) & cmask);
+                        for (int e = 0; e < 8; ++e) {
+                            const float cf = (float)((word[bf][u] >> (e * bits)) & cmask);
+                            const float kv = fmaf(cf, gs[e], gz[e]) * fk[e];
 #pragma unroll
-                        for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], cf, part[h]);
+                            for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], kv, part[h]);
+                        }
+#pragma unroll
+                        for (int h = 0; h < G; ++h) part[h] = row_allreduce<LPR>(fmaf(av[bf][u], qbl[h], part[h]));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float cf = (float)((word[bf][u] >> (e * bits)) & cmask) * fk[e];
+#pragma unroll
+                            for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], cf, part[h]);
+                        }
+                        // + A[t][colq] (B^T q)[colq] in the lanes colq < r, then the row sum
+#pragma unroll
+                        for (int h = 0; h < G; ++h)
+                            part[h] = row_allreduce<LPR>(
+                                fmaf(av[bf][u], qbl[h], fmaf(sc[bf][u], part[h], zp[bf][u] * qsf[h])));
                     }
-                    // + A[t][colq] (B^T q)[colq] in the lanes colq < r, then the row sum
-#pragma unroll
-                    for (int h = 0; h < G; ++h)
-                        part[h] = row_allreduce<LPR>(
-                            fmaf(av[bf][u], qbl[h], fmaf(sc[bf][u], part[h], zp[bf][u] * qs[h])));
                     if (tok < pc.len && colq == 0) {
 #pragma unroll
                         for (int h = 0; h < G; ++h) s_sc[(base + tok) * G + h] = part[h];
@@ -353,7 +381,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 for (int k = s_rp[i]; k < s_rp[i + 1]; ++k) {
                     const uint32_t cv = csr_entry(p, pc.mk, k, i);
                     const int cj = (int)(cv & (D - 1));
-                    const float v = h2f(cv >> 16);
+                    const float v = h2f(cv >> 16) * (p.chan ? p.chan[(size_t)pc.mk * D + cj] : 1.0f);
 #pragma unroll
                     for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
                 }
@@ -454,6 +482,9 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             const uint32_t cmask = (1u << bits) - 1u;
             stage_csr(p, pc.mv, pc.row0, pc.len);
             __syncthreads();
+            float fv[8];   // ZipCache: the value matrix's factors of the lane's columns
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fv[e] = p.chan ? p.chan[(size_t)pc.mv * D + colq * 8 + e] : 1.0f;
             float pa[G];   // sum_t p_t A[t][colq] in the lanes colq < r
 #pragma unroll
             for (int h = 0; h < G; ++h) pa[h] = 0.0f;
@@ -523,7 +554,8 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     for (int h = 0; h < G; ++h) pr[h] = ok ? s_sc[(base + tok) * G + h] : 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float dv = fmaf((float)((word[bf][u] >> (e * bits)) & cmask), sc[bf][u], zp[bf][u]) + sv[e];
+                        const float dv =
+                            (fmaf((float)((word[bf][u] >> (e * bits)) & cmask), sc[bf][u], zp[bf][u]) + sv[e]) * fv[e];
 #pragma unroll
                         for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pr[h], dv, acc[h][e]);
                     }
@@ -555,7 +587,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                              s_pa[(2 * G + h) * kMaxRank + c] + s_pa[(3 * G + h) * kMaxRank + c];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float bv = p.B[((size_t)pc.mv * D + colq * 8 + e) * r + c];
+                    const float bv = p.B[((size_t)pc.mv * D + colq * 8 + e) * r + c] * fv[e];
 #pragma unroll
                     for (int h = 0; h < G; ++h) acc[h][e] = fmaf(tot[h], bv, acc[h][e]);
                 }
@@ -666,7 +698,11 @@ __device__ __forceinline__ void unpack8(uint32_t w, float (&cf)[8]) {
 template <int G>
 constexpr int prompt_waves() { return G == 1 ? 8 : G == 4 ? 4 : 2; }
 
-template <int D, int G, int BITS>
+// QK: the prompt's backbone.  0: GEAR's own; 1: KIVI (keys quantized per
+// channel in groups of p.group tokens: the score takes each column's scale and
+// zero of the token's group); 2: ZipCache (q is taken times the key matrix's
+// channel factors, the output numerators times the value matrix's).
+template <int D, int G, int BITS, int QK = 0>
 __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TPW = kTPS / kFastWaves, SPW = TPW / RPS;
     constexpr int CPT = kFastCap / kFastThreads;      // staged CSR entries per thread
@@ -725,6 +761,9 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     float q[G][8], qs[G];
     {
         const uint16_t* qb = a.q + ((size_t)b * a.Hq + hk * G) * D;
+        float fk[8];   // ZipCache: the key matrix's channel factors of the lane's columns
+#pragma unroll
+        for (int e = 0; e < 8; ++e) fk[e] = QK == 2 ? p.chan[(size_t)pc.mk * D + colq * 8 + e] : 1.0f;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const uint4 w = *reinterpret_cast<const uint4*>(qb + h * D + colq * 8);
@@ -732,11 +771,12 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
             qs[h] = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                q[h][e] = h2f(w4[e >> 1] >> (16 * (e & 1)));
+                q[h][e] = h2f(w4[e >> 1] >> (16 * (e & 1))) * fk[e];   // exact (a power of two)
                 qs[h] += q[h][e];
             }
         }
-        for (int i = tid; i < G * D; i += kFastThreads) s_q[i] = h2f(qb[i]);
+        for (int i = tid; i < G * D; i += kFastThreads)
+            s_q[i] = h2f(qb[i]) * (QK == 2 ? p.chan[(size_t)pc.mk * D + i % D] : 1.0f);
     }
     uint32_t wk[SPW];
     const unsigned char* ck = p.codes + mrk * ROWB;
@@ -753,11 +793,11 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     struct Side {
         f4v gsz, av;
     };
-    auto load_side = [&](size_t mrow) {
+    auto load_side = [&](size_t mrow, bool scales) {
         const int i = tid & 127;
         const float* src = (tid < 128 ? p.scale : p.zero) + mrow * ngr;
         Side sd;
-        sd.gsz = (tid < 256 && i < ng4) ? reinterpret_cast<const f4v*>(src)[i] : z4;
+        sd.gsz = (scales && tid < 256 && i < ng4) ? reinterpret_cast<const f4v*>(src)[i] : z4;
         sd.av = tid < na4 ? reinterpret_cast<const f4v*>(p.A + mrow * r)[tid] : z4;
         return sd;
     };
@@ -767,7 +807,7 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
         if (tid < na4) reinterpret_cast<f4v*>(s_a)[tid] = sd.av;
     };
     {
-        const Side sk = load_side(mrk);
+        const Side sk = load_side(mrk, QK != 1);   // keys per channel: no per-token scales
         const int32_t* rpk = p.row_ptr + (size_t)pc.mk * (p.rows + 1) + pc.row0;
         const int32_t* rpv = p.row_ptr + (size_t)pc.mv * (p.rows + 1) + pc.row0;
         // threads [0, kTPS] read K's row pointers, [256, 256 + kTPS] V's
@@ -838,21 +878,47 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
         const int tok = tok0 + s * RPS;
-        const float scv = s_gs[gidx0 + s * gstep], zpv = s_gz[gidx0 + s * gstep];
         const float av = colq < r ? s_a[aidx0 + s * astep] : 0.0f;
         float cf[8];
         unpack8<BITS>(wk[s], cf);
         float part[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) part[h] = 0.0f;
+        if constexpr (QK == 1) {
+            // keys per channel: scale and zero of each column, the token's group
+            const size_t gb = ((size_t)pc.mk * (p.rows / p.group) + (size_t)(pc.row0 + tok) / p.group) * D +
+                              colq * 8;
+            float csc[8], czp[8];
+            {
+                const float4 s0 = *reinterpret_cast<const float4*>(p.scale + gb);
+                const float4 s1 = *reinterpret_cast<const float4*>(p.scale + gb + 4);
+                const float4 z0 = *reinterpret_cast<const float4*>(p.zero + gb);
+                const float4 z1 = *reinterpret_cast<const float4*>(p.zero + gb + 4);
+                csc[0] = s0.x, csc[1] = s0.y, csc[2] = s0.z, csc[3] = s0.w;
+                csc[4] = s1.x, csc[5] = s1.y, csc[6] = s1.z, csc[7] = s1.w;
+                czp[0] = z0.x, czp[1] = z0.y, czp[2] = z0.z, czp[3] = z0.w;
+                czp[4] = z1.x, czp[5] = z1.y, czp[6] = z1.z, czp[7] = z1.w;
+            }
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+            for (int e = 0; e < 8; ++e)
 #pragma unroll
-            for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], cf[e], part[h]);
+                for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], fmaf(cf[e], csc[e], czp[e]), part[h]);
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float v = row_allreduce<LPR>(fmaf(av, qbl[h], fmaf(scv, part[h], zpv * qs[h])));
-            if (colq == 0) s_sc[tok * G + h] = v;
+            for (int h = 0; h < G; ++h) {
+                const float v = row_allreduce<LPR>(fmaf(av, qbl[h], part[h]));
+                if (colq == 0) s_sc[tok * G + h] = v;
+            }
+        } else {
+            const float scv = s_gs[gidx0 + s * gstep], zpv = s_gz[gidx0 + s * gstep];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], cf[e], part[h]);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float v = row_allreduce<LPR>(fmaf(av, qbl[h], fmaf(scv, part[h], zpv * qs[h])));
+                if (colq == 0) s_sc[tok * G + h] = v;
+            }
         }
     }
     // K's CSR entries into LDS
@@ -866,7 +932,7 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     for (int s = 0; s < SPW; ++s)
         wvv[s] = BITS == 4 ? ld_at<uint32_t>(cvb, coff0 + s * RPS * ROWB)
                            : (uint32_t)ld_at<uint16_t>(cvb, coff0 + s * RPS * ROWB);
-    const Side sv = load_side(mrv);
+    const Side sv = load_side(mrv, true);
     __syncthreads();
 
     // ---------------- sparse part (one thread per token, waves 0..3), softmax
@@ -1023,7 +1089,8 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
             if (!VTILE && kVsRows == 8) sp += (vs[4 * RS] + vs[5 * RS]) + (vs[6 * RS] + vs[7 * RS]);
             float dn = 0.0f;
             for (int w = 0; w < nrows; ++w) dn += rows[(w * G + h) * D + j];
-            part[h * (D + 2) + j] = dn + lr + sp;
+            const float fv = QK == 2 ? p.chan[(size_t)pc.mv * D + j] : 1.0f;   // ZipCache value factor
+            part[h * (D + 2) + j] = (dn + lr + sp) * fv;
         }
     };
     if constexpr (G == 1) {
@@ -1090,10 +1157,16 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
         Timed t(kKAttnSplit, st);
         if (a.split0 > 0) {
             const dim3 grid((unsigned)a.split0, (unsigned)a.Hkv, (unsigned)a.B);
-            if (a.prompt.p.bits == 4)
-                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4>), grid, dim3(kFastThreads), 0, st, a);
-            else
-                hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2>), grid, dim3(kFastThreads), 0, st, a);
+            const int qk = a.prompt.p.chan ? 2 : a.prompt.p.ch_mats > 0 ? 1 : 0;
+            if (a.prompt.p.bits == 4) {
+                if (qk == 0) hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4, 0>), grid, dim3(kFastThreads), 0, st, a);
+                else if (qk == 1) hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4, 1>), grid, dim3(kFastThreads), 0, st, a);
+                else hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4, 2>), grid, dim3(kFastThreads), 0, st, a);
+            } else {
+                if (qk == 0) hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2, 0>), grid, dim3(kFastThreads), 0, st, a);
+                else if (qk == 1) hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2, 1>), grid, dim3(kFastThreads), 0, st, a);
+                else hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2, 2>), grid, dim3(kFastThreads), 0, st, a);
+            }
         }
         if (a.splits > a.split0)
             hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(pairs * (a.splits - a.split0)), dim3(kThreads),

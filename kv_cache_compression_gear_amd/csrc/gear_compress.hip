@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
-    const int64_t mm = group_id_x();
+    const int64_t mm = a.m0 + group_id_x();
     const int rows = o.rows;
     const uint32_t kk = (uint32_t)o.k;
     uint32_t* sel = a.sel + (size_t)mm * kSelStride;
@@ -739,8 +739,10 @@ __device__ __forceinline__ uint32_t wave_max_key(const uint4 (&xr)[SS]) {
 __device__ __forceinline__ float pow2f(int e) { return __builtin_bit_cast(float, (uint32_t)(127 + e) << 23); }
 
 // GL: lanes per quantization group when fixed at compile time (D/8: a group
-// is a whole token row), 0 for the group size of the call.
-template <int D, int RK, int GL>
+// is a whole token row), 0 for the group size of the call.  CH: keys quantized
+// per channel (groups of out.group tokens; their scales and zeros already in
+// the packed buffer, [rows / group][D]); the matrices have no outliers then.
+template <int D, int RK, int GL, bool CH = false>
 __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressArgs a) {
     constexpr int LPR = D / 8;              // lanes per token row
     constexpr int RPS = 64 / LPR;           // rows per wave per step
@@ -765,11 +767,11 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const Packed& o = a.out;
-    const int64_t mm = group_id_x();
+    const int64_t mm = a.m0 + group_id_x();
     const int rows = o.rows;
     const int bits = o.bits;
     const int gl = GL > 0 ? GL : o.group / 8, ngr = D / (8 * gl);
-    const uint32_t kk = (uint32_t)o.k;
+    const uint32_t kk = CH ? 0u : (uint32_t)o.k;
     const float qmax = (float)((1 << bits) - 1);
     // 1/qmax rounded to nearest: with one fma correction the quotient
     // y / qmax is correctly rounded for every fp32 y (checked exhaustively
@@ -832,6 +834,18 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
         for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
     uint32_t ties_seen = 0;
 
+    // per-channel parameters (CH) of the group the wave's slab slice lies in
+    // (its 8 rows are in one group: groups are multiples of 16 tokens)
+    const float* chs = o.scale + (size_t)mm * (CH ? rows / o.group : 0) * D + colq * 8;
+    const float* chz = o.zero + (size_t)mm * (CH ? rows / o.group : 0) * D + colq * 8;
+    auto load_chp = [&](float (&cs)[8], float (&cz)[8], int sl) {
+        const int row = min(wr0 + sl * kWaveSlab, rows - 1);
+        const uint32_t off = (uint32_t)(row / o.group) * D * 4;
+        const float4 s0 = ld_at<float4>(chs, off), s1 = ld_at<float4>(chs, off + 16);
+        const float4 z0 = ld_at<float4>(chz, off), z1 = ld_at<float4>(chz, off + 16);
+        cs[0] = s0.x, cs[1] = s0.y, cs[2] = s0.z, cs[3] = s0.w, cs[4] = s1.x, cs[5] = s1.y, cs[6] = s1.z, cs[7] = s1.w;
+        cz[0] = z0.x, cz[1] = z0.y, cz[2] = z0.z, cz[3] = z0.w, cz[4] = z1.x, cz[5] = z1.y, cz[6] = z1.z, cz[7] = z1.w;
+    };
     auto load_slab = [&](uint4 (&xr)[SS], int sl) {
 #pragma unroll
         for (int u = 0; u < SS; ++u) {
@@ -845,6 +859,8 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
 
     auto do_slab = [&](const uint4 (&xr)[SS], const uint4 (&xn)[SS], int sl) {
         unsigned char* slab = s_big + (sl & 1) * 2 * kPlane;
+        float chsc[8], chzp[8];
+        if constexpr (CH) load_chp(chsc, chzp, sl);
         if (slab_ex) {   // wave-uniform
             const uint4 e0 = *reinterpret_cast<const uint4*>(&s_ex[sl & 1][0]);
             const uint4 e1 = *reinterpret_cast<const uint4*>(&s_ex[sl & 1][4]);
@@ -977,17 +993,42 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             // are taken on the fp16 values (exact), then scaled.
             const h2v a0 = __builtin_bit_cast(h2v, dm[u][0]), a1 = __builtin_bit_cast(h2v, dm[u][1]);
             const h2v a2 = __builtin_bit_cast(h2v, dm[u][2]), a3 = __builtin_bit_cast(h2v, dm[u][3]);
+            const h2v hv[4] = {a0, a1, a2, a3};
+            float t[8], cf[8], R[8];
+            float mn = 0.0f, sc = 0.0f;
+            if constexpr (CH) {
+                // the column's group minimum and scale, in units of 2^ex; the
+                // same rounding and near-tie rule per column
+                bool near_tie = false;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sce = chsc[e] * sx;
+                    const float inv = fminf(__builtin_amdgcn_rcpf(sce), 3.4028234664e38f);
+                    t[e] = fmaf((float)hv[e >> 1][e & 1], sx, -(chzp[e] * sx));
+                    cf[e] = rintf(t[e] * inv);
+                    R[e] = fmaf(-cf[e], sce, t[e]);
+                    near_tie |= fabsf(R[e]) > 0.49999f * sce;
+                }
+                if (near_tie) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float sce = chsc[e] * sx;
+                        cf[e] = sce > 0.0f ? rintf(t[e] / sce) : 0.0f;
+                        R[e] = fmaf(-cf[e], sce, t[e]);
+                    }
+                }
+            } else {
             const h2v n2 = __builtin_elementwise_min(__builtin_elementwise_min(a0, a1),
                                                      __builtin_elementwise_min(a2, a3));
             const h2v x2 = __builtin_elementwise_max(__builtin_elementwise_max(a0, a1),
                                                      __builtin_elementwise_max(a2, a3));
-            float mn = (float)__builtin_elementwise_min(n2[0], n2[1]) * sx;
+            mn = (float)__builtin_elementwise_min(n2[0], n2[1]) * sx;
             float mx = (float)__builtin_elementwise_max(x2[0], x2[1]) * sx;
             group_minmax<GL>(mn, mx, gl);
             const float y = mx - mn;
             const float q0 = y * rq;
             // RN(y / qmax); y = +0 gives +0 (every term is +0 or a +0 - 0 sum)
-            const float sc = fmaf(fmaf(-q0, qmax, y), rq, q0);
+            sc = fmaf(fmaf(-q0, qmax, y), rq, q0);
             // a finite reciprocal also for sc = 0 (then every t is 0 and its
             // code 0); for a tiny sc the near-tie test below sends the group
             // to the exact division
@@ -996,8 +1037,6 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             // rint can differ from it only when t / sc is within 1e-5 of a
             // half-integer, that is when |R| > 0.49999 sc
             const float hs = 0.49999f * sc;
-            const h2v hv[4] = {a0, a1, a2, a3};
-            float t[8], cf[8], R[8];
             bool near_tie = false;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1013,6 +1052,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                     cf[e] = rintf(t[e] / sc);
                     R[e] = fmaf(-cf[e], sc, t[e]);
                 }
+            }
             }
             // 0 <= t <= mx - mn, so rint(t / sc) already lies in [0, 2^b - 1]
             uint32_t word = 0;
@@ -1035,10 +1075,12 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 const uint32_t co = valid ? urow * (D / 4) + colq * 2 : kDrop;
                 __builtin_amdgcn_raw_buffer_store_b16((uint16_t)word, codes_r, (int)co, 0, 0);
             }
-            const uint32_t go = (valid && (colq % gl) == 0) ? (urow * ngr + colq / gl) * 4 : kDrop;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc * rsx), scale_r, (int)go, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, (mn + 0.0f) * rsx), zero_r,
-                                                  (int)go, 0, 0);
+            if (!CH) {   // per-channel parameters were written before this kernel
+                const uint32_t go = (valid && (colq % gl) == 0) ? (urow * ngr + colq / gl) * 4 : kDrop;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sc * rsx), scale_r, (int)go, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, (mn + 0.0f) * rsx), zero_r,
+                                                      (int)go, 0, 0);
+            }
             if (LR) {
                 // fp16 hi (toward zero) + lo of R * 2^ex, row-major into the slab
                 uint32_t hw[4], lw[4];
@@ -1251,7 +1293,7 @@ __device__ __forceinline__ float ubyte_f(uint32_t x) {
 // BITS4: 4-bit codes (else 2-bit); ONEG: a lane's columns lie in one
 // quantization group.  Compile-time, so that each variant gets the registers
 // it needs on its own.
-template <int D, int RK, bool BITS4, bool ONEG>
+template <int D, int RK, bool BITS4, bool ONEG, bool CH = false>
 __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     constexpr int CPL = D / 4;                // columns per lane
     constexpr int NX = CPL / 8;               // 16-byte chunks of X per lane
@@ -1266,7 +1308,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     const int ngl = g >= CPL ? 1 : CPL / g;   // groups within a lane's columns (<= 4)
     const uint32_t kk = (uint32_t)o.k;
     const int nblk = (rows + ROWS_WG - 1) / ROWS_WG;
-    const int64_t mm = group_id_x() / nblk;
+    const int64_t mm = a.m0 + group_id_x() / nblk;
     const int blk = (int)(group_id_x() % nblk);
     const int r0 = blk * ROWS_WG + wv * ROWS_W;
     const int c0 = CPL * q;                   // first column of this lane
@@ -1284,6 +1326,22 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     constexpr bool VPATH = RK <= 4 && ONEG;
     float Bv[VPATH ? 1 : CPL];                // MFMA B operand: Bf[c0 + j][n = rr]
     __shared__ __attribute__((aligned(16))) float s_bm[VPATH ? D * 4 : 4];   // Bf rows, padded to 4
+    // CH: the per-channel scales and zeros of the token groups of this
+    // workgroup's rows (groups of at least 16 tokens: a 16-row step lies in one)
+    constexpr int kChG = CH ? ROWS_WG / 16 : 1;
+    __shared__ __attribute__((aligned(16))) float s_cs[kChG * D];
+    __shared__ __attribute__((aligned(16))) float s_cz[kChG * D];
+    const int cg0 = CH ? blk * ROWS_WG / o.group : 0;
+    if constexpr (CH) {
+        const int cg1 = (min(blk * ROWS_WG + ROWS_WG, rows) - 1) / o.group;
+        const float* cs = o.scale + (size_t)mm * (rows / o.group) * D;
+        const float* cz = o.zero + (size_t)mm * (rows / o.group) * D;
+        for (int i = tid; i < (cg1 - cg0 + 1) * D; i += kThreads) {
+            s_cs[i] = cs[(size_t)cg0 * D + i];
+            s_cz[i] = cz[(size_t)cg0 * D + i];
+        }
+        if (!VPATH) __syncthreads();   // the VALU path has a barrier of its own below
+    }
     if constexpr (VPATH) {
         if (tid < D) {
             const float* src = a.bf + ((size_t)mm * D + tid) * RK;
@@ -1362,7 +1420,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
         for (int t = 0; t < 4; ++t) {
             bf.sc[t] = 0.0f;
             bf.zp[t] = 0.0f;
-            if (t < ngl) {
+            if (!CH && t < ngl) {
                 const uint32_t go = (rc * ngr + (c0 + t * g) / g) * 4;
                 bf.sc[t] = ld_at<float>(scb, go);
                 bf.zp[t] = ld_at<float>(zpb, go);
@@ -1421,11 +1479,26 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) cf[e] = (float)((w >> (2 * e)) & 3u);
             }
+            float chs8[8], chz8[8];
+            if constexpr (CH) {   // columns c0 + 8 c .. + 7 of this step's token group
+                const int gi = (r0 + s * 16) / o.group - cg0;
+                const float* ps = s_cs + gi * D + c0 + 8 * c;
+                const float* pz = s_cz + gi * D + c0 + 8 * c;
+                const float4 s0 = *reinterpret_cast<const float4*>(ps), s1 = *reinterpret_cast<const float4*>(ps + 4);
+                const float4 z0 = *reinterpret_cast<const float4*>(pz), z1 = *reinterpret_cast<const float4*>(pz + 4);
+                chs8[0] = s0.x, chs8[1] = s0.y, chs8[2] = s0.z, chs8[3] = s0.w;
+                chs8[4] = s1.x, chs8[5] = s1.y, chs8[6] = s1.z, chs8[7] = s1.w;
+                chz8[0] = z0.x, chz8[1] = z0.y, chz8[2] = z0.z, chz8[3] = z0.w;
+                chz8[4] = z1.x, chz8[5] = z1.y, chz8[6] = z1.z, chz8[7] = z1.w;
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int jj = 8 * c + e;
                 float scv = bf.sc[0], zpv = bf.zp[0];
-                if (!ONEG) {   // groups of 8 or 16 columns: group of column jj
+                if (CH) {
+                    scv = chs8[e];
+                    zpv = chz8[e];
+                } else if (!ONEG) {   // groups of 8 or 16 columns: group of column jj
                     const int t = jj / (g == 8 ? 8 : 16);
                     scv = t == 0 ? bf.sc[0] : t == 1 ? bf.sc[1] : t == 2 ? bf.sc[2] : bf.sc[3];
                     zpv = t == 0 ? bf.zp[0] : t == 1 ? bf.zp[1] : t == 2 ? bf.zp[2] : bf.zp[3];
@@ -1493,6 +1566,137 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     else run(BoolTag<false>{});
 }
 
+// ---------------------------------------------------------------------------
+// KIVI keys: scale and zero per channel for each group of `group` tokens of a
+// matrix without outliers -- min and max of the group's entries in the
+// column, scale = RN((max - min) / (2^b - 1)), zero = min (both +0 when zero),
+// as the per-token groups take them.  One workgroup per (matrix, group): 16
+// row slots of D/8 lanes, 8 columns per lane, then the slots' results merged.
+template <int D>
+__global__ void __launch_bounds__(kThreads) channel_params_kernel(CompressArgs a) {
+    constexpr int LPR = D / 8, SLOTS = kThreads / LPR;
+    __shared__ float s_mn[SLOTS * D];
+    __shared__ float s_mx[SLOTS * D];
+    const Packed& o = a.out;
+    const int tid = thread_id(), colq = tid % LPR, slot = tid / LPR;
+    const int g = o.group, ngroups = o.rows / g;
+    const int64_t mm = a.m0 + group_id_x() / ngroups;
+    const int gi = (int)(group_id_x() % ngroups);
+    const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * o.rows * D
+                                        : a.x2 + (size_t)(mm - a.m_split) * o.rows * D;
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    h2 mn[4], mx[4];
+    const bool any = slot < g;   // the slot has at least one row of the group
+    for (int row = gi * g + slot; row < (gi + 1) * g; row += SLOTS) {
+        const uint4 w = *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8);
+        const uint32_t wv4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const h2 v = __builtin_bit_cast(h2, wv4[i]);
+            if (row == gi * g + slot) {
+                mn[i] = v;
+                mx[i] = v;
+            } else {
+                mn[i] = __builtin_elementwise_min(mn[i], v);
+                mx[i] = __builtin_elementwise_max(mx[i], v);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        s_mn[slot * D + colq * 8 + e] = any ? (float)mn[e >> 1][e & 1] : INFINITY;
+        s_mx[slot * D + colq * 8 + e] = any ? (float)mx[e >> 1][e & 1] : -INFINITY;
+    }
+    __syncthreads();
+    if (tid < D) {
+        float lo = s_mn[tid], hi = s_mx[tid];
+        for (int q = 1; q < SLOTS; ++q) {
+            lo = fminf(lo, s_mn[q * D + tid]);
+            hi = fmaxf(hi, s_mx[q * D + tid]);
+        }
+        const float qmax = (float)((1 << o.bits) - 1);
+        const float rq = o.bits == 4 ? 0x1.111112p-4f : 0x1.555556p-2f;
+        const float y = hi - lo;
+        const float q0 = y * rq;
+        const float sc = fmaf(fmaf(-q0, qmax, y), rq, q0);   // RN(y / qmax)
+        const size_t at = ((size_t)mm * ngroups + gi) * D + tid;
+        o.scale[at] = sc + 0.0f;
+        o.zero[at] = lo + 0.0f;
+    }
+}
+
+// ZipCache: per compressed matrix, the channel factors 2^e_j (the smallest
+// power of two not below the column's largest |x|; 1 for an all-zero
+// column), one workgroup per matrix.
+template <int D>
+__global__ void __launch_bounds__(kThreads) channel_exponent_kernel(CompressArgs a) {
+    constexpr int LPR = D / 8, SLOTS = kThreads / LPR;
+    __shared__ uint32_t s_key[SLOTS * D];
+    const Packed& o = a.out;
+    const int tid = thread_id(), colq = tid % LPR, slot = tid / LPR;
+    const int64_t mm = a.m0 + group_id_x();
+    const uint16_t* xm = mm < a.m_split ? a.x + (size_t)mm * o.rows * D
+                                        : a.x2 + (size_t)(mm - a.m_split) * o.rows * D;
+    typedef unsigned short u2 __attribute__((ext_vector_type(2)));
+    u2 m[4] = {{0, 0}, {0, 0}, {0, 0}, {0, 0}};
+    for (int row = slot; row < o.rows; row += SLOTS) {
+        const uint4 w = *reinterpret_cast<const uint4*>(xm + (size_t)row * D + colq * 8);
+        const uint32_t wv4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            m[i] = __builtin_elementwise_max(m[i], __builtin_bit_cast(u2, wv4[i] & 0x7fff7fffu));
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_key[slot * D + colq * 8 + e] = m[e >> 1][e & 1];
+    __syncthreads();
+    if (tid < D) {
+        uint32_t key = 0;
+        for (int q = 0; q < SLOTS; ++q) key = max(key, s_key[q * D + tid]);
+        int k = 0;
+        if (key != 0) {
+            int ex;
+            const float f = frexpf((float)__builtin_bit_cast(_Float16, (uint16_t)key), &ex);
+            k = f == 0.5f ? ex - 1 : ex;
+        }
+        o.chan[(size_t)mm * D + tid] = __builtin_bit_cast(float, (uint32_t)(127 + k) << 23);
+    }
+}
+
+// ZipCache: xt = fl16(x / factor_j), 8 values per thread, grid-stride.
+template <int D>
+__global__ void __launch_bounds__(kThreads) channel_normalize_kernel(CompressArgs a, uint16_t* xt,
+                                                                     int nblocks) {
+    const Packed& o = a.out;
+    constexpr int LPR = D / 8;
+    const size_t per_mat = (size_t)o.rows * LPR;
+    const size_t total = (size_t)(a.m1 - a.m0) * per_mat;
+    for (size_t i = (size_t)group_id_x() * kThreads + thread_id(); i < total;
+         i += (size_t)nblocks * kThreads) {
+        const int64_t mm = a.m0 + (int64_t)(i / per_mat);
+        const size_t rem = i % per_mat;
+        const int colq = (int)(rem % LPR);
+        const uint16_t* src = (mm < a.m_split ? a.x + (size_t)mm * o.rows * D
+                                              : a.x2 + (size_t)(mm - a.m_split) * o.rows * D) + rem * 8;
+        const uint4 w = *reinterpret_cast<const uint4*>(src);
+        const float4 f0 = *reinterpret_cast<const float4*>(o.chan + (size_t)mm * D + colq * 8);
+        const float4 f1 = *reinterpret_cast<const float4*>(o.chan + (size_t)mm * D + colq * 8 + 4);
+        // 1 / 2^e, exact
+        const float fi[8] = {1.0f / f0.x, 1.0f / f0.y, 1.0f / f0.z, 1.0f / f0.w,
+                             1.0f / f1.x, 1.0f / f1.y, 1.0f / f1.z, 1.0f / f1.w};
+        const uint32_t wi[4] = {w.x, w.y, w.z, w.w};
+        uint32_t wo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = h2f(wi[q] & 0xffffu) * fi[2 * q];        // exact in fp32
+            const float hi = h2f(wi[q] >> 16) * fi[2 * q + 1];
+            // one rounding to fp16, to nearest even
+            wo[q] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+        }
+        *reinterpret_cast<uint4*>(xt + (size_t)mm * o.rows * D + rem * 8) = make_uint4(wo[0], wo[1], wo[2], wo[3]);
+    }
+}
+
 // Compute units of the current device, cached per device.
 int cu_count() {
     static std::atomic<int> cached[64];
@@ -1511,7 +1715,30 @@ constexpr int lowrank_rows_per_wg() { return 4 * 16 * kLrSteps; }
 
 template <int D, int RK>
 hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
-    const unsigned M = (unsigned)a.out.M;
+    const unsigned M = (unsigned)(a.m1 - a.m0);
+    if (a.chan_q) {   // KIVI keys (no outliers): the per-channel path
+        hipError_t e;
+        {
+            Timed t(kKCompress, st);
+            hipLaunchKernelGGL((compress_kernel<D, RK, D / 8, true>), dim3(M), dim3(kCompressThreads), 0, st, a);
+            e = hipGetLastError();
+        }
+        if constexpr (RK > 0) {
+            if (e != hipSuccess) return e;
+            constexpr int RPW = lowrank_rows_per_wg<D>();
+            const int64_t blocks = (int64_t)M * ((a.out.rows + RPW - 1) / RPW);
+            if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+            Timed t(kKLowrankA, st);
+            if (a.out.bits == 4)
+                hipLaunchKernelGGL((lowrank_a_kernel<D, RK, true, true, true>), dim3((unsigned)blocks),
+                                   dim3(kThreads), 0, st, a);
+            else
+                hipLaunchKernelGGL((lowrank_a_kernel<D, RK, false, true, true>), dim3((unsigned)blocks),
+                                   dim3(kThreads), 0, st, a);
+            e = hipGetLastError();
+        }
+        return e;
+    }
     if (a.out.k > 0) {   // without outliers the compress kernel bounds R itself
         Timed t(kKSelect, st);
         // 16 waves per matrix when the matrices are too few to give every CU
@@ -1536,7 +1763,7 @@ hipError_t launch_d_rk(const CompressArgs& a, hipStream_t st) {
     if constexpr (RK > 0) {
         if (e != hipSuccess) return e;
         constexpr int RPW = lowrank_rows_per_wg<D>();
-        const int64_t blocks = a.out.M * ((a.out.rows + RPW - 1) / RPW);
+        const int64_t blocks = (int64_t)M * ((a.out.rows + RPW - 1) / RPW);
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
         Timed t(kKLowrankA, st);
         const bool one_group = a.out.group >= D / 4;   // a lane's D/4 columns in one group
@@ -1572,12 +1799,51 @@ size_t compress_workspace(int64_t M, int d, int rank) {
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st) {
-    if (a.out.M <= 0) return hipSuccess;
-    if (a.out.M > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.m1 <= a.m0) return hipSuccess;
+    if (a.m1 - a.m0 > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.out.rank > 0 && (a.out.rows < 1 || a.iters < 1)) return hipErrorInvalidValue;
+    if (a.chan_q && (a.out.k != 0 || a.out.group < 16 || a.out.rows % a.out.group != 0))
+        return hipErrorInvalidValue;
     if (a.out.d == 64) return launch_d<64>(a, st);
     if (a.out.d == 128) return launch_d<128>(a, st);
     return hipErrorInvalidValue;
 }
+
+hipError_t launch_channel_params(const CompressArgs& a, hipStream_t st) {
+    if (a.m1 <= a.m0) return hipSuccess;
+    if (a.out.group < 16 || a.out.rows % a.out.group != 0) return hipErrorInvalidValue;
+    const int64_t blocks = (a.m1 - a.m0) * (a.out.rows / a.out.group);
+    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+    Timed t(kKChannel, st);
+    if (a.out.d == 64)
+        hipLaunchKernelGGL((channel_params_kernel<64>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    else if (a.out.d == 128)
+        hipLaunchKernelGGL((channel_params_kernel<128>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_channel_normalize(const CompressArgs& a, uint16_t* xt, hipStream_t st) {
+    if (a.m1 <= a.m0) return hipSuccess;
+    if (a.m1 - a.m0 > 0x7fffffffLL || !a.out.chan) return hipErrorInvalidValue;
+    const size_t total = (size_t)(a.m1 - a.m0) * a.out.rows * (a.out.d / 8);
+    size_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 8192) blocks = 8192;
+    Timed t(kKChannel, st);
+    if (a.out.d == 64) {
+        hipLaunchKernelGGL((channel_exponent_kernel<64>), dim3((unsigned)(a.m1 - a.m0)), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((channel_normalize_kernel<64>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a,
+                           xt, (int)blocks);
+    } else if (a.out.d == 128) {
+        hipLaunchKernelGGL((channel_exponent_kernel<128>), dim3((unsigned)(a.m1 - a.m0)), dim3(kThreads), 0, st, a);
+        hipLaunchKernelGGL((channel_normalize_kernel<128>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a,
+                           xt, (int)blocks);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 
 }  // namespace gear

@@ -1,5 +1,6 @@
 // gear_decompress.hip -- reconstruction X^ = deq(Q) + A B^T + S of packed GEAR
-// matrices ("GEAR: Efficient KV Cache Compression for LLM Inference", Q3: the
+// matrices, for the three quantization backbones (GEAR's own, KIVI keys per
+// channel, ZipCache's channel factors) ("GEAR: Efficient KV Cache Compression for LLM Inference", Q3: the
 // quantized backbone, the low-rank part and the sparse part add up; app.cochat.ai
 // "Cites" list, sentence quoted under the Zafrir et al. entry: low-rank for the
 // coherent error, sparse for the outliers).
@@ -41,8 +42,12 @@ __device__ __forceinline__ float ubyte_f(uint32_t x) {
     return f;
 }
 
-template <int D, int RK>
-__global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t* out) {
+// QM: how the codes were quantized.  0: groups of head_dim columns of a token
+// (GEAR's own); 1: groups of p.group tokens of a channel (KIVI keys; scale and
+// zero [rows / group][D]); 2: as 0, on a matrix whose channels were divided
+// by the factors p.chan (ZipCache), multiplied back here.
+template <int D, int RK, int QM>
+__global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t* out, int64_t m0) {
     constexpr int kSteps = steps_for(RK);
     constexpr int LPR = D / 8, RPS = 64 / LPR;
     constexpr int ROWS_STEP = 4 * RPS;
@@ -54,12 +59,16 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     __shared__ __attribute__((aligned(16))) uint16_t s_s[ROWS_WG * D];
     __shared__ int32_t s_rp[ROWS_WG + 1];
     __shared__ uint32_t s_cv[kCsrCap];   // column | fp16 value << 16
+    // per-channel scale and zero of the block's token groups (QM 1)
+    constexpr int kChG = QM == 1 ? ROWS_WG / 16 : 1;
+    __shared__ __attribute__((aligned(16))) float s_cs[kChG * D];
+    __shared__ __attribute__((aligned(16))) float s_cz[kChG * D];
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
     const int rows = p.rows;
     const int blocks_per_mat = (rows + ROWS_WG - 1) / ROWS_WG;
-    const int64_t mm = group_id_x() / blocks_per_mat;
+    const int64_t mm = m0 + group_id_x() / blocks_per_mat;
     const int row0 = (int)(group_id_x() % blocks_per_mat) * ROWS_WG;
     const int nrows = min(ROWS_WG, rows - row0);
     const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
@@ -79,9 +88,11 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         const uint32_t tk = (uint32_t)min(lr, nrows - 1);
         word[s] = bits == 4 ? ld_at<uint32_t>(cbase, tk * (D / 2) + colq * 4)
                             : (uint32_t)ld_at<uint16_t>(cbase, tk * (D / 4) + colq * 2);
-        const uint32_t go = (tk * ngr + colq / gl) * 4;
-        sc[s] = ld_at<float>(sbase, go);
-        zp[s] = ld_at<float>(zbase, go);
+        if (QM != 1) {
+            const uint32_t go = (tk * ngr + colq / gl) * 4;
+            sc[s] = ld_at<float>(sbase, go);
+            zp[s] = ld_at<float>(zbase, go);
+        }
         if (RK > 0 && r == RK) {            // the A row as one or two vector loads
             if (RK >= 4) {
 #pragma unroll
@@ -141,6 +152,18 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         }
     if (tid <= nrows) s_rp[tid] = min(max(rpv0, 0), p.k);
     if (tid + kThreads <= nrows) s_rp[tid + kThreads] = min(max(rpv1, 0), p.k);
+    if constexpr (QM == 1) {
+        // the groups the block's rows fall in (group >= 16 tokens, the block
+        // starts at a multiple of 16): group gi of the block at s_cs[gi * D]
+        const int g = p.group;
+        const int gfirst = row0 / g, glast = (row0 + nrows - 1) / g;
+        const float* cs = p.scale + (size_t)mm * (rows / g) * D;
+        const float* cz = p.zero + (size_t)mm * (rows / g) * D;
+        for (int i = tid; i < (glast - gfirst + 1) * D; i += kThreads) {
+            s_cs[i] = cs[(size_t)gfirst * D + i];
+            s_cz[i] = cz[(size_t)gfirst * D + i];
+        }
+    }
     __syncthreads();
     // the block's CSR entries: one contiguous range, from the guessed window
     // when it covers the range, else loaded again (coalesced)
@@ -183,6 +206,13 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     float Bm[8][RKX];
     float one = 1.0f;   // opaque 1: keeps the outlier add a single mixed fma
     asm volatile("" : "+s"(one));
+    float cfac[8];      // QM 2: the channel factors of the lane's columns
+    if constexpr (QM == 2) {
+        const float4 f0 = *reinterpret_cast<const float4*>(p.chan + (size_t)mm * D + colq * 8);
+        const float4 f1 = *reinterpret_cast<const float4*>(p.chan + (size_t)mm * D + colq * 8 + 4);
+        cfac[0] = f0.x, cfac[1] = f0.y, cfac[2] = f0.z, cfac[3] = f0.w;
+        cfac[4] = f1.x, cfac[5] = f1.y, cfac[6] = f1.z, cfac[7] = f1.w;
+    }
     __syncthreads();
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -206,13 +236,26 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
             for (int e = 0; e < 8; ++e) cf[e] = (float)((word[s] >> (2 * e)) & 3u);
         }
         float x[8];
+        float csc[8], czp[8];   // QM 1: this row's group, the lane's columns
+        if constexpr (QM == 1) {
+            const int gi = (row0 + min(lr, nrows - 1)) / p.group - row0 / p.group;
+            const float4 s0 = *reinterpret_cast<const float4*>(s_cs + gi * D + colq * 8);
+            const float4 s1 = *reinterpret_cast<const float4*>(s_cs + gi * D + colq * 8 + 4);
+            const float4 z0 = *reinterpret_cast<const float4*>(s_cz + gi * D + colq * 8);
+            const float4 z1 = *reinterpret_cast<const float4*>(s_cz + gi * D + colq * 8 + 4);
+            csc[0] = s0.x, csc[1] = s0.y, csc[2] = s0.z, csc[3] = s0.w;
+            csc[4] = s1.x, csc[5] = s1.y, csc[6] = s1.z, csc[7] = s1.w;
+            czp[0] = z0.x, czp[1] = z0.y, czp[2] = z0.z, czp[3] = z0.w;
+            czp[4] = z1.x, czp[5] = z1.y, czp[6] = z1.z, czp[7] = z1.w;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float v = fmaf(cf[e], sc[s], zp[s]);
+            float v = QM == 1 ? fmaf(cf[e], csc[e], czp[e]) : fmaf(cf[e], sc[s], zp[s]);
 #pragma unroll
             for (int c = 0; c < RKX; ++c) v = fmaf(ar[s][c], Bm[e][c], v);
             // + the fp16 outlier value (fp16 operand of a mixed fma)
             x[e] = fmaf(h2f(sw[e >> 1] >> (16 * (e & 1))), one, v);
+            if (QM == 2) x[e] *= cfac[e];   // a power of two: exact
         }
         if (lr < nrows) {
             u32x4 o;
@@ -225,15 +268,25 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     }
 }
 
-template <int D, int RK>
-hipError_t launch_dr(const Packed& p, uint16_t* out, hipStream_t st) {
+template <int D, int RK, int QM>
+hipError_t launch_drq(const Packed& p, uint16_t* out, int64_t m0, int64_t m1, hipStream_t st) {
     constexpr int ROWS_WG = steps_for(RK) * 4 * (64 / (D / 8));
-    const int64_t blocks = p.M * ((p.rows + ROWS_WG - 1) / ROWS_WG);
+    const int64_t blocks = (m1 - m0) * ((p.rows + ROWS_WG - 1) / ROWS_WG);
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     Timed t(kKDecompress, st);
-    hipLaunchKernelGGL((decompress_kernel<D, RK>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p, out);
+    hipLaunchKernelGGL((decompress_kernel<D, RK, QM>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
+                       out, m0);
     return hipGetLastError();
+}
+
+template <int D, int RK>
+hipError_t launch_dr(const Packed& p, uint16_t* out, hipStream_t st) {
+    if (p.chan) return launch_drq<D, RK, 2>(p, out, 0, p.M, st);
+    hipError_t e = hipSuccess;
+    if (p.ch_mats > 0) e = launch_drq<D, RK, 1>(p, out, 0, p.ch_mats, st);
+    if (e == hipSuccess && p.ch_mats < p.M) e = launch_drq<D, RK, 0>(p, out, p.ch_mats, p.M, st);
+    return e;
 }
 
 template <int D>

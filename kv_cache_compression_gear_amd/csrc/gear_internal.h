@@ -76,7 +76,7 @@ __device__ __forceinline__ void st_at(void* base, uint32_t byte_off, T v) {
 // launch with HIP events on its stream while timing is on; a no-op otherwise.
 enum KernelId {
     kKSelect, kKCompress, kKLowrankA, kKDecompress, kKAttnSplit, kKAttnCombine,
-    kKBufferAppend, kKernelCount
+    kKBufferAppend, kKChannel, kKernelCount
 };
 bool timing_on();
 hipEvent_t timing_begin(hipStream_t st);                    // nullptr on failure
@@ -99,6 +99,8 @@ struct Packed {
     int64_t M;         // compressed matrices
     int32_t rows;      // tokens per compressed matrix
     int32_t d, bits, group, rank, k;
+    int64_t ch_mats;   // matrices [0, ch_mats) are quantized per channel (KIVI
+                       // keys: scale / zero [rows / group][d]); the rest per token
     uint8_t* codes;
     float* scale;
     float* zero;
@@ -107,6 +109,7 @@ struct Packed {
     uint16_t* val;     // fp16 bits
     float* A;
     float* B;
+    float* chan;       // ZipCache channel factors [M][d], else nullptr
 };
 
 // ---- compress -------------------------------------------------------------
@@ -114,6 +117,8 @@ struct CompressArgs {
     const uint16_t* x;     // matrices [0, m_split): [m][rows][d] fp16 bits
     const uint16_t* x2;    // matrices [m_split, M) (a second tensor)
     int64_t m_split;
+    int64_t m0, m1;        // this launch compresses matrices [m0, m1)
+    int32_t chan_q;        // 1: quantize per channel (groups of out.group tokens)
     Packed out;
     int32_t iters;
     uint64_t seed;
@@ -137,7 +142,14 @@ __host__ __device__ inline int wave_rows(int rows) {
     return ((rows + kCompressWaves - 1) / kCompressWaves + 7) / 8 * 8;
 }
 size_t compress_workspace(int64_t M, int d, int rank);
+// Compress matrices [a.m0, a.m1) of a.out.
 hipError_t launch_compress(const CompressArgs& a, hipStream_t st);
+// Per-channel scale and zero of matrices [a.m0, a.m1) (KIVI keys without
+// outliers): groups of out.group tokens of each channel.
+hipError_t launch_channel_params(const CompressArgs& a, hipStream_t st);
+// ZipCache: channel factors 2^e_j of every matrix into out.chan, then the
+// normalized stack fl16(x 2^-e_j) into xt ([M][rows][d], contiguous).
+hipError_t launch_channel_normalize(const CompressArgs& a, uint16_t* xt, hipStream_t st);
 
 // ---- decompress -----------------------------------------------------------
 hipError_t launch_decompress(const Packed& p, uint16_t* out, hipStream_t st);

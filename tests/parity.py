@@ -23,7 +23,13 @@ REL_TOL = 1e-3
 
 def to_orc_params(p) -> orc.Params:
     return orc.Params(bits=p.bits, group=p.group, outlier_ppm=p.outlier_ppm, rank=p.rank,
-                      power_iters=p.power_iters, chunk_tokens=p.chunk_tokens, seed=p.seed)
+                      power_iters=p.power_iters, chunk_tokens=p.chunk_tokens, seed=p.seed,
+                      quant=p.quant)
+
+
+def channel_keys(p, role: int) -> bool:
+    """Whether a matrix of this role is quantized per channel (KIVI keys)."""
+    return p.quant == orc.QUANT_KIVI and role == orc.ROLE_KEYS
 
 
 def unpack_codes(packed_rows: np.ndarray, d: int, bits: int) -> np.ndarray:
@@ -35,17 +41,20 @@ def unpack_codes(packed_rows: np.ndarray, d: int, bits: int) -> np.ndarray:
     return out
 
 
-def tie_quotients(x16: np.ndarray, ref: orc.Compressed, p) -> np.ndarray:
+def tie_quotients(x16: np.ndarray, ref: orc.Compressed, p, role: int = 0) -> np.ndarray:
     """fp64 distance of the oracle quotient to the nearest half-integer."""
     n, d = x16.shape
+    if p.quant == orc.QUANT_ZIPCACHE:   # the quotients are of the normalized matrix
+        x16 = orc.channel_normalize(x16, orc.channel_exponents(x16))
     xs = x16.view(np.float16).astype(np.float64)
     mask = np.zeros((n, d), bool)
     for t in range(n):
         for e in range(ref.row_ptr[t], ref.row_ptr[t + 1]):
             mask[t, ref.col[e]] = True
     D = np.where(mask, 0.0, xs)
-    sc = np.repeat(ref.scale.astype(np.float64), p.group, axis=1)
-    zr = np.repeat(ref.zero.astype(np.float64), p.group, axis=1)
+    axis = 0 if channel_keys(p, role) else 1
+    sc = np.repeat(ref.scale.astype(np.float64), p.group, axis=axis)
+    zr = np.repeat(ref.zero.astype(np.float64), p.group, axis=axis)
     with np.errstate(divide="ignore", invalid="ignore"):
         v = np.where(sc > 0, (D - zr) / sc, 0.0)
     return np.abs(v - np.floor(v) - 0.5)
@@ -64,8 +73,9 @@ class Report:
 
 
 def check_matrix(x16: np.ndarray, packed, m: int, ref: orc.Compressed, p, rep: Report,
-                 xhat_gpu: np.ndarray | None = None):
-    """Compare compressed matrix m of `packed` (GPU) with the oracle's `ref`."""
+                 xhat_gpu: np.ndarray | None = None, role: int = 0):
+    """Compare compressed matrix m of `packed` (GPU) with the oracle's `ref`
+    (role: what matrix m holds, keys or values)."""
     n, d = x16.shape
     k = packed.k
     # CSR of the outliers: exact
@@ -76,18 +86,21 @@ def check_matrix(x16: np.ndarray, packed, m: int, ref: orc.Compressed, p, rep: R
     val = packed.val()[m].cpu().view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(val, ref.val), f"outlier values differ (matrix {m})"
     assert k == len(ref.col)
-    # scale, zero: exact
-    assert np.array_equal(packed.scale()[m].cpu().numpy().view(np.uint32),
-                          ref.scale.view(np.uint32)), f"scale differs (matrix {m})"
-    assert np.array_equal(packed.zero()[m].cpu().numpy().view(np.uint32),
-                          ref.zero.view(np.uint32)), f"zero differs (matrix {m})"
+    # scale, zero: exact (the per-channel layout of KIVI keys holds as many)
+    assert np.array_equal(packed.scale()[m].cpu().numpy().reshape(-1).view(np.uint32),
+                          ref.scale.reshape(-1).view(np.uint32)), f"scale differs (matrix {m})"
+    assert np.array_equal(packed.zero()[m].cpu().numpy().reshape(-1).view(np.uint32),
+                          ref.zero.reshape(-1).view(np.uint32)), f"zero differs (matrix {m})"
+    if p.quant == orc.QUANT_ZIPCACHE:
+        assert np.array_equal(packed.chan()[m].cpu().numpy().view(np.uint32),
+                              ref.chan.view(np.uint32)), f"channel factors differ (matrix {m})"
     # codes: exact up to counted rounding-boundary ties
     gc = packed.codes()[m].cpu().numpy()
     if not np.array_equal(gc, ref.packed):
         cg = unpack_codes(gc, d, p.bits)
         co = unpack_codes(ref.packed, d, p.bits)
         bad = cg != co
-        dist = tie_quotients(x16, ref, p)
+        dist = tie_quotients(x16, ref, p, role)
         assert np.all(dist[bad] < 1e-5), f"code mismatch away from a rounding tie (matrix {m})"
         rep.ties += int(bad.sum())
     rep.entries += n * d

@@ -230,3 +230,54 @@ def test_noalloc_compress_rejects_more_than_its_static_scratch():
     assert b"static scratch" in lib.gear_last_error()
     assert lib.gear_compress_noalloc(ctypes.byref(p._c()), ctypes.byref(s), ctypes.c_void_p(0x10000008),
                                      fake, None) == 1
+
+
+def test_backbone_settings_checked_on_the_host():
+    """KIVI keys need no outliers, whole token groups of at least 16; ZipCache
+    quantizes tokenwise (group = head_dim) and adds a channel-factor section;
+    the reserved fields must be zero."""
+    lib = gear.lib()
+    K, V, KV = gear.ROLE_KEYS, gear.ROLE_VALUES, gear.ROLE_KEYS_THEN_VALUES
+
+    def st(p, M, n, d, role):
+        L = gear._Layout()
+        return lib.gear_packed_layout(ctypes.byref(p._c()), ctypes.byref(gear._shape(M, n, d, role)),
+                                      ctypes.byref(L)), L
+    kivi = gear.Params(2, 32, 0, 4, 2, quant=gear.QUANT_KIVI)
+    assert st(kivi, 4, 256, 128, K)[0] == 0
+    assert st(kivi, 4, 256, 128, KV)[0] == 0
+    assert st(kivi, 3, 256, 128, KV)[0] == 1                     # odd keys-then-values stack
+    assert st(gear.Params(2, 32, 20000, 4, 2, quant=gear.QUANT_KIVI), 4, 256, 128, K)[0] == 2
+    assert st(gear.Params(2, 32, 20000, 4, 2, quant=gear.QUANT_KIVI), 4, 256, 128, V)[0] == 0
+    assert st(kivi, 4, 240, 128, K)[0] == 1                      # 240 tokens: not whole groups
+    assert st(gear.Params(4, 8, 0, 2, 2, quant=gear.QUANT_KIVI), 4, 256, 64, K)[0] == 2
+    # same byte count for per-token and per-channel parameters
+    a = st(gear.Params(2, 32, 0, 4, 2), 4, 256, 128, K)[1]
+    b = st(kivi, 4, 256, 128, K)[1]
+    assert a.total_bytes == b.total_bytes and a.off_chan == b.off_chan
+    zc = gear.Params(4, 128, 20000, 4, 3, quant=gear.QUANT_ZIPCACHE)
+    s0, L = st(zc, 6, 512, 128, K)
+    assert s0 == 0 and L.total_bytes - L.off_chan == (6 * 128 * 4 + 255) // 256 * 256
+    assert st(gear.Params(4, 64, 20000, 4, 3, quant=gear.QUANT_ZIPCACHE), 6, 512, 128, K)[0] == 1
+    assert st(gear.Params(4, 128, 20000, 4, 3, quant=3), 6, 512, 128, K)[0] == 1
+    bad = gear.Params(4, 128, 20000, 4, 3)._c()
+    bad.reserved = 1
+    L = gear._Layout()
+    assert lib.gear_packed_layout(ctypes.byref(bad), ctypes.byref(gear._shape(2, 64, 128)), ctypes.byref(L)) == 1
+    # ZipCache's workspace holds a normalized copy of the stack
+    wz = lib.gear_compress_workspace_bytes(ctypes.byref(zc._c()), ctypes.byref(gear._shape(6, 512, 128)))
+    wg = lib.gear_compress_workspace_bytes(ctypes.byref(gear.Params(4, 128, 20000, 4, 3)._c()),
+                                           ctypes.byref(gear._shape(6, 512, 128)))
+    assert wz - wg >= 6 * 512 * 128 * 2
+
+
+def test_kivi_cache_buffer_holds_whole_key_groups():
+    lib = gear.lib()
+    pp = gear.Params(2, 32, 0, 4, 3, quant=gear.QUANT_KIVI)
+    fp = gear.Params(2, 32, 0, 2, 3, quant=gear.QUANT_KIVI)
+    ok = gear._CacheConfig(pp._c(), fp._c(), 2, 2, 128, 256, 64, 128)
+    assert lib.gear_cache_arena_bytes(ctypes.byref(ok)) > 0
+    bad = gear._CacheConfig(pp._c(), fp._c(), 2, 2, 128, 256, 48, 128)     # 48 = 1.5 groups
+    assert lib.gear_cache_arena_bytes(ctypes.byref(bad)) == 0
+    mixed = gear._CacheConfig(pp._c(), gear.Params(2, 32, 0, 2, 3)._c(), 2, 2, 128, 256, 64, 128)
+    assert lib.gear_cache_arena_bytes(ctypes.byref(mixed)) == 0
