@@ -39,6 +39,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import ctypes
 import hashlib
 import json
 import os
@@ -555,6 +556,137 @@ def _stream_decode(gear, WORKLOADS, torch):
     return rec
 
 
+# The memory/throughput study of the GEAR pages (app.cochat.ai, "Cites" list,
+# Method sentence quoted under the KIVI entry: the batch size is raised until
+# the memory runs out, and peak memory and throughput are compared between
+# FP16 KV caches and 2-bit KIVI, GEAR and GEAR-L), on one GPU and KV caches
+# only: a 7B-shaped model's 32 layers of 32 heads x 128, each layer a streaming
+# cache of this library; one decode step appends one token per sequence to
+# every layer and runs decode attention in every layer.  FP16 is a cache whose
+# fp16 buffer holds every token (no compression; the same attention kernels).
+SWEEP_CONFIGS = [
+    # name, bits, group, outlier_ppm, rank, power_iters, quant (None: fp16)
+    ("fp16", None, None, None, None, None, None),
+    ("gear_4bit", 4, 128, 20000, 4, 3, 0),
+    ("gear_l_4bit", 4, 128, 0, 4, 3, 0),
+    ("gear_2bit", 2, 64, 20000, 4, 3, 0),
+    ("gear_l_2bit", 2, 64, 0, 4, 3, 0),
+    ("kivi_2bit", 2, 64, 0, 0, 0, 1),
+    ("kivi_gear_l_2bit", 2, 64, 0, 4, 3, 1),
+]
+
+
+def _sweep(gear, torch, layers, heads, d, prompt, new, steps, warm):
+    """Largest batch each cache kind fits in free HBM (from the library's own
+    arena and workspace sizes, plus one layer's fp16 prompt while it is
+    compressed), decode throughput at doubling batch sizes up to it, peak
+    memory at each."""
+    pool_b = 4                      # distinct synthetic sequences, tiled over the batch
+    from kv_cache_compression_gear_amd.synth import KVSynth
+    syn = KVSynth(pool_b, heads, d, 4, seed=0, device="cuda")
+    kp, vp = syn.prompt(prompt)
+    steps_k = torch.stack([syn.step()[0] for _ in range(4)])   # [4, pool_b, H, d]
+    steps_v = torch.stack([syn.step()[1] for _ in range(4)])
+    qpool = syn.queries(heads)
+    torch.cuda.synchronize()
+    out = {}
+    for name, bits, group, ppm, rank, iters, quant in SWEEP_CONFIGS:
+        if bits is None:   # fp16: everything stays in the buffer
+            pp = fp = gear.Params(4, 128, 0, 0, 0)
+            n_prompt, buf, max_new = 0, prompt + new + 1, prompt + new
+        else:
+            pp = gear.Params(bits, group, ppm, rank, iters, quant=quant)
+            fp = gear.Params(bits, group, ppm, min(rank, 2), iters, quant=quant)
+            n_prompt, buf, max_new = prompt, 64, new
+
+        def per_seq(B):
+            c = gear._CacheConfig(pp._c(), fp._c(), B, heads, d, n_prompt, buf, max_new)
+            return (gear.lib().gear_cache_arena_bytes(ctypes.byref(c)),
+                    gear.lib().gear_cache_workspace_bytes(ctypes.byref(c), heads))
+        a64, w64 = per_seq(64)
+        # per sequence: every layer's arena and workspace, and the fp16 prompt
+        # (K and V) the layers are loaded from
+        seq_bytes = layers * (a64 + w64) / 64 + 2 * heads * prompt * d * 2
+        torch.cuda.empty_cache()
+        free, total = torch.cuda.mem_get_info()
+        bmax = int((free * 0.92 - (2 << 30)) // seq_bytes)
+        batches = sorted({b for b in (8, 16, 32, 64, 128, 256, 512, 1024) if b < bmax} | {bmax})
+        rec = {"cache_bytes_per_sequence": round(layers * a64 / 64), "max_batch": bmax, "runs": []}
+        for B in batches:
+            torch.cuda.empty_cache()
+            torch.cuda.reset_peak_memory_stats()
+            caches = []
+            try:
+                reps = (B + pool_b - 1) // pool_b
+                k = kp.repeat(reps, 1, 1, 1)[:B].contiguous()
+                v = vp.repeat(reps, 1, 1, 1)[:B].contiguous()
+                for _ in range(layers):
+                    c = gear.Cache(B, heads, d, pp, fp, n_prompt, buf_tokens=buf, max_new_tokens=max_new,
+                                   q_heads=heads)
+                    if n_prompt:
+                        c.load_prompt(k, v)
+                    else:
+                        c.append(k, v)
+                    caches.append(c)
+                del k, v
+                kn = steps_k.repeat(1, reps, 1, 1)[:, :B].contiguous()
+                vn = steps_v.repeat(1, reps, 1, 1)[:, :B].contiguous()
+                q = qpool.repeat(reps, 1, 1)[:B].contiguous()
+                o = torch.empty((B, heads, d), dtype=torch.float32, device="cuda")
+                torch.cuda.synchronize()
+                t0 = None
+                for s_ in range(warm + steps):
+                    if s_ == warm:
+                        torch.cuda.synchronize()
+                        t0 = time.perf_counter()
+                    for c in caches:
+                        c.append(kn[s_ % 4], vn[s_ % 4])
+                        c.decode_attn(q, out=o)
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                rec["runs"].append({"batch": B, "tok_s": round(B * steps / dt, 1),
+                                    "ms_per_step": round(dt * 1e3 / steps, 3),
+                                    "peak_GB": round(torch.cuda.max_memory_allocated() / 1e9, 2)})
+                print(f"[sweep] {name} B={B}: {B * steps / dt:.0f} tok/s, peak "
+                      f"{torch.cuda.max_memory_allocated() / 1e9:.1f} GB", file=sys.stderr, flush=True)
+            except torch.cuda.OutOfMemoryError:
+                rec["runs"].append({"batch": B, "oom": True})
+                print(f"[sweep] {name} B={B}: out of memory", file=sys.stderr, flush=True)
+            del caches
+            torch.cuda.synchronize()
+        done = [r for r in rec["runs"] if "tok_s" in r]
+        rec["peak_tok_s"] = max((r["tok_s"] for r in done), default=None)
+        out[name] = rec
+    base = out["fp16"]
+    for name, rec in out.items():
+        if base["peak_tok_s"] and rec["peak_tok_s"]:
+            rec["throughput_vs_fp16"] = round(rec["peak_tok_s"] / base["peak_tok_s"], 2)
+        rec["max_batch_vs_fp16"] = round(rec["max_batch"] / max(base["max_batch"], 1), 2)
+        same = [r for r in rec["runs"] if r.get("batch") == 64 and "peak_GB" in r]
+        fb = [r for r in base["runs"] if r.get("batch") == 64 and "peak_GB" in r]
+        if same and fb:
+            rec["peak_memory_vs_fp16_at_batch_64"] = round(fb[0]["peak_GB"] / same[0]["peak_GB"], 2)
+    return out
+
+
+def sweep_table(path: str) -> str:
+    """The text table of a --sweep JSON line (profiles/ summary)."""
+    with open(path) as f:
+        d = json.loads([l for l in f if l.startswith("{")][-1])
+    lines = [f"# {d['metric']}", f"# {d['model']}; {d['data']}; wall {d['wall_s']} s",
+             f"{'cache':18s} {'MB/seq':>8s} {'max_batch':>9s} {'peak_tok_s':>10s} {'tok/s vs fp16':>13s} "
+             f"{'batch vs fp16':>13s} {'mem vs fp16 @64':>15s}"]
+    for k, v in d["configs"].items():
+        lines.append(f"{k:18s} {v['cache_bytes_per_sequence'] / 1e6:8.1f} {v['max_batch']:9d} "
+                     f"{v['peak_tok_s'] or 0:10.1f} {v.get('throughput_vs_fp16', 0):13.2f} "
+                     f"{v['max_batch_vs_fp16']:13.2f} {v.get('peak_memory_vs_fp16_at_batch_64', 0):15.2f}")
+    lines.append("# per batch: (batch, tok/s, peak GB)")
+    for k, v in d["configs"].items():
+        lines.append(f"{k:18s} " + " ".join(f"({r['batch']}, {r.get('tok_s', 'oom')}, {r.get('peak_GB', '-')})"
+                                             for r in v["runs"]))
+    return "\n".join(lines) + "\n"
+
+
 def _bound_from_counters(kernel: str, workload: str, launch_ms: float, algo_bytes: float):
     """The binding resource of `kernel` from the committed counters: VALU
     issue (instructions x 4 cycles over the launch's SIMD-cycles, as measured)
@@ -596,9 +728,38 @@ def main():
                     help="run the rocprofv3 passes and write the summary tables under OUTDIR")
     ap.add_argument("--keep-raw", action="store_true",
                     help="with --make-profiles: keep the raw rocprofv3 output")
+    ap.add_argument("--sweep", action="store_true",
+                    help="KV-only decode sweep (batch until HBM is full, 32 layers, FP16 / GEAR / "
+                         "GEAR-L / KIVI) instead of the benchmark step")
+    ap.add_argument("--sweep-layers", type=int, default=32)
+    ap.add_argument("--sweep-prompt", type=int, default=2048)
+    ap.add_argument("--sweep-new", type=int, default=64)
+    ap.add_argument("--sweep-steps", type=int, default=8)
+    ap.add_argument("--sweep-table", metavar="JSON", help="print the table of a --sweep output")
     args = ap.parse_args()
+    if args.sweep_table:
+        print(sweep_table(args.sweep_table), end="")
+        return
     if args.make_profiles:
         sys.exit(make_profiles(os.path.abspath(args.make_profiles), args.workload, args.keep_raw))
+    if args.sweep:
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        import torch
+
+        import kv_cache_compression_gear_amd as gear
+        torch.cuda.set_device(0)
+        t0 = time.perf_counter()
+        res = _sweep(gear, torch, args.sweep_layers, 32, 128, args.sweep_prompt, args.sweep_new,
+                     args.sweep_steps, 2)
+        print(json.dumps({"metric": "KV-only decode sweep: tok/s and peak HBM, batch raised until HBM is full",
+                          "model": f"7B-shaped KV caches: {args.sweep_layers} layers x 32 heads x 128, "
+                                   f"prompt {args.sweep_prompt} + {args.sweep_new} new tokens "
+                                   f"({args.sweep_steps} timed decode steps)",
+                          "data": "synthetic (seeded, tiled over the batch)",
+                          "wall_s": round(time.perf_counter() - t0, 1), "configs": res}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the GEAR path has no cross-GPU step and this "
               f"build measures one GPU (--gpus {args.gpus} requested)", file=sys.stderr)

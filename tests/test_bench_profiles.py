@@ -102,3 +102,20 @@ def test_kernel_names_match_whole_symbols():
     assert bench._kernel_key("void gear::(anonymous namespace)::decompress_kernel<128, 4>(x)") == "decompress"
     assert bench._kernel_key(COMP) == "compress"
     assert bench._kernel_key("void at::native::elementwise_kernel<4>(x)") is None
+
+
+def test_sweep_table_from_a_sweep_line(tmp_path):
+    line = {"metric": "m", "model": "x", "data": "s", "wall_s": 1.0, "configs": {
+        "fp16": {"cache_bytes_per_sequence": 2e9, "max_batch": 100, "peak_tok_s": 10.0,
+                 "throughput_vs_fp16": 1.0, "max_batch_vs_fp16": 1.0, "peak_memory_vs_fp16_at_batch_64": 1.0,
+                 "runs": [{"batch": 64, "tok_s": 10.0, "peak_GB": 128.0}]},
+        "gear_4bit": {"cache_bytes_per_sequence": 1e9, "max_batch": 200, "peak_tok_s": 25.0,
+                      "throughput_vs_fp16": 2.5, "max_batch_vs_fp16": 2.0, "peak_memory_vs_fp16_at_batch_64": 2.0,
+                      "runs": [{"batch": 64, "tok_s": 25.0, "peak_GB": 64.0}, {"batch": 300, "oom": True}]}}}
+    import json
+    p = tmp_path / "s.json"
+    p.write_text("[sweep] progress\n" + json.dumps(line) + "\n")
+    t = bench.sweep_table(str(p))
+    row = [l for l in t.splitlines() if l.startswith("gear_4bit ")][0].split()
+    assert row[1] == "1000.0" and row[2] == "200" and float(row[4]) == 2.5
+    assert "(300, oom, -)" in t
