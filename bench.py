@@ -69,13 +69,14 @@ METRIC = "GEAR compress+decompress GB/s (fp16 KV in) & decode tok/s; % of HBM pe
 # kernel (name used by gear_timing_read, plus attn_prompt) -> source file
 KERNEL_SOURCE = {"select": "gear_compress.hip", "compress": "gear_compress.hip",
                  "lowrank_a": "gear_compress.hip", "decompress": "gear_decompress.hip",
-                 "attn_prompt": "gear_attn.hip", "attn_split": "gear_attn.hip",
-                 "attn_combine": "gear_attn.hip", "buffer_append": "gear_attn.hip"}
-# device symbol of each kernel ("attn_prompt" and "attn_split" are timed
-# together by the library, as "attn_split": the decode attention over all splits)
+                 "attn_prompt": "gear_attn.hip", "attn_gqa": "gear_attn.hip",
+                 "attn_split": "gear_attn.hip", "attn_combine": "gear_attn.hip", "buffer_append": "gear_attn.hip"}
+# device symbol of each kernel ("attn_prompt", "attn_gqa" and "attn_split" are
+# timed together by the library, as "attn_split": the decode attention over all splits)
 KERNEL_SYMBOL = {"select": "select_kernel", "compress": "compress_kernel",
                  "lowrank_a": "lowrank_a_kernel", "decompress": "decompress_kernel",
-                 "attn_prompt": "attn_prompt_kernel", "attn_split": "attn_split_kernel",
+                 "attn_prompt": "attn_prompt_kernel", "attn_gqa": "attn_gqa_kernel",
+                 "attn_split": "attn_split_kernel",
                  "attn_combine": "attn_combine_kernel", "buffer_append": "buffer_append_kernel"}
 SQ_PASSES = [
     ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES",
@@ -175,7 +176,7 @@ def kernel_stats_table(trace_csv: str, last: int, bench_json: dict | None, heade
         lines.append(f"# same run: value {bench_json['value']} GB/s, ms_per_step "
                      f"{bench_json['ms_per_step']}, roofline {bench_json['roofline']['kernel']} "
                      f"launch {bench_json['roofline']['launch_ms']} ms")
-    lines.append("# (bench_us: attn_prompt_kernel and attn_split_kernel are timed together as "
+    lines.append("# (bench_us: attn_prompt_kernel, attn_gqa_kernel and attn_split_kernel are timed together as "
                  "attn_split by the library)")
     return "\n".join(lines) + "\n"
 
@@ -270,7 +271,8 @@ def _entries_of(workload: str) -> dict:
     from kv_cache_compression_gear_amd.synth import WORKLOADS
     w = WORKLOADS[workload]
     n = 2 * w.batch * w.heads * w.seq * w.head_dim
-    return {"select": n, "compress": n, "lowrank_a": n, "decompress": n, "attn_prompt": n}
+    return {"select": n, "compress": n, "lowrank_a": n, "decompress": n, "attn_prompt": n,
+            "attn_gqa": n}
 
 
 def make_profiles(outdir: str, workload: str, keep_raw: bool = False) -> int:
@@ -393,7 +395,7 @@ def _median(v):
     return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
 
 
-def _codec_config(gear, torch, w, p, label, reps=10, decode=False):
+def _codec_config(gear, torch, w, p, label, reps=10, decode=False, role=0):
     """Compress and decompress of one whole workload (inputs resident), median
     of `reps` timed calls after 3 warm-up calls, per-kernel means from a second
     pass with the library's HIP events; optionally one decode step (append +
@@ -403,18 +405,18 @@ def _codec_config(gear, torch, w, p, label, reps=10, decode=False):
     k, v = syn.prompt(n)
     x = torch.cat([k.reshape(B * H, n, d), v.reshape(B * H, n, d)]).contiguous()
     M = x.shape[0]
-    L = gear.packed_layout(p, M, n, d)
-    packed = gear.Packed(torch.empty(L.total_bytes, dtype=torch.uint8, device="cuda"), p, M, n, d, L)
-    ws = torch.empty(gear.compress_workspace_bytes(p, M, n, d), dtype=torch.uint8, device="cuda")
+    L = gear.packed_layout(p, M, n, d, role)
+    packed = gear.Packed(torch.empty(L.total_bytes, dtype=torch.uint8, device="cuda"), p, M, n, d, L, role)
+    ws = torch.empty(gear.compress_workspace_bytes(p, M, n, d, role), dtype=torch.uint8, device="cuda")
     xhat = torch.empty_like(x)
     for _ in range(3):
-        gear.compress(x, p, out=packed, workspace=ws)
+        gear.compress(x, p, out=packed, workspace=ws, role=role)
         gear.decompress(packed, out=xhat)
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
     for e in ev:
         e[0].record()
-        gear.compress(x, p, out=packed, workspace=ws)
+        gear.compress(x, p, out=packed, workspace=ws, role=role)
         e[1].record()
         gear.decompress(packed, out=xhat)
         e[2].record()
@@ -423,7 +425,7 @@ def _codec_config(gear, torch, w, p, label, reps=10, decode=False):
     d_ms = _median([e[1].elapsed_time(e[2]) for e in ev])
     gear.timing_enable(True)
     for _ in range(reps):
-        gear.compress(x, p, out=packed, workspace=ws)
+        gear.compress(x, p, out=packed, workspace=ws, role=role)
         gear.decompress(packed, out=xhat)
     torch.cuda.synchronize()
     kt = gear.timing_read()
@@ -442,7 +444,8 @@ def _codec_config(gear, torch, w, p, label, reps=10, decode=False):
     del xhat, ws
     if decode:
         Hq = w.q_heads or H
-        fp = gear.Params(w.bits, w.group, w.outlier_ppm, w.fill_rank, w.power_iters)
+        fp = gear.Params(p.bits, p.group, p.outlier_ppm, min(p.rank, w.fill_rank), p.power_iters,
+                         quant=p.quant)
         cache = gear.Cache(B, H, d, p, fp, n, buf_tokens=w.buf_tokens, max_new_tokens=1, q_heads=Hq)
         cache.load_prompt(k.contiguous(), v.contiguous())
         kn, vn = syn.step()
@@ -471,17 +474,29 @@ def _codec_config(gear, torch, w, p, label, reps=10, decode=False):
 
 def _configs(gear, torch, WORKLOADS):
     out = {}
-    for name, s0, decode in (("tiny", False, True), ("2bit", False, True), ("long_ctx", False, True),
-                             ("7b_layer", True, False), ("2bit", True, False)):
-        w = WORKLOADS[name]
-        ppm = 0 if s0 else w.outlier_ppm
-        p = gear.Params(w.bits, w.group, ppm, w.rank, w.power_iters, w.chunk_tokens)
-        key = f"{name}_gear_l" if s0 else name
-        label = (f"{name}{' GEAR-L' if s0 else ''}: batch {w.batch}, {w.heads} heads, {w.seq} tokens, "
-                 f"head_dim {w.head_dim}, b={w.bits} g={w.group} s={ppm / 1e4:g}% r={w.rank} "
+    # (key, workload, bits, group, outlier_ppm, quant, role, decode step)
+    runs = [("tiny", "tiny", None, None, None, 0, 0, True),
+            ("2bit", "2bit", None, None, None, 0, 0, True),
+            ("long_ctx", "long_ctx", None, None, None, 0, 0, True),
+            ("7b_layer_gear_l", "7b_layer", None, None, 0, 0, 0, True),
+            ("2bit_gear_l", "2bit", None, None, 0, 0, 0, False),
+            # the backbones at the 7B-layer shape: KIVI 2-bit keys per channel
+            # in groups of 64 tokens (values per token), low rank, no outliers;
+            # ZipCache 4-bit tokenwise with 2% outliers
+            ("7b_layer_kivi_2bit_gear_l", "7b_layer", 2, 64, 0, 1, 2, True),
+            ("7b_layer_zipcache", "7b_layer", 4, 128, None, 2, 0, True)]
+    names = {0: "", 1: " KIVI", 2: " ZipCache"}
+    for key, wname, bits, group, ppm, quant, role, decode in runs:
+        w = WORKLOADS[wname]
+        bits = w.bits if bits is None else bits
+        group = w.group if group is None else group
+        ppm = w.outlier_ppm if ppm is None else ppm
+        p = gear.Params(bits, group, ppm, w.rank, w.power_iters, w.chunk_tokens, quant=quant)
+        label = (f"{wname}{names[quant]}{' GEAR-L' if ppm == 0 else ''}: batch {w.batch}, {w.heads} heads, "
+                 f"{w.seq} tokens, head_dim {w.head_dim}, b={bits} g={group} s={ppm / 1e4:g}% r={w.rank} "
                  f"t={w.power_iters}" + (f", chunks of {w.chunk_tokens}" if w.chunk_tokens else ""))
         print(f"[bench] config {key}", file=sys.stderr, flush=True)
-        out[key] = _codec_config(gear, torch, w, p, label, decode=decode)
+        out[key] = _codec_config(gear, torch, w, p, label, decode=decode, role=role)
     return out
 
 

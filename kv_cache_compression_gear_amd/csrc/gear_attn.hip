@@ -47,6 +47,13 @@ struct Piece {
     int len;
 };
 
+// Workgroup barrier for LDS traffic only: the wave's LDS operations are
+// complete, global loads in flight stay in flight (the compiler waits for
+// them where their registers are used).
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ Piece find_piece(const AttnArgs& a, int b, int hk, int t, int t_end) {
     Piece pc;
     const int pt = a.prompt.count ? a.prompt.chunks * a.prompt.p.rows : 0;
@@ -1125,6 +1132,549 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     }
 }
 
+// ---------------------------------------------------------------------------
+// Whole prompt splits with G = 2, 4 or 8 query heads per KV head (head_dim
+// 128, one or two quantization groups per token, GEAR's own quantizer), with
+// the G-head products on the matrix cores.  fp16(q) times a small integer code
+// is exact in fp32, so the products are those of the VALU kernels; only the
+// order of the fp32 sums differs.
+//   K: a wave's 32 tokens in two tiles of 16.  Each lane turns 8 codes of a
+//      token into 8 exact fp16 values (byte permutes, minus 1024), and
+//      v_mfma_f32_16x16x32_f16 gives q_h . codes_t for all heads (rows of Q,
+//      zero past G) and the tile's tokens at once, one accumulator per
+//      quantization group; scale, zero, low-rank and sparse terms are added
+//      per token as in the VALU kernels.
+//   V: per 16-token piece the codes go to the wave's fp16 LDS tile (row per
+//      token), transposing reads (ds_read_b64_tr_b16) give the B operands of
+//      v_mfma_f32_16x16x16_f16 with A = p_t scale_t (an fp16 hi + lo pair:
+//      the product is accurate to ~2^-22); the piece's V outliers are then
+//      written into the cleared tile and added the same way with A = p_t.
+//      Zero-point and low-rank terms are per-head sums over the tokens.
+// 8 waves, one workgroup per (split, KV head, batch); two workgroups per CU.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+constexpr int kMmCap = 1024;        // CSR entries of a matrix split staged in LDS
+constexpr bool kUseGqaKernel = true;
+constexpr int kMmWaves = 8;
+constexpr int kMmThreads = 64 * kMmWaves;
+
+// Position, among the 8 fp16 values codes_f16 makes from one word, of the
+// word's e-th code: 4-bit words give the codes in the order 0,2,4,6,1,3,5,7,
+// 2-bit (16-bit) words 0,4,1,5,2,6,3,7.
+template <int BITS>
+__device__ __forceinline__ int code_pos(int e) {
+    return BITS == 4 ? ((e & 1) ? 4 + (e >> 1) : (e >> 1)) : (2 * (e & 3) + (e >> 2));
+}
+template <int BITS>
+__device__ __forceinline__ int code_at(int p) {   // inverse of code_pos
+    return BITS == 4 ? ((p < 4) ? 2 * p : 2 * (p - 4) + 1) : (4 * (p & 1) + (p >> 1));
+}
+
+// 8 codes of a word as 8 exact fp16 values (order: code_pos).  Each byte c
+// becomes the fp16 pattern 0x64cc = 1024 + c, and 1024 is subtracted exactly.
+template <int BITS>
+__device__ __forceinline__ f16x8 codes_f16(uint32_t w) {
+    uint32_t u0, u1;
+    if (BITS == 4) {
+        u0 = w & 0x0F0F0F0Fu;              // codes 0, 2, 4, 6 as bytes
+        u1 = (w >> 4) & 0x0F0F0F0Fu;       // codes 1, 3, 5, 7
+    } else {
+        const uint32_t b0 = w & 0x0303u, b1 = (w >> 2) & 0x0303u;
+        const uint32_t b2 = (w >> 4) & 0x0303u, b3 = (w >> 6) & 0x0303u;
+        u0 = b0 | (b1 << 16);              // codes 0, 4, 1, 5
+        u1 = b2 | (b3 << 16);              // codes 2, 6, 3, 7
+    }
+    const uint32_t k64 = 0x64646464u;
+    const f16x2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+    const f16x2 h0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(k64, u0, 0x04010400u)) + m1024;
+    const f16x2 h1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(k64, u0, 0x04030402u)) + m1024;
+    const f16x2 h2 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(k64, u1, 0x04010400u)) + m1024;
+    const f16x2 h3 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(k64, u1, 0x04030402u)) + m1024;
+    return f16x8{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+}
+
+// byte offset in the wave's V tile (16 rows of 128 fp16) of the 16-byte chunk
+// c of row r, XOR-swizzled so that transposing reads and row writes spread
+// over the banks
+__device__ __forceinline__ int vtile_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+
+template <int G, int BITS, int NGR>
+__global__ void __launch_bounds__(kMmThreads, 4) attn_gqa_kernel(AttnArgs a) {
+    constexpr int D = 128, TPW = kTPS / kMmWaves;       // 32 tokens per wave
+    constexpr int ROWB = D * BITS / 8;                   // code bytes per token
+    constexpr int CPT = kMmCap / kMmThreads;             // staged entries per thread
+    constexpr int RL = G > 4 ? 32 : 16;                  // lanes holding a tile's results
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    // LDS.  Until phase 2 the region of the per-wave V tiles (at the end, of
+    // the waves' output rows) holds what only the K phase reads: q in fp32,
+    // B_K transposed, K's scales, zeros, A rows and CSR entries.  A rows and
+    // B matrices are padded to kMaxRank with zeros, so that the rank loops
+    // run unconditionally over kMaxRank.
+    constexpr int kTileBytes = 16 * D * 2;
+    constexpr int kVBytes = kMmWaves * kTileBytes > kMmWaves * G * D * 4 ? kMmWaves * kTileBytes
+                                                                         : kMmWaves * G * D * 4;
+    constexpr int kOffBkt = G * D * 4;
+    constexpr int kOffGsk = kOffBkt + kMaxRank * D * 4;
+    constexpr int kOffGzk = kOffGsk + kTPS * NGR * 4;
+    constexpr int kOffAk = kOffGzk + kTPS * NGR * 4;
+    constexpr int kOffCvk = kOffAk + kTPS * kMaxRank * 4;
+    static_assert(kOffCvk + kMmCap * 4 <= kVBytes, "the K phase's data fits the tiles' region");
+    __shared__ __attribute__((aligned(16))) unsigned char s_v[kVBytes];
+    float* s_q = reinterpret_cast<float*>(s_v);
+    float* s_bkt = reinterpret_cast<float*>(s_v + kOffBkt);    // [c][j]
+    float* s_gsk = reinterpret_cast<float*>(s_v + kOffGsk);
+    float* s_gzk = reinterpret_cast<float*>(s_v + kOffGzk);
+    float* s_ak = reinterpret_cast<float*>(s_v + kOffAk);
+    uint32_t* s_cvk = reinterpret_cast<uint32_t*>(s_v + kOffCvk);   // column | value << 16
+    __shared__ __attribute__((aligned(16))) uint16_t s_qh[G * D];     // q's fp16 bits
+    __shared__ __attribute__((aligned(16))) float s_qb[G * kMaxRank];
+    __shared__ float s_qs[G * NGR];                      // sum of q over each group
+    __shared__ float s_sc[kTPS * G];                     // scores, then probabilities
+    // V's scales, zeros, A rows and CSR entries; B_V ([j][c])
+    __shared__ __attribute__((aligned(16))) float s_gs[kTPS * NGR];
+    __shared__ __attribute__((aligned(16))) float s_gz[kTPS * NGR];
+    __shared__ __attribute__((aligned(16))) float s_a[kTPS * kMaxRank];
+    __shared__ uint32_t s_cv[kMmCap];
+    __shared__ __attribute__((aligned(16))) float s_bv[D * kMaxRank];
+    __shared__ int32_t s_rk[kTPS + 1];
+    __shared__ int32_t s_rv[kTPS + 1];
+    __shared__ float s_wm[4 * G];
+    __shared__ float s_ws[4 * G];
+
+    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
+    const int split = (int)group_id_x(), hk = (int)group_id_y(), b = (int)group_id_z();
+    const int pair = b * a.Hkv + hk;
+    const int t0 = split * kTPS;
+    const Piece pc = find_piece(a, b, hk, t0, t0 + kTPS);
+    const Packed& p = pc.p;
+    const int r = p.rank;
+    const uint32_t kk = (uint32_t)p.k;
+    const size_t mrk = (size_t)pc.mk * p.rows + pc.row0, mrv = (size_t)pc.mv * p.rows + pc.row0;
+    const int li = lane & 15, kb = lane >> 4;           // MFMA lane coordinates
+
+    // ---------------- one round of loads: everything the split reads.  The
+    // CSR ranges come from the row pointers at both ends (uniform, read
+    // first).  What goes to LDS is issued first and stored at once (one wait,
+    // for loads issued together); K's and V's codes stay in registers, V's in
+    // flight through the K phase (the barriers wait on LDS only:
+    // lds_barrier).  Every load is unconditional, from a clamped (valid)
+    // address, and selected where it is stored: a load under a divergent
+    // condition is waited for inside its branch, and the in-order counter
+    // then drains every load issued before it.  With r = 0 or no outliers
+    // the matrix's scales or row pointers stand in for the A, B, column and
+    // value arrays (which may then be absent): a valid address whose value
+    // is not used.
+    static_assert(kTPS == 256 && kTPS * NGR / 4 <= 128 && D <= 128 && G * D <= 2 * kMmThreads,
+                  "thread mapping of the staged loads");
+    const int32_t* rpk = p.row_ptr + (size_t)pc.mk * (p.rows + 1) + pc.row0;
+    const int32_t* rpv = p.row_ptr + (size_t)pc.mv * (p.rows + 1) + pc.row0;
+    const int beg_k = min(max(rpk[0], 0), (int)kk);
+    const int cnt_k = max(min(max(rpk[kTPS], 0), (int)kk) - beg_k, 0);
+    const int beg_v = min(max(rpv[0], 0), (int)kk);
+    const int cnt_v = max(min(max(rpv[kTPS], 0), (int)kk) - beg_v, 0);
+    const bool stg_k = cnt_k <= kMmCap, stg_v = cnt_v <= kMmCap;
+    // (which half, and which quarter below, a thread is in depends on its wave
+    // only: read as wave-uniform, so that every base address is scalar and
+    // each lane adds a 32-bit offset)
+    const int half = __builtin_amdgcn_readfirstlane(tid >> 8);      // 0 stages K's data, 1 V's
+    const int qtr = __builtin_amdgcn_readfirstlane((tid >> 7) & 1);
+    const int ri = tid & 255;
+    const size_t mrow_h = half ? mrv : mrk;
+    const int ng4 = kTPS * NGR / 4, rl1 = max(r, 1) - 1;
+    // scales (threads [0, 128) of a half) and zeros ([128, 256)): one float4 each
+    const float* gsrc = (qtr ? p.zero : p.scale) + mrow_h * NGR;
+    const f4v gsz = ld_at<f4v>(gsrc, (uint32_t)min(ri & 127, ng4 - 1) * 16u);
+    // row ri of A of the half's matrix
+    const float* asrc = r > 0 ? p.A + mrow_h * r : p.scale + mrow_h * NGR;
+    float arow[kMaxRank];
+#pragma unroll
+    for (int c = 0; c < kMaxRank; ++c) arow[c] = ld_at<float>(asrc, (uint32_t)(ri * r + min(c, rl1)) * 4u);
+    const uint16_t* qb = a.q + ((size_t)b * a.Hq + hk * G) * D;
+    uint16_t qv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) qv[u] = ld_at<uint16_t>(qb, (uint32_t)min(tid + u * kMmThreads, G * D - 1) * 2u);
+    // the half's row pointers
+    const int32_t* rph = half ? rpv : rpk;
+    const int32_t rp0 = ld_at<int32_t>(rph, (uint32_t)ri * 4u);
+    const int32_t rp1 = rph[kTPS];
+    // row bj of B_K (threads [0, 128)) or of B_V ([128, 256))
+    const int bj = tid & 127;
+    const float* bsrc = r > 0 ? p.B + (size_t)(qtr ? pc.mv : pc.mk) * D * r : p.scale + mrk * NGR;
+    float brow[kMaxRank];
+#pragma unroll
+    for (int c = 0; c < kMaxRank; ++c) brow[c] = ld_at<float>(bsrc, (uint32_t)(bj * r + min(c, rl1)) * 4u);
+    // both matrices' CSR entries of the split (contiguous ranges)
+    const uint16_t* rps = reinterpret_cast<const uint16_t*>(rpk);
+    const uint16_t* colk = kk > 0 ? p.col + (size_t)pc.mk * kk : rps;
+    const uint16_t* valk = kk > 0 ? p.val + (size_t)pc.mk * kk : rps;
+    const uint16_t* colv = kk > 0 ? p.col + (size_t)pc.mv * kk : rps;
+    const uint16_t* valv = kk > 0 ? p.val + (size_t)pc.mv * kk : rps;
+    const int klast = max((int)kk, 1) - 1;
+    uint16_t ekc[CPT], ekv[CPT], evc[CPT], evv[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const uint32_t ik = (uint32_t)min(beg_k + tid + j * kMmThreads, klast) * 2u;
+        const uint32_t iv = (uint32_t)min(beg_v + tid + j * kMmThreads, klast) * 2u;
+        ekc[j] = ld_at<uint16_t>(colk, ik);
+        ekv[j] = ld_at<uint16_t>(valk, ik);
+        evc[j] = ld_at<uint16_t>(colv, iv);
+        evv[j] = ld_at<uint16_t>(valv, iv);
+    }
+    // K codes of the wave's two tiles: lane (li, kb) takes token li of a tile
+    // and, for MFMA m, the 8 columns kcol(m) .. + 7: 32 contiguous columns
+    // (one load) with one group per token, 16 in each group with two (the
+    // MFMA's reduction order is free, as long as Q's operand follows it)
+    auto kcol = [&](int m) { return NGR == 1 ? 32 * kb + 8 * m : 64 * (m >> 1) + 16 * kb + 8 * (m & 1); };
+    const unsigned char* ck = p.codes + mrk * ROWB;
+    uint32_t wk[2][4];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t row = (uint32_t)((wv * TPW + tt * 16 + li) * ROWB);
+        if (NGR == 1) {
+            const uint32_t off = row + (uint32_t)(32 * kb * BITS / 8);
+            if (BITS == 4) {
+                const uint4 w = ld_at<uint4>(ck, off);
+                wk[tt][0] = w.x, wk[tt][1] = w.y, wk[tt][2] = w.z, wk[tt][3] = w.w;
+            } else {
+                const uint2 w = ld_at<uint2>(ck, off);
+                wk[tt][0] = w.x & 0xffffu, wk[tt][1] = w.x >> 16, wk[tt][2] = w.y & 0xffffu, wk[tt][3] = w.y >> 16;
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const uint32_t off = row + (uint32_t)((64 * g + 16 * kb) * BITS / 8);
+                if (BITS == 4) {
+                    const uint2 w = ld_at<uint2>(ck, off);
+                    wk[tt][2 * g] = w.x, wk[tt][2 * g + 1] = w.y;
+                } else {
+                    const uint32_t w = ld_at<uint32_t>(ck, off);
+                    wk[tt][2 * g] = w & 0xffffu, wk[tt][2 * g + 1] = w >> 16;
+                }
+            }
+        }
+    }
+    // V's codes: lane (row 4 s + kb of a 16-token piece, columns 8 li .. + 7)
+    // of the wave's two pieces
+    const unsigned char* cvb = p.codes + mrv * ROWB;
+    uint32_t wvv[2][4];
+#pragma unroll
+    for (int pcs = 0; pcs < 2; ++pcs)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t off = (uint32_t)((wv * TPW + pcs * 16 + 4 * s + kb) * ROWB + li * BITS);
+            wvv[pcs][s] = BITS == 4 ? ld_at<uint32_t>(cvb, off) : (uint32_t)ld_at<uint16_t>(cvb, off);
+        }
+    // into LDS
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        if (tid + u * kMmThreads < G * D) {
+            s_q[tid + u * kMmThreads] = h2f(qv[u]);
+            s_qh[tid + u * kMmThreads] = qv[u];
+        }
+    {
+        float* gdst = half ? (qtr ? s_gz : s_gs) : (qtr ? s_gzk : s_gsk);
+        if ((ri & 127) < ng4) reinterpret_cast<f4v*>(gdst)[ri & 127] = gsz;
+        f4v a0, a1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            a0[c] = c < r ? arow[c] : 0.0f;
+            a1[c] = c + 4 < r ? arow[c + 4] : 0.0f;
+        }
+        float* adst = (half ? s_a : s_ak) + ri * kMaxRank;
+        reinterpret_cast<f4v*>(adst)[0] = a0;
+        reinterpret_cast<f4v*>(adst)[1] = a1;
+        int32_t* srp = half ? s_rv : s_rk;
+        srp[ri] = min(max(rp0, 0), (int)kk);
+        if (ri == 0) srp[kTPS] = min(max(rp1, 0), (int)kk);
+    }
+    if (tid < 128) {
+#pragma unroll
+        for (int c = 0; c < kMaxRank; ++c) s_bkt[c * D + bj] = c < r ? brow[c] : 0.0f;
+    } else if (tid < 256) {
+        f4v b0, b1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            b0[c] = c < r ? brow[c] : 0.0f;
+            b1[c] = c + 4 < r ? brow[c + 4] : 0.0f;
+        }
+        reinterpret_cast<f4v*>(s_bv + bj * kMaxRank)[0] = b0;
+        reinterpret_cast<f4v*>(s_bv + bj * kMaxRank)[1] = b1;
+    }
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const int i = tid + j * kMmThreads;
+        if (stg_k && i < cnt_k) s_cvk[i] = (uint32_t)ekc[j] | ((uint32_t)ekv[j] << 16);
+        if (stg_v && i < cnt_v) s_cv[i] = (uint32_t)evc[j] | ((uint32_t)evv[j] << 16);
+    }
+    lds_barrier();
+
+    // (B_K^T q)[h][c] and the sums of q over each group: 16 lanes per output,
+    // D / 16 columns each, summed over the lane row
+    for (int i = tid; i < G * kMaxRank * 16; i += kMmThreads) {
+        const int hc = i / 16, j0 = (i % 16) * (D / 16);
+        const int h = hc / kMaxRank, c = hc % kMaxRank;
+        float v = 0.0f;   // (zero past the rank: s_bkt is padded with zeros)
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j) v = fmaf(s_q[h * D + j0 + j], s_bkt[c * D + j0 + j], v);
+        v = row_allreduce<16>(v);
+        if ((i % 16) == 0) s_qb[hc] = v;
+    }
+    for (int i = tid; i < G * NGR * 16; i += kMmThreads) {
+        const int hg = i / 16, h = hg / NGR, gi = hg % NGR;
+        const int j0 = gi * (D / NGR) + (i % 16) * (D / NGR / 16);
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < D / NGR / 16; ++j) v += s_q[h * D + j0 + j];
+        v = row_allreduce<16>(v);
+        if ((i % 16) == 0) s_qs[hg] = v;
+    }
+    // Q operands: row li (head, zero past G), the columns of MFMA m and lane
+    // group kb in the order of the code words
+    // (q's 8 fp16 values of the columns, one 16-byte read, then their halves
+    // rearranged in code_pos order by byte permutes)
+    f16x8 qop[4];
+    {
+        const int qrow = min(li, G - 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const uint4 w = *reinterpret_cast<const uint4*>(s_qh + qrow * D + kcol(m));
+            uint32_t o0, o1, o2, o3;
+            if (BITS == 4) {   // values 0, 2, 4, 6, 1, 3, 5, 7
+                o0 = __builtin_amdgcn_perm(w.y, w.x, 0x05040100u);
+                o1 = __builtin_amdgcn_perm(w.w, w.z, 0x05040100u);
+                o2 = __builtin_amdgcn_perm(w.y, w.x, 0x07060302u);
+                o3 = __builtin_amdgcn_perm(w.w, w.z, 0x07060302u);
+            } else {           // values 0, 4, 1, 5, 2, 6, 3, 7
+                o0 = __builtin_amdgcn_perm(w.z, w.x, 0x05040100u);
+                o1 = __builtin_amdgcn_perm(w.z, w.x, 0x07060302u);
+                o2 = __builtin_amdgcn_perm(w.w, w.y, 0x05040100u);
+                o3 = __builtin_amdgcn_perm(w.w, w.y, 0x07060302u);
+            }
+            const bool on = li < G;   // rows past the heads are zero
+            qop[m] = __builtin_bit_cast(f16x8, make_uint4(on ? o0 : 0u, on ? o1 : 0u, on ? o2 : 0u, on ? o3 : 0u));
+        }
+    }
+    lds_barrier();
+
+    // ---------------- phase 1: q . K^_t on the matrix cores
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+        f32x4 acc[NGR];
+#pragma unroll
+        for (int gi = 0; gi < NGR; ++gi) acc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f16x8 bop = codes_f16<BITS>(wk[tt][m]);
+            const int gi = NGR == 1 ? 0 : m / 2;
+            acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[m], bop, acc[gi], 0, 0, 0);
+        }
+        // lane (li, kb < RL / 16) holds heads 4 kb + i of token li of the tile
+        // (the zero-point, low-rank and sparse terms follow, per token)
+        if (lane < RL) {
+            const int tok = wv * TPW + tt * 16 + li;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * kb + i;
+                if (h < G) {
+                    float v = 0.0f;
+#pragma unroll
+                    for (int gi = 0; gi < NGR; ++gi) v = fmaf(s_gsk[tok * NGR + gi], acc[gi][i], v);
+                    s_sc[tok * G + h] = v;
+                }
+            }
+        }
+    }
+    lds_barrier();
+
+    // ---------------- sparse part of the scores (one thread per token), softmax
+    float pr[G];
+    if (tid < kTPS) {
+        float add[G];
+        // zero-point and low-rank terms (A rows and B_K^T q padded with zeros
+        // past the rank)
+        const f4v a0 = reinterpret_cast<const f4v*>(s_ak + tid * kMaxRank)[0];
+        const f4v a1 = reinterpret_cast<const f4v*>(s_ak + tid * kMaxRank)[1];
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const f4v q0 = reinterpret_cast<const f4v*>(s_qb + h * kMaxRank)[0];
+            const f4v q1 = reinterpret_cast<const f4v*>(s_qb + h * kMaxRank)[1];
+            float v = 0.0f;
+#pragma unroll
+            for (int gi = 0; gi < NGR; ++gi) v = fmaf(s_gzk[tid * NGR + gi], s_qs[h * NGR + gi], v);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v = fmaf(a0[c], q0[c], fmaf(a1[c], q1[c], v));
+            add[h] = v;
+        }
+        for (int k2 = s_rk[tid]; k2 < s_rk[tid + 1]; ++k2) {
+            const uint32_t e = stg_k ? s_cvk[k2 - beg_k] : ((uint32_t)colk[k2] | ((uint32_t)valk[k2] << 16));
+            const int cj = (int)(e & (D - 1));
+            const float v = h2f(e >> 16);
+#pragma unroll
+            for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
+        }
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            pr[h] = a.sm_scale * (s_sc[tid * G + h] + add[h]);
+            const float m = wave_max(pr[h]);
+            if (lane == 0) s_wm[wv * G + h] = m;
+        }
+    }
+    // (also ends the reads of what the K phase staged in the tiles' region)
+    lds_barrier();
+    if (tid < kTPS) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float m = fmaxf(fmaxf(s_wm[h], s_wm[G + h]), fmaxf(s_wm[2 * G + h], s_wm[3 * G + h]));
+            pr[h] = expf(pr[h] - m);
+            s_sc[tid * G + h] = pr[h];
+            const float sm = wave_sum(pr[h]);
+            if (lane == 0) s_ws[wv * G + h] = sm;
+        }
+    }
+    lds_barrier();
+
+    // ---------------- phase 2: sum_t p_t V^_t on the matrix cores
+    unsigned char* tile = s_v + wv * kTileBytes;
+    f32x4 vacc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) vacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // sum_t p_t A_t[c] and sum_t p_t zero_t[g] per head (into s_qb and s_qs,
+    // whose K-side values are no longer read): 16 lanes per (head, term),
+    // lane l taking tokens l, l + 16, ... (consecutive lanes, consecutive
+    // tokens: no bank conflicts), summed over the lane row
+    constexpr int NTM = kMaxRank + NGR;
+    for (int i = tid; i < G * NTM * 16; i += kMmThreads) {
+        const int ht = i / 16, tl = i % 16;
+        const int h = ht / NTM, c = ht % NTM;
+        float v = 0.0f;
+        if (c < r) {
+#pragma unroll
+            for (int t = 0; t < kTPS; t += 16)
+                v = fmaf(s_sc[(t + tl) * G + h], s_a[(t + tl) * kMaxRank + c], v);
+        } else if (c >= kMaxRank) {
+#pragma unroll
+            for (int t = 0; t < kTPS; t += 16)
+                v = fmaf(s_sc[(t + tl) * G + h], s_gz[(t + tl) * NGR + c - kMaxRank], v);
+        }
+        v = row_allreduce<16>(v);
+        if ((i % 16) == 0) {
+            if (c < kMaxRank) s_qb[h * kMaxRank + c] = v;
+            else s_qs[h * NGR + c - kMaxRank] = v;
+        }
+    }
+#pragma unroll
+    for (int pcs = 0; pcs < 2; ++pcs) {
+        const int pb = wv * TPW + pcs * 16;            // the piece's first token
+        // the codes as fp16 rows of the tile (row 4 s + kb, 16-byte chunk li)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const f16x8 hv = codes_f16<BITS>(wvv[pcs][s]);
+            *reinterpret_cast<f16x8*>(tile + vtile_off(4 * s + kb, li)) = hv;
+        }
+        // A operands: row li (head), tokens 4 kb + i of the piece
+        f16x4 ahi[NGR], alo[NGR], phi, plo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tok = pb + 4 * kb + i;
+            const float pv = li < G ? s_sc[tok * G + li] : 0.0f;
+            const _Float16 h0 = (_Float16)pv;
+            phi[i] = h0;
+            plo[i] = (_Float16)(pv - (float)h0);
+#pragma unroll
+            for (int gi = 0; gi < NGR; ++gi) {
+                const float ps = pv * s_gs[tok * NGR + gi];
+                const _Float16 s0 = (_Float16)ps;
+                ahi[gi][i] = s0;
+                alo[gi][i] = (_Float16)(ps - (float)s0);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // B operands: transposing reads of the tile (column 16 nb + li of rows
+        // 4 kb .. 4 kb + 3); lane (li, kb) gives the address of row 4 kb + li / 4,
+        // columns 16 nb + 4 (li % 4) .. + 3
+        auto bop_at = [&](int nb) {
+            const int row = 4 * kb + (li >> 2);
+            const int col = 16 * nb + 4 * (li & 3);
+            const int off = vtile_off(row, col >> 3) + (col & 7) * 2;
+            return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off)));
+        };
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const int gi = NGR == 1 ? 0 : nb / 4;
+            const f16x4 bv = bop_at(nb);
+            vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(ahi[gi], bv, vacc[nb], 0, 0, 0);
+            vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(alo[gi], bv, vacc[nb], 0, 0, 0);
+        }
+        // the piece's V outliers: the tile cleared, each token's entries
+        // written (lane li < 16 takes token pb + li), then the same products
+        // with A = p_t
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            *reinterpret_cast<uint4*>(tile + vtile_off(4 * s + kb, li)) = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_wave_barrier();
+        const bool any = s_rv[pb + 16] > s_rv[pb];      // wave-uniform
+        if (any) {
+            if (lane < 16) {
+                const int tk = pb + lane;
+                for (int k2 = s_rv[tk]; k2 < s_rv[tk + 1]; ++k2) {
+                    const uint32_t e = stg_v ? s_cv[k2 - beg_v] : ((uint32_t)colv[k2] | ((uint32_t)valv[k2] << 16));
+                    const int cj = (int)(e & (D - 1));
+                    const int tc = (cj & ~7) | code_pos<BITS>(cj & 7);   // tile column of column cj
+                    *reinterpret_cast<uint16_t*>(tile + vtile_off(lane, tc >> 3) + (tc & 7) * 2) = (uint16_t)(e >> 16);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) {
+                const f16x4 bv = bop_at(nb);
+                vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(phi, bv, vacc[nb], 0, 0, 0);
+                vacc[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(plo, bv, vacc[nb], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    lds_barrier();   // every wave is done with its tile
+    // the waves' output rows (heads 4 kb + i, tile column 16 nb + li)
+    float* rows = reinterpret_cast<float*>(s_v);
+    if (lane < RL) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = 4 * kb + i;
+                if (h < G) rows[(wv * G + h) * D + 16 * nb + li] = vacc[nb][i];
+            }
+    }
+    __syncthreads();
+    float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
+    if (tid < G) {
+        part[tid * (D + 2) + D] = fmaxf(fmaxf(s_wm[tid], s_wm[G + tid]), fmaxf(s_wm[2 * G + tid], s_wm[3 * G + tid]));
+        part[tid * (D + 2) + D + 1] = s_ws[tid] + s_ws[G + tid] + s_ws[2 * G + tid] + s_ws[3 * G + tid];
+    }
+    for (int i = tid; i < G * D; i += kMmThreads) {
+        const int h = i / D, j = i % D;
+        const int tc = (j & ~7) | code_pos<BITS>(j & 7);   // tile column of column j
+        const int gi = NGR == 1 ? 0 : j / (D / NGR);
+        float num = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kMmWaves; ++w) num += rows[(w * G + h) * D + tc];
+        float lr = 0.0f;   // (B_V rows padded with zeros past the rank)
+        const f4v t0 = reinterpret_cast<const f4v*>(s_qb + h * kMaxRank)[0];
+        const f4v t1 = reinterpret_cast<const f4v*>(s_qb + h * kMaxRank)[1];
+        const f4v b0 = reinterpret_cast<const f4v*>(s_bv + j * kMaxRank)[0];
+        const f4v b1 = reinterpret_cast<const f4v*>(s_bv + j * kMaxRank)[1];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lr = fmaf(t0[c], b0[c], fmaf(t1[c], b1[c], lr));
+        part[h * (D + 2) + j] = num + s_qs[h * NGR + gi] + lr;
+    }
+}
+
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
     __shared__ float s_m[kThreads / 64];
@@ -1158,6 +1708,20 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
         if (a.split0 > 0) {
             const dim3 grid((unsigned)a.split0, (unsigned)a.Hkv, (unsigned)a.B);
             const int qk = a.prompt.p.chan ? 2 : a.prompt.p.ch_mats > 0 ? 1 : 0;
+            // several query heads per KV head: the matrix-core kernel
+            if constexpr (D == 128 && G >= 2) {
+                if (qk == 0 && kUseGqaKernel) {
+                    const int ngr = D / a.prompt.p.group;
+                    if (a.prompt.p.bits == 4) {
+                        if (ngr == 1) hipLaunchKernelGGL((attn_gqa_kernel<G, 4, 1>), grid, dim3(kMmThreads), 0, st, a);
+                        else hipLaunchKernelGGL((attn_gqa_kernel<G, 4, 2>), grid, dim3(kMmThreads), 0, st, a);
+                    } else {
+                        if (ngr == 1) hipLaunchKernelGGL((attn_gqa_kernel<G, 2, 1>), grid, dim3(kMmThreads), 0, st, a);
+                        else hipLaunchKernelGGL((attn_gqa_kernel<G, 2, 2>), grid, dim3(kMmThreads), 0, st, a);
+                    }
+                    goto prompt_done;
+                }
+            }
             if (a.prompt.p.bits == 4) {
                 if (qk == 0) hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4, 0>), grid, dim3(kFastThreads), 0, st, a);
                 else if (qk == 1) hipLaunchKernelGGL((attn_prompt_kernel<D, G, 4, 1>), grid, dim3(kFastThreads), 0, st, a);
@@ -1168,6 +1732,7 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
                 else hipLaunchKernelGGL((attn_prompt_kernel<D, G, 2, 2>), grid, dim3(kFastThreads), 0, st, a);
             }
         }
+    prompt_done:
         if (a.splits > a.split0)
             hipLaunchKernelGGL((attn_split_kernel<D, G>), dim3(pairs * (a.splits - a.split0)), dim3(kThreads),
                                0, st, a);
