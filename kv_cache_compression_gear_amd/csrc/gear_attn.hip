@@ -1204,15 +1204,16 @@ __device__ __forceinline__ f16x8 codes_f16(uint32_t w) {
 __device__ __forceinline__ int vtile_off(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
 
 template <int G, int BITS, int NGR>
-__global__ void __launch_bounds__(kMmThreads, 4) attn_gqa_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(AttnArgs a) {
     constexpr int D = 128, TPW = kTPS / kMmWaves;       // 32 tokens per wave
     constexpr int ROWB = D * BITS / 8;                   // code bytes per token
     constexpr int CPT = kMmCap / kMmThreads;             // staged entries per thread
     constexpr int RL = G > 4 ? 32 : 16;                  // lanes holding a tile's results
     typedef float f4v __attribute__((ext_vector_type(4)));
     // LDS.  Until phase 2 the region of the per-wave V tiles (at the end, of
-    // the waves' output rows) holds what only the K phase reads: q in fp32,
-    // B_K transposed, K's scales, zeros, A rows and CSR entries.  A rows and
+    // the waves' output rows) holds what only the K phase reads (q in fp32,
+    // B_K transposed, K's scales, zeros, A rows and CSR entries) and V's A
+    // rows (read by the sums that precede the tiles).  A rows and
     // B matrices are padded to kMaxRank with zeros, so that the rank loops
     // run unconditionally over kMaxRank.
     constexpr int kTileBytes = 16 * D * 2;
@@ -1223,7 +1224,8 @@ __global__ void __launch_bounds__(kMmThreads, 4) attn_gqa_kernel(AttnArgs a) {
     constexpr int kOffGzk = kOffGsk + kTPS * NGR * 4;
     constexpr int kOffAk = kOffGzk + kTPS * NGR * 4;
     constexpr int kOffCvk = kOffAk + kTPS * kMaxRank * 4;
-    static_assert(kOffCvk + kMmCap * 4 <= kVBytes, "the K phase's data fits the tiles' region");
+    constexpr int kOffAv = kOffCvk + kMmCap * 4;   // V's A rows (read before the tiles are written)
+    static_assert(kOffAv + kTPS * kMaxRank * 4 <= kVBytes, "the staged data fits the tiles' region");
     __shared__ __attribute__((aligned(16))) unsigned char s_v[kVBytes];
     float* s_q = reinterpret_cast<float*>(s_v);
     float* s_bkt = reinterpret_cast<float*>(s_v + kOffBkt);    // [c][j]
@@ -1231,14 +1233,14 @@ __global__ void __launch_bounds__(kMmThreads, 4) attn_gqa_kernel(AttnArgs a) {
     float* s_gzk = reinterpret_cast<float*>(s_v + kOffGzk);
     float* s_ak = reinterpret_cast<float*>(s_v + kOffAk);
     uint32_t* s_cvk = reinterpret_cast<uint32_t*>(s_v + kOffCvk);   // column | value << 16
+    float* s_a = reinterpret_cast<float*>(s_v + kOffAv);
     __shared__ __attribute__((aligned(16))) uint16_t s_qh[G * D];     // q's fp16 bits
     __shared__ __attribute__((aligned(16))) float s_qb[G * kMaxRank];
     __shared__ float s_qs[G * NGR];                      // sum of q over each group
     __shared__ float s_sc[kTPS * G];                     // scores, then probabilities
-    // V's scales, zeros, A rows and CSR entries; B_V ([j][c])
+    // V's scales, zeros and CSR entries; B_V ([j][c])
     __shared__ __attribute__((aligned(16))) float s_gs[kTPS * NGR];
     __shared__ __attribute__((aligned(16))) float s_gz[kTPS * NGR];
-    __shared__ __attribute__((aligned(16))) float s_a[kTPS * kMaxRank];
     __shared__ uint32_t s_cv[kMmCap];
     __shared__ __attribute__((aligned(16))) float s_bv[D * kMaxRank];
     __shared__ int32_t s_rk[kTPS + 1];
@@ -1567,6 +1569,7 @@ __global__ void __launch_bounds__(kMmThreads, 4) attn_gqa_kernel(AttnArgs a) {
             else s_qs[h * NGR + c - kMaxRank] = v;
         }
     }
+    lds_barrier();   // (V's A rows are read; the tiles take their bytes)
 #pragma unroll
     for (int pcs = 0; pcs < 2; ++pcs) {
         const int pb = wv * TPW + pcs * 16;            // the piece's first token
