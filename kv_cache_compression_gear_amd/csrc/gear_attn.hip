@@ -1247,6 +1247,8 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     __shared__ int32_t s_rv[kTPS + 1];
     __shared__ float s_wm[4 * G];
     __shared__ float s_ws[4 * G];
+    __shared__ float s_pa[4 * G * kMaxRank];            // per wave of a half: sum_t p_t A_t[c]
+    __shared__ float s_pz[4 * G * NGR];                 // sum_t p_t zero_t[g]
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int split = (int)group_id_x(), hk = (int)group_id_y(), b = (int)group_id_z();
@@ -1493,49 +1495,71 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     }
     lds_barrier();
 
-    // ---------------- sparse part of the scores (one thread per token), softmax
-    float pr[G];
-    if (tid < kTPS) {
-        float add[G];
+    // ---------------- rest of the scores, softmax: two threads per token,
+    // each with half of the heads (waves 0..3 the first half, 4..7 the other)
+    constexpr int GH = G / 2;
+    static_assert(G % 2 == 0, "an even number of query heads per KV head");
+    const int tt = tid & (kTPS - 1), h0 = half * GH;
+    const int wh = wv & 3;                               // wave within the half
+    float pr[GH];
+    {
+        float add[GH];
         // zero-point and low-rank terms (A rows and B_K^T q padded with zeros
         // past the rank)
-        const f4v a0 = reinterpret_cast<const f4v*>(s_ak + tid * kMaxRank)[0];
-        const f4v a1 = reinterpret_cast<const f4v*>(s_ak + tid * kMaxRank)[1];
+        const f4v a0 = reinterpret_cast<const f4v*>(s_ak + tt * kMaxRank)[0];
+        const f4v a1 = reinterpret_cast<const f4v*>(s_ak + tt * kMaxRank)[1];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+        for (int j = 0; j < GH; ++j) {
+            const int h = h0 + j;
             const f4v q0 = reinterpret_cast<const f4v*>(s_qb + h * kMaxRank)[0];
             const f4v q1 = reinterpret_cast<const f4v*>(s_qb + h * kMaxRank)[1];
             float v = 0.0f;
 #pragma unroll
-            for (int gi = 0; gi < NGR; ++gi) v = fmaf(s_gzk[tid * NGR + gi], s_qs[h * NGR + gi], v);
+            for (int gi = 0; gi < NGR; ++gi) v = fmaf(s_gzk[tt * NGR + gi], s_qs[h * NGR + gi], v);
 #pragma unroll
             for (int c = 0; c < 4; ++c) v = fmaf(a0[c], q0[c], fmaf(a1[c], q1[c], v));
-            add[h] = v;
+            add[j] = v;
         }
-        for (int k2 = s_rk[tid]; k2 < s_rk[tid + 1]; ++k2) {
+        // the sparse term, entries in CSR order
+        for (int k2 = s_rk[tt]; k2 < s_rk[tt + 1]; ++k2) {
             const uint32_t e = stg_k ? s_cvk[k2 - beg_k] : ((uint32_t)colk[k2] | ((uint32_t)valk[k2] << 16));
             const int cj = (int)(e & (D - 1));
             const float v = h2f(e >> 16);
 #pragma unroll
-            for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
+            for (int j = 0; j < GH; ++j) add[j] = fmaf(s_q[(h0 + j) * D + cj], v, add[j]);
         }
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            pr[h] = a.sm_scale * (s_sc[tid * G + h] + add[h]);
-            const float m = wave_max(pr[h]);
-            if (lane == 0) s_wm[wv * G + h] = m;
+        for (int j = 0; j < GH; ++j) {
+            pr[j] = a.sm_scale * (s_sc[tt * G + h0 + j] + add[j]);
+            const float m = wave_max(pr[j]);
+            if (lane == 0) s_wm[wh * G + h0 + j] = m;
         }
     }
-    // (also ends the reads of what the K phase staged in the tiles' region)
+    // (also ends the reads of the K phase's data in the tiles' region)
     lds_barrier();
-    if (tid < kTPS) {
+    // probabilities; with them the wave's sums of p_t, p_t zero_t[g] and
+    // p_t A_t[c] (V's A rows padded with zeros past the rank) per head
+    const f4v av0 = reinterpret_cast<const f4v*>(s_a + tt * kMaxRank)[0];
+    const f4v av1 = reinterpret_cast<const f4v*>(s_a + tt * kMaxRank)[1];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float m = fmaxf(fmaxf(s_wm[h], s_wm[G + h]), fmaxf(s_wm[2 * G + h], s_wm[3 * G + h]));
-            pr[h] = expf(pr[h] - m);
-            s_sc[tid * G + h] = pr[h];
-            const float sm = wave_sum(pr[h]);
-            if (lane == 0) s_ws[wv * G + h] = sm;
+    for (int j = 0; j < GH; ++j) {
+        const int h = h0 + j;
+        const float m = fmaxf(fmaxf(s_wm[h], s_wm[G + h]), fmaxf(s_wm[2 * G + h], s_wm[3 * G + h]));
+        pr[j] = expf(pr[j] - m);
+        s_sc[tt * G + h] = pr[j];
+        const float sm = wave_sum(pr[j]);
+        if (lane == 0) s_ws[wh * G + h] = sm;
+#pragma unroll
+        for (int gi = 0; gi < NGR; ++gi) {
+            const float z = wave_sum(pr[j] * s_gz[tt * NGR + gi]);
+            if (lane == 0) s_pz[(wh * G + h) * NGR + gi] = z;
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxRank; ++c) {
+            if (c < r) {   // uniform
+                const float v = wave_sum(pr[j] * (c < 4 ? av0[c & 3] : av1[c & 3]));
+                if (lane == 0) s_pa[(wh * G + h) * kMaxRank + c] = v;
+            }
         }
     }
     lds_barrier();
@@ -1545,31 +1569,6 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     f32x4 vacc[8];
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) vacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // sum_t p_t A_t[c] and sum_t p_t zero_t[g] per head (into s_qb and s_qs,
-    // whose K-side values are no longer read): 16 lanes per (head, term),
-    // lane l taking tokens l, l + 16, ... (consecutive lanes, consecutive
-    // tokens: no bank conflicts), summed over the lane row
-    constexpr int NTM = kMaxRank + NGR;
-    for (int i = tid; i < G * NTM * 16; i += kMmThreads) {
-        const int ht = i / 16, tl = i % 16;
-        const int h = ht / NTM, c = ht % NTM;
-        float v = 0.0f;
-        if (c < r) {
-#pragma unroll
-            for (int t = 0; t < kTPS; t += 16)
-                v = fmaf(s_sc[(t + tl) * G + h], s_a[(t + tl) * kMaxRank + c], v);
-        } else if (c >= kMaxRank) {
-#pragma unroll
-            for (int t = 0; t < kTPS; t += 16)
-                v = fmaf(s_sc[(t + tl) * G + h], s_gz[(t + tl) * NGR + c - kMaxRank], v);
-        }
-        v = row_allreduce<16>(v);
-        if ((i % 16) == 0) {
-            if (c < kMaxRank) s_qb[h * kMaxRank + c] = v;
-            else s_qs[h * NGR + c - kMaxRank] = v;
-        }
-    }
-    lds_barrier();   // (V's A rows are read; the tiles take their bytes)
 #pragma unroll
     for (int pcs = 0; pcs < 2; ++pcs) {
         const int pb = wv * TPW + pcs * 16;            // the piece's first token
@@ -1623,13 +1622,15 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
         __builtin_amdgcn_wave_barrier();
         const bool any = s_rv[pb + 16] > s_rv[pb];      // wave-uniform
         if (any) {
-            if (lane < 16) {
-                const int tk = pb + lane;
-                for (int k2 = s_rv[tk]; k2 < s_rv[tk + 1]; ++k2) {
+            {
+                // token pb + li's entries, every fourth from the kb-th (columns
+                // of a row are distinct: no two lanes write one element)
+                const int tk = pb + li;
+                for (int k2 = s_rv[tk] + kb; k2 < s_rv[tk + 1]; k2 += 4) {
                     const uint32_t e = stg_v ? s_cv[k2 - beg_v] : ((uint32_t)colv[k2] | ((uint32_t)valv[k2] << 16));
                     const int cj = (int)(e & (D - 1));
                     const int tc = (cj & ~7) | code_pos<BITS>(cj & 7);   // tile column of column cj
-                    *reinterpret_cast<uint16_t*>(tile + vtile_off(lane, tc >> 3) + (tc & 7) * 2) = (uint16_t)(e >> 16);
+                    *reinterpret_cast<uint16_t*>(tile + vtile_off(li, tc >> 3) + (tc & 7) * 2) = (uint16_t)(e >> 16);
                 }
             }
             __builtin_amdgcn_wave_barrier();
@@ -1643,6 +1644,15 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
         __builtin_amdgcn_wave_barrier();
     }
     lds_barrier();   // every wave is done with its tile
+    // the zero-point and low-rank sums over the 4 waves of a half, per head
+    // (into s_qs and s_qb, whose K-side values are no longer read)
+    if (tid < G * NGR) {
+        s_qs[tid] = (s_pz[tid] + s_pz[G * NGR + tid]) + (s_pz[2 * G * NGR + tid] + s_pz[3 * G * NGR + tid]);
+    } else if (tid >= 64 && tid < 64 + G * kMaxRank) {
+        const int hc = tid - 64;
+        constexpr int W = G * kMaxRank;
+        s_qb[hc] = hc % kMaxRank < r ? (s_pa[hc] + s_pa[W + hc]) + (s_pa[2 * W + hc] + s_pa[3 * W + hc]) : 0.0f;
+    }
     // the waves' output rows (heads 4 kb + i, tile column 16 nb + li)
     float* rows = reinterpret_cast<float*>(s_v);
     if (lane < RL) {
