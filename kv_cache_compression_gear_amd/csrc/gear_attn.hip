@@ -1688,15 +1688,59 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     }
 }
 
+// out[b][hq][:] = merge over the splits of (numerators, max, sum): one wave
+// per query head, lane l taking columns l D / 64 .. (D / 64 of them).  The
+// splits go in chunks of 8, whose (max, sum) pairs and the lane's numerators
+// are loaded together and folded into running sums under a running maximum
+// (no LDS, no barrier).
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_combine_kernel(AttnArgs a) {
-    __shared__ float s_m[kThreads / 64];
-    __shared__ float s_num[kThreads];
-    __shared__ float s_den[kThreads];
-    const int bh = (int)group_id_x();                 // b * Hq + hq
+    constexpr int CPL = D / 64, CH = 8;
+    const int lane = thread_id() & 63;
+    const int bh = (int)group_id_x() * (kThreads / 64) + wave_id(thread_id());   // b * Hq + hq
+    if (bh >= a.B * a.Hq) return;                     // (whole waves)
     const int b = bh / a.Hq, hq = bh % a.Hq;
     const int hk = hq / G, h = hq % G;
-    merge_head<D, G>(a, b * a.Hkv + hk, bh, h, s_m, s_num, s_den);
+    const float* base = a.partial + ((size_t)(b * a.Hkv + hk) * a.splits * G + h) * (D + 2);
+    const size_t stride = (size_t)G * (D + 2);        // between splits
+    float m = -INFINITY, den = 0.0f, num[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) num[c] = 0.0f;
+    for (int s0 = 0; s0 < a.splits; s0 += CH) {
+        float ms[CH], ls[CH], vs[CH][CPL];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const float* part = base + (size_t)min(s0 + u, a.splits - 1) * stride;
+            const float2 ml = *reinterpret_cast<const float2*>(part + D);
+            ms[u] = ml.x;
+            ls[u] = s0 + u < a.splits ? ml.y : 0.0f;   // past the last split: left out
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) vs[u][c] = part[lane * CPL + c];
+        }
+        float mc = m;
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (ls[u] > 0.0f) mc = fmaxf(mc, ms[u]);
+        if (mc > m) {   // the running sums to the new maximum (from -inf: times 0)
+            const float f = expf(m - mc);
+            den *= f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) num[c] *= f;
+            m = mc;
+        }
+        // (selects, not branches: a load sunk into a branch would be waited
+        // for there, one split after another)
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const bool in = ls[u] > 0.0f;
+            const float w = expf((in ? ms[u] : m) - m);
+            den = in ? fmaf(w, ls[u], den) : den;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) num[c] = in ? fmaf(w, vs[u][c], num[c]) : num[c];
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) a.out[(size_t)bh * D + lane * CPL + c] = den > 0.0f ? num[c] / den : 0.0f;
 }
 
 // Splits [0, split0) go to attn_prompt_kernel: the prompt's splits when every
@@ -1754,7 +1798,8 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
     if (e != hipSuccess || a.fuse_combine) return e;
     {
         Timed t(kKAttnCombine, st);
-        hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((unsigned)(a.B * a.Hq)), dim3(kThreads), 0, st, a);
+        const unsigned heads = (unsigned)(a.B * a.Hq), per = kThreads / 64;
+        hipLaunchKernelGGL((attn_combine_kernel<D, G>), dim3((heads + per - 1) / per), dim3(kThreads), 0, st, a);
         e = hipGetLastError();
     }
     return e;
