@@ -1247,8 +1247,7 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     __shared__ int32_t s_rv[kTPS + 1];
     __shared__ float s_wm[4 * G];
     __shared__ float s_ws[4 * G];
-    __shared__ float s_pa[4 * G * kMaxRank];            // per wave of a half: sum_t p_t A_t[c]
-    __shared__ float s_pz[4 * G * NGR];                 // sum_t p_t zero_t[g]
+    __shared__ float s_tm[kMmWaves * G * 16];           // per wave: sum_t p_t [A_t | zero_t | 1]
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int split = (int)group_id_x(), hk = (int)group_id_y(), b = (int)group_id_z();
@@ -1537,30 +1536,40 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     }
     // (also ends the reads of the K phase's data in the tiles' region)
     lds_barrier();
-    // probabilities; with them the wave's sums of p_t, p_t zero_t[g] and
-    // p_t A_t[c] (V's A rows padded with zeros past the rank) per head
-    const f4v av0 = reinterpret_cast<const f4v*>(s_a + tt * kMaxRank)[0];
-    const f4v av1 = reinterpret_cast<const f4v*>(s_a + tt * kMaxRank)[1];
+    // probabilities
 #pragma unroll
     for (int j = 0; j < GH; ++j) {
         const int h = h0 + j;
         const float m = fmaxf(fmaxf(s_wm[h], s_wm[G + h]), fmaxf(s_wm[2 * G + h], s_wm[3 * G + h]));
         pr[j] = expf(pr[j] - m);
         s_sc[tt * G + h] = pr[j];
-        const float sm = wave_sum(pr[j]);
-        if (lane == 0) s_ws[wh * G + h] = sm;
+    }
+    lds_barrier();
+    // sum_t p_t [A_t | zero_t | 1] per head over the wave's 32 tokens, by
+    // v_mfma_f32_16x16x4_f32 (M = 16 heads, N = 16 terms, K = 4 tokens; exact
+    // fp32 products): lane (li, kb) gives p of head li and term li of token
+    // 4 kb + i of each 16-token piece -- A_t[li] (li < 8, zero past the rank),
+    // zero_t[li - 8], then 1 (the softmax denominator) -- and receives heads
+    // 4 kb + 0..3 of term li.  Before the barrier that hands V's A rows' LDS
+    // to the tiles.
+    constexpr int kTermOne = kMaxRank + NGR;             // the column of 1
+    static_assert(kTermOne < 16, "the terms fit the MFMA's 16 columns");
+    {
+        f32x4 tacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int gi = 0; gi < NGR; ++gi) {
-            const float z = wave_sum(pr[j] * s_gz[tt * NGR + gi]);
-            if (lane == 0) s_pz[(wh * G + h) * NGR + gi] = z;
-        }
+        for (int pcs = 0; pcs < 2; ++pcs)
 #pragma unroll
-        for (int c = 0; c < kMaxRank; ++c) {
-            if (c < r) {   // uniform
-                const float v = wave_sum(pr[j] * (c < 4 ? av0[c & 3] : av1[c & 3]));
-                if (lane == 0) s_pa[(wh * G + h) * kMaxRank + c] = v;
+            for (int i = 0; i < 4; ++i) {
+                const int tok = wv * TPW + pcs * 16 + 4 * kb + i;
+                const float pv = li < G ? s_sc[tok * G + min(li, G - 1)] : 0.0f;
+                const float av = s_a[tok * kMaxRank + min(li, kMaxRank - 1)];
+                const float zv = s_gz[tok * NGR + min(max(li - kMaxRank, 0), NGR - 1)];
+                const float tv = li < kMaxRank ? av : li < kTermOne ? zv : li == kTermOne ? 1.0f : 0.0f;
+                tacc = __builtin_amdgcn_mfma_f32_16x16x4f32(pv, tv, tacc, 0, 0, 0);
             }
-        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * kb + i < G && li <= kTermOne) s_tm[(wv * G + 4 * kb + i) * 16 + li] = tacc[i];
     }
     lds_barrier();
 
@@ -1644,14 +1653,16 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
         __builtin_amdgcn_wave_barrier();
     }
     lds_barrier();   // every wave is done with its tile
-    // the zero-point and low-rank sums over the 4 waves of a half, per head
-    // (into s_qs and s_qb, whose K-side values are no longer read)
-    if (tid < G * NGR) {
-        s_qs[tid] = (s_pz[tid] + s_pz[G * NGR + tid]) + (s_pz[2 * G * NGR + tid] + s_pz[3 * G * NGR + tid]);
-    } else if (tid >= 64 && tid < 64 + G * kMaxRank) {
-        const int hc = tid - 64;
-        constexpr int W = G * kMaxRank;
-        s_qb[hc] = hc % kMaxRank < r ? (s_pa[hc] + s_pa[W + hc]) + (s_pa[2 * W + hc] + s_pa[3 * W + hc]) : 0.0f;
+    // the terms summed over the waves, per head: low-rank into s_qb, zero-point
+    // into s_qs (whose K-side values are no longer read), 1 into s_ws
+    if (tid < G * 16) {
+        const int h = tid / 16, c = tid % 16;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kMmWaves; ++w) v += s_tm[(w * G + h) * 16 + c];
+        if (c < kMaxRank) s_qb[h * kMaxRank + c] = v;
+        else if (c < kTermOne) s_qs[h * NGR + c - kMaxRank] = v;
+        else if (c == kTermOne) s_ws[h] = v;
     }
     // the waves' output rows (heads 4 kb + i, tile column 16 nb + li)
     float* rows = reinterpret_cast<float*>(s_v);
@@ -1668,7 +1679,7 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
     if (tid < G) {
         part[tid * (D + 2) + D] = fmaxf(fmaxf(s_wm[tid], s_wm[G + tid]), fmaxf(s_wm[2 * G + tid], s_wm[3 * G + tid]));
-        part[tid * (D + 2) + D + 1] = s_ws[tid] + s_ws[G + tid] + s_ws[2 * G + tid] + s_ws[3 * G + tid];
+        part[tid * (D + 2) + D + 1] = s_ws[tid];
     }
     for (int i = tid; i < G * D; i += kMmThreads) {
         const int h = i / D, j = i % D;
