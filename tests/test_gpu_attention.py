@@ -47,6 +47,20 @@ def _new_cache(B, Hkv, Hq, d, pp, fp, n_prompt, nb, max_new):
     ("whole_splits_dense_outliers", 1, 2, 2, 128, 512, P(4, 128, 100000, 4, 2)),
     # head_dim 64, two groups per token, no low-rank term
     ("whole_splits_d64_r0", 2, 2, 2, 64, 768, P(4, 32, 20000, 0, 0)),
+    # the matrix-core kernel (2, 4 or 8 query heads per KV head, whole
+    # 256-token splits) at every code width and group count it is built for
+    ("gqa2_whole_4bit", 1, 2, 4, 128, 512, P(4, 128, 20000, 4, 3)),
+    ("gqa2_whole_4bit_g64_r2", 1, 2, 4, 128, 512, P(4, 64, 20000, 2, 2)),
+    ("gqa4_whole_2bit_r8", 1, 2, 8, 128, 512, P(2, 128, 20000, 8, 3)),
+    ("gqa4_whole_2bit_g64", 1, 2, 8, 128, 768, P(2, 64, 20000, 4, 3)),
+    ("gqa4_whole_4bit_r3", 2, 2, 8, 128, 512, P(4, 128, 20000, 3, 3)),
+    # no low-rank term and no outliers: the A, B, column and value arrays are
+    # replaced by stand-in addresses
+    ("gqa4_whole_r0_no_outliers", 1, 2, 8, 128, 512, P(4, 64, 0, 0, 0)),
+    ("gqa8_whole_2bit_g64_r1", 1, 2, 16, 128, 512, P(2, 64, 20000, 1, 2)),
+    ("gqa8_whole_2bit_s0_r8", 1, 2, 16, 128, 512, P(2, 128, 0, 8, 3)),
+    # more outliers in a split than the kernel stages in LDS (read from HBM)
+    ("gqa8_whole_dense_outliers", 1, 2, 16, 128, 512, P(4, 64, 100000, 4, 2)),
 ])
 def test_decode_attention_over_compressed_prompt(name, B, Hkv, Hq, d, n, pp):
     _say(f"[attention] {name}")
