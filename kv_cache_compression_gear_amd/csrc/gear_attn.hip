@@ -800,12 +800,17 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     struct Side {
         f4v gsz, av;
     };
+    // (loads from clamped, always valid addresses -- with r = 0 the matrix's
+    // scales stand in for A -- selected when stored: a load under a divergent
+    // condition would be waited for inside its branch, and the in-order
+    // counter would drain every load issued before it)
     auto load_side = [&](size_t mrow, bool scales) {
-        const int i = tid & 127;
         const float* src = (tid < 128 ? p.scale : p.zero) + mrow * ngr;
+        const f4v* asrc = reinterpret_cast<const f4v*>(r > 0 ? p.A + mrow * r : p.scale + mrow * ngr);
         Side sd;
-        sd.gsz = (scales && tid < 256 && i < ng4) ? reinterpret_cast<const f4v*>(src)[i] : z4;
-        sd.av = tid < na4 ? reinterpret_cast<const f4v*>(p.A + mrow * r)[tid] : z4;
+        const f4v g4 = reinterpret_cast<const f4v*>(src)[min(tid & 127, ng4 - 1)];
+        sd.gsz = scales ? g4 : z4;
+        sd.av = asrc[min(tid, max(na4, 1) - 1)];
         return sd;
     };
     auto store_side = [&](const Side sd) {
@@ -820,16 +825,17 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
         // threads [0, kTPS] read K's row pointers, [256, 256 + kTPS] V's
         const int ri = tid & 255;
         const int32_t rp0 = (tid < 256 ? rpk : rpv)[ri];
-        const int32_t rp1 = ri == 0 ? (tid < 256 ? rpk : rpv)[kTPS] : 0;
+        const int32_t rp1 = (tid < 256 ? rpk : rpv)[kTPS];
         // B_K transposed: thread i takes element [c = i / D][j = i % D] (r D <= 1024)
-        const float* bkm = p.B + (size_t)pc.mk * D * r;
+        const float* bkm = r > 0 ? p.B + (size_t)pc.mk * D * r : p.scale + mrk * ngr;
+        const f4v* bvm = reinterpret_cast<const f4v*>(r > 0 ? p.B + (size_t)pc.mv * D * r : p.scale + mrv * ngr);
         float bkt[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int i = tid + u * kFastThreads;
-            bkt[u] = i < r * D ? bkm[(i % D) * r + i / D] : 0.0f;
+            const int i = min(tid + u * kFastThreads, max(r * D, 1) - 1);
+            bkt[u] = bkm[(i % D) * r + i / D];
         }
-        const f4v bv = tid < nb4 ? reinterpret_cast<const f4v*>(p.B + (size_t)pc.mv * D * r)[tid] : z4;
+        const f4v bv = bvm[min(tid, max(nb4, 1) - 1)];
         store_side(sk);
         int32_t* srp = tid < 256 ? s_rk : s_rv;
         srp[ri] = min(max(rp0, 0), (int)kk);
@@ -847,17 +853,30 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     const int beg_k = s_rk[0], cnt_k = max(s_rk[kTPS] - beg_k, 0);
     const int beg_v = s_rv[0], cnt_v = max(s_rv[kTPS] - beg_v, 0);
     const bool stg_k = cnt_k <= kFastCap, stg_v = cnt_v <= kFastCap;
-    const uint16_t* colk = p.col + (size_t)pc.mk * kk;
-    const uint16_t* valk = p.val + (size_t)pc.mk * kk;
-    const uint16_t* colv = p.col + (size_t)pc.mv * kk;
-    const uint16_t* valv = p.val + (size_t)pc.mv * kk;
+    // (unconditional loads from clamped indices -- with no outliers the row
+    // pointers stand in for the column and value arrays -- all issued before
+    // any is combined, so that they make one round trip, not one each)
+    const uint16_t* rps = reinterpret_cast<const uint16_t*>(p.row_ptr);
+    const uint16_t* colk = kk > 0 ? p.col + (size_t)pc.mk * kk : rps;
+    const uint16_t* valk = kk > 0 ? p.val + (size_t)pc.mk * kk : rps;
+    const uint16_t* colv = kk > 0 ? p.col + (size_t)pc.mv * kk : rps;
+    const uint16_t* valv = kk > 0 ? p.val + (size_t)pc.mv * kk : rps;
+    const int klast = max((int)kk, 1) - 1;
+    // K's entries now (one round trip); V's after the K phase, issued before
+    // V's codes and combined after them, so that only they are waited for
     uint32_t ek[CPT], ev[CPT];
+    auto load_csr = [&](const uint16_t* colm, const uint16_t* valm, int beg, uint32_t (&e)[CPT]) {
+        uint16_t c[CPT], v[CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        const int i = tid + j * kFastThreads;
-        ek[j] = (stg_k && i < cnt_k) ? ((uint32_t)colk[beg_k + i] | ((uint32_t)valk[beg_k + i] << 16)) : 0u;
-        ev[j] = (stg_v && i < cnt_v) ? ((uint32_t)colv[beg_v + i] | ((uint32_t)valv[beg_v + i] << 16)) : 0u;
-    }
+        for (int j = 0; j < CPT; ++j) {
+            const uint32_t off = (uint32_t)min(beg + tid + j * kFastThreads, klast) * 2u;
+            c[j] = ld_at<uint16_t>(colm, off);
+            v[j] = ld_at<uint16_t>(valm, off);
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) e[j] = (uint32_t)c[j] | ((uint32_t)v[j] << 16);
+    };
+    load_csr(colk, valk, beg_k, ek);
 
     // (B_K^T q)[h][c]: 16 lanes per (h, c), 8 columns each, summed over the
     // lane row
@@ -932,14 +951,23 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         if (stg_k && tid + j * kFastThreads < cnt_k) s_cv[tid + j * kFastThreads] = ek[j];
-    // V's codes and side data, consumed after the softmax (issued only now,
-    // so that they hold no registers during the K phase)
+    // V's CSR entries, codes and side data, consumed after the softmax
+    // (issued only now, so that they hold no registers during the K phase)
+    uint16_t vcol[CPT], vval[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        const uint32_t off = (uint32_t)min(beg_v + tid + j * kFastThreads, klast) * 2u;
+        vcol[j] = ld_at<uint16_t>(colv, off);
+        vval[j] = ld_at<uint16_t>(valv, off);
+    }
     uint32_t wvv[SPW];
 #pragma unroll
     for (int s = 0; s < SPW; ++s)
         wvv[s] = BITS == 4 ? ld_at<uint32_t>(cvb, coff0 + s * RPS * ROWB)
                            : (uint32_t)ld_at<uint16_t>(cvb, coff0 + s * RPS * ROWB);
     const Side sv = load_side(mrv, true);
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) ev[j] = (uint32_t)vcol[j] | ((uint32_t)vval[j] << 16);
     __syncthreads();
 
     // ---------------- sparse part (one thread per token, waves 0..3), softmax
