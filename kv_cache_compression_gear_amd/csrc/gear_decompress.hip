@@ -46,7 +46,7 @@ __device__ __forceinline__ float ubyte_f(uint32_t x) {
 // (GEAR's own); 1: groups of p.group tokens of a channel (KIVI keys; scale and
 // zero [rows / group][D]); 2: as 0, on a matrix whose channels were divided
 // by the factors p.chan (ZipCache), multiplied back here.
-template <int D, int RK, int QM>
+template <int D, int RK, int QM, int BITS>
 __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t* out, int64_t m0) {
     constexpr int kSteps = steps_for(RK);
     constexpr int LPR = D / 8, RPS = 64 / LPR;
@@ -71,7 +71,43 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     const int64_t mm = m0 + group_id_x() / blocks_per_mat;
     const int row0 = (int)(group_id_x() % blocks_per_mat) * ROWS_WG;
     const int nrows = min(ROWS_WG, rows - row0);
-    const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
+    const int r = p.rank, gl = p.group / 8, ngr = D / p.group;
+    constexpr int bits = BITS;   // (a template parameter: one load per code word)
+
+    // Every load below is unconditional, from a clamped (always valid)
+    // address: a load under a divergent condition is waited for inside its
+    // branch, and the in-order counter then drains every load issued before
+    // it.  The row pointers and the CSR window go first, the tokens' loads
+    // after them, so that the LDS staging below waits for the former only.
+    //
+    // row pointers of the block: nrows + 1 of them, up to 2 * kThreads - 1
+    // (ROWS_WG <= 256)
+    static_assert(ROWS_WG < 2 * kThreads, "two row pointers per thread at most");
+    const int32_t* rp = p.row_ptr + (size_t)mm * (rows + 1) + row0;
+    const int32_t rpv0 = rp[min(tid, nrows)];
+    const int32_t rpv1 = rp[min(tid + kThreads, nrows)];
+    // the block's CSR entries, guessed before the row pointers arrive: a
+    // window around the block's share of k at a uniform density, 1.5 times
+    // that share plus 128 entries wide (whole multiples of kThreads, at most
+    // kCsrCap).  One round of loads instead of two when it covers the block's
+    // range; otherwise the entries are loaded again below.  (With no outliers
+    // the row pointers stand in for the column and value arrays.)
+    const uint16_t* rps = reinterpret_cast<const uint16_t*>(rp);
+    const uint16_t* cm = p.k > 0 ? p.col + (size_t)mm * p.k : rps;
+    const uint16_t* vm = p.k > 0 ? p.val + (size_t)mm * p.k : rps;
+    constexpr int EPT = kCsrCap / kThreads;   // entries per thread, at most
+    const int share = (int)((int64_t)nrows * p.k / rows);
+    const int wsize = min(kCsrCap, (share * 3 / 2 + 128 + kThreads - 1) / kThreads * kThreads);
+    const int guess = (int)((int64_t)row0 * p.k / rows) - (wsize - share) / 2;
+    const int wbeg = max(min(guess, p.k - wsize), 0);
+    const int klast = max(p.k, 1) - 1;
+    uint16_t wcol[EPT], wval[EPT];   // (combined where they are stored)
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        const uint32_t off = (uint32_t)min(wbeg + tid + j * kThreads, klast) * 2u;
+        wcol[j] = ld_at<uint16_t>(cm, off);
+        wval[j] = ld_at<uint16_t>(vm, off);
+    }
 
     // issue the loads of all the lane's tokens first (clamped rows: always
     // valid addresses)
@@ -114,33 +150,6 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         }
     }
 
-    // row pointers of the block (with the loads above), S tile cleared, B
-    // nrows + 1 pointers, up to 2 * kThreads - 1 of them (ROWS_WG <= 256)
-    static_assert(ROWS_WG < 2 * kThreads, "two row pointers per thread at most");
-    const int32_t* rp = p.row_ptr + (size_t)mm * (rows + 1) + row0;
-    const int32_t rpv0 = tid <= nrows ? rp[tid] : 0;
-    const int32_t rpv1 = tid + kThreads <= nrows ? rp[tid + kThreads] : 0;
-    // the block's CSR entries, guessed before the row pointers arrive: a
-    // window around the block's share of k at a uniform density, 1.5 times
-    // that share plus 128 entries wide (whole multiples of kThreads, at most
-    // kCsrCap).  One round of loads instead of two when it covers the block's
-    // range; otherwise the entries are loaded again below.
-    const uint16_t* cm = p.col + (size_t)mm * p.k;
-    const uint16_t* vm = p.val + (size_t)mm * p.k;
-    constexpr int EPT = kCsrCap / kThreads;   // entries per thread, at most
-    const int share = (int)((int64_t)nrows * p.k / rows);
-    const int wsize = min(kCsrCap, (share * 3 / 2 + 128 + kThreads - 1) / kThreads * kThreads);
-    const int guess = (int)((int64_t)row0 * p.k / rows) - (wsize - share) / 2;
-    const int wbeg = max(min(guess, p.k - wsize), 0);
-    uint32_t went[EPT] = {};
-    if (p.k > 0) {   // workgroup-uniform; indices clamped to valid entries
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            if (j * kThreads >= wsize) break;   // workgroup-uniform
-            const int ic = min(wbeg + tid + j * kThreads, p.k - 1);
-            went[j] = (uint32_t)cm[ic] | ((uint32_t)vm[ic] << 16);
-        }
-    }
     {
         uint4* t4 = reinterpret_cast<uint4*>(s_s);
         for (int i = tid; i < ROWS_WG * D / 8; i += kThreads) t4[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -174,7 +183,8 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
                 const int i = wbeg + tid + j * kThreads - beg;
-                if (j * kThreads < wsize && i >= 0 && i < cnt) s_cv[i] = went[j];
+                if (j * kThreads < wsize && i >= 0 && i < cnt)
+                    s_cv[i] = (uint32_t)wcol[j] | ((uint32_t)wval[j] << 16);
             }
         } else {
             // all of the thread's loads in flight at once
@@ -275,8 +285,12 @@ hipError_t launch_drq(const Packed& p, uint16_t* out, int64_t m0, int64_t m1, hi
     if (blocks <= 0) return hipSuccess;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
     Timed t(kKDecompress, st);
-    hipLaunchKernelGGL((decompress_kernel<D, RK, QM>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
-                       out, m0);
+    if (p.bits == 4)
+        hipLaunchKernelGGL((decompress_kernel<D, RK, QM, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
+                           out, m0);
+    else
+        hipLaunchKernelGGL((decompress_kernel<D, RK, QM, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
+                           out, m0);
     return hipGetLastError();
 }
 
