@@ -133,49 +133,68 @@ __device__ __forceinline__ float sum_rowgroups(float v) {
 constexpr int kAttnCsrCap = 2048;   // outliers of one piece staged in LDS
 constexpr int kAU = 4;              // token steps per batch of loads
 
-// out[b][hq][:] = merge over the pair's splits of (acc, max, sum), by the
-// kThreads threads of a workgroup; the splits are shared out over
-// kThreads / D threads per column.  s_m: kThreads / 64 floats, s_num and s_den:
-// kThreads floats each (LDS).
+// out[b][hq][:] = merge over the pair's splits of (numerators, max, sum), by
+// the kThreads threads of a workgroup: thread (j, q) takes column j of the
+// splits q, q + NQ, ... (NQ = kThreads / D), in chunks of 8 whose loads are
+// issued together (selects, not branches: a load in a branch would be
+// waited for there) and folded into running sums under a running maximum;
+// then the NQ partial results of each column are merged through LDS.
+// s_m, s_num, s_den: kThreads floats each.
 template <int D, int G>
 __device__ __forceinline__ void merge_head(const AttnArgs& a, int pair, int bh, int h, float* s_m,
                                            float* s_num, float* s_den) {
-    constexpr int NQ = kThreads / D;
-    const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
+    constexpr int NQ = kThreads / D, CH = 8;
+    const int tid = thread_id();
     const float* base = a.partial + ((size_t)pair * a.splits * G + h) * (D + 2);
     const size_t stride = (size_t)G * (D + 2);   // between splits
-    float m = -INFINITY;
-    for (int s = tid; s < a.splits; s += kThreads) {
-        const float* part = base + s * stride;
-        if (part[D + 1] > 0.0f) m = fmaxf(m, part[D]);
-    }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if (lane == 0) s_m[wv] = m;
-    __syncthreads();
-    m = s_m[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, s_m[w]);
     const int j = tid % D, q = tid / D;
-    float num = 0.0f, den = 0.0f;
-    for (int s = q; s < a.splits; s += NQ) {
-        const float* part = base + s * stride;
-        const float l = part[D + 1];
-        if (l > 0.0f) {
-            const float w = expf(part[D] - m);
-            num = fmaf(w, part[j], num);
-            den = fmaf(w, l, den);
+    float m = -INFINITY, num = 0.0f, den = 0.0f;
+    for (int s0 = q; s0 < a.splits; s0 += NQ * CH) {
+        float ms[CH], ls[CH], vs[CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int sx = s0 + u * NQ;
+            const float* part = base + (size_t)min(sx, a.splits - 1) * stride;
+            const float2 ml = *reinterpret_cast<const float2*>(part + D);
+            ms[u] = ml.x;
+            ls[u] = sx < a.splits ? ml.y : 0.0f;   // past the last split: left out
+            vs[u] = part[j];
+        }
+        float mc = m;
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (ls[u] > 0.0f) mc = fmaxf(mc, ms[u]);
+        if (mc > m) {   // the running sums to the new maximum (from -inf: times 0)
+            const float f = expf(m - mc);
+            num *= f;
+            den *= f;
+            m = mc;
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const bool in = ls[u] > 0.0f;
+            const float w = expf((in ? ms[u] : m) - m);
+            num = in ? fmaf(w, vs[u], num) : num;
+            den = in ? fmaf(w, ls[u], den) : den;
         }
     }
+    s_m[tid] = m;
     s_num[tid] = num;
     s_den[tid] = den;
     __syncthreads();
     if (q == 0) {
-        for (int qq = 1; qq < NQ; ++qq) {
-            num += s_num[qq * D + j];
-            den += s_den[qq * D + j];
+        float M = m;
+#pragma unroll
+        for (int qq = 1; qq < NQ; ++qq) M = fmaxf(M, s_m[qq * D + j]);
+        float tn = 0.0f, td = 0.0f;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) {
+            const float mq = s_m[qq * D + j];
+            const float f = mq > -INFINITY ? expf(mq - M) : 0.0f;
+            tn = fmaf(f, s_num[qq * D + j], tn);
+            td = fmaf(f, s_den[qq * D + j], td);
         }
-        a.out[(size_t)bh * D + j] = den > 0.0f ? num / den : 0.0f;
+        a.out[(size_t)bh * D + j] = td > 0.0f ? tn / td : 0.0f;
     }
 }
 
@@ -201,7 +220,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     __shared__ uint32_t s_cv[kAttnCsrCap];
     __shared__ __attribute__((aligned(16))) float s_tile[4 * RPS * D];
     __shared__ float s_pa[4 * G * kMaxRank];
-    __shared__ float s_mg[kThreads / 64 + 2 * kThreads];   // merge scratch (fuse_combine)
+    __shared__ float s_mg[3 * kThreads];   // merge scratch (fuse_combine)
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
@@ -397,27 +416,37 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             }
         } else {
             const uint16_t* kb = a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
-            for (int tt = 0; tt < pc.len; tt += TILE) {
-                const int tok = tt + wv * RPS + rl;
-                const bool valid = tok < pc.len;
-                float part[G];
+            // 4 steps' rows loaded together (clamped rows, unconditional: a
+            // load under a divergent condition is waited for at once)
+            for (int tt0 = 0; tt0 < pc.len; tt0 += 4 * TILE) {
+                uint4 wb[4];
 #pragma unroll
-                for (int h = 0; h < G; ++h) part[h] = 0.0f;
-                if (valid) {
-                    const uint4 w = *reinterpret_cast<const uint4*>(kb + (size_t)(pc.row0 + tok) * D + colq * 8);
-                    const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+                for (int u = 0; u < 4; ++u) {
+                    const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
+                    wb[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int tt = tt0 + u * TILE;
+                    if (tt >= pc.len) break;   // workgroup-uniform
+                    const int tok = tt + wv * RPS + rl;
+                    const bool valid = tok < pc.len;
+                    float part[G];
+#pragma unroll
+                    for (int h = 0; h < G; ++h) part[h] = 0.0f;
+                    const uint32_t w4[4] = {wb[u].x, wb[u].y, wb[u].z, wb[u].w};
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        const float kv = h2f(w4[e >> 1] >> (16 * (e & 1)));
+                        const float kv = valid ? h2f(w4[e >> 1] >> (16 * (e & 1))) : 0.0f;
 #pragma unroll
                         for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], kv, part[h]);
                     }
-                }
 #pragma unroll
-                for (int h = 0; h < G; ++h) part[h] = row_allreduce<LPR>(part[h]);
-                if (valid && colq == 0) {
+                    for (int h = 0; h < G; ++h) part[h] = row_allreduce<LPR>(part[h]);
+                    if (valid && colq == 0) {
 #pragma unroll
-                    for (int h = 0; h < G; ++h) s_sc[(base + tok) * G + h] = part[h];
+                        for (int h = 0; h < G; ++h) s_sc[(base + tok) * G + h] = part[h];
+                    }
                 }
             }
         }
@@ -601,19 +630,31 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             }
         } else {
             const uint16_t* vb = a.buf + (((size_t)(1 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
-            for (int tt = 0; tt < pc.len; tt += TILE) {
-                const int tok = tt + wv * RPS + rl;
-                if (tok >= pc.len) continue;
-                float pr[G];
+            // 4 steps' rows loaded together, as for K
+            for (int tt0 = 0; tt0 < pc.len; tt0 += 4 * TILE) {
+                uint4 wb[4];
 #pragma unroll
-                for (int h = 0; h < G; ++h) pr[h] = s_sc[(base + tok) * G + h];
-                const uint4 w = *reinterpret_cast<const uint4*>(vb + (size_t)(pc.row0 + tok) * D + colq * 8);
-                const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+                for (int u = 0; u < 4; ++u) {
+                    const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
+                    wb[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float vv = h2f(w4[e >> 1] >> (16 * (e & 1)));
+                for (int u = 0; u < 4; ++u) {
+                    // rows past the piece weigh 0 (selects: a branch here
+                    // would take the load into it)
+                    const int tok = tt0 + u * TILE + wv * RPS + rl;
+                    const bool valid = tok < pc.len;
+                    const int tc = min(tok, pc.len - 1);
+                    float pr[G];
 #pragma unroll
-                    for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pr[h], vv, acc[h][e]);
+                    for (int h = 0; h < G; ++h) pr[h] = valid ? s_sc[(base + tc) * G + h] : 0.0f;
+                    const uint32_t w4[4] = {wb[u].x, wb[u].y, wb[u].z, wb[u].w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float vv = h2f(w4[e >> 1] >> (16 * (e & 1)));
+#pragma unroll
+                        for (int h = 0; h < G; ++h) acc[h][e] = fmaf(pr[h], vv, acc[h][e]);
+                    }
                 }
             }
         }
@@ -650,7 +691,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         // by this workgroup (visible to it after the barrier)
         __syncthreads();
         float* s_m = s_mg;
-        float* s_num = s_mg + kThreads / 64;
+        float* s_num = s_mg + kThreads;
         float* s_den = s_num + kThreads;
 #pragma unroll 1
         for (int h = 0; h < G; ++h) {
