@@ -109,6 +109,19 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         wval[j] = ld_at<uint16_t>(vm, off);
     }
 
+    // B (D x r), one element per slot of B's padded rows, from a clamped
+    // column: issued with the first round so that staging it does not wait
+    // for the tokens' loads
+    constexpr int BPT = (D * RKX + kThreads - 1) / kThreads;
+    const int rl1 = max(r, 1) - 1;
+    const float* bsrc = RK > 0 ? p.B + (size_t)mm * D * r : p.scale;
+    float bv[BPT];
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) {
+        const int i = min(tid + u * kThreads, D * RKX - 1);
+        bv[u] = RK > 0 ? ld_at<float>(bsrc, (uint32_t)((i / RKX) * r + min(i % RKX, rl1)) * 4u) : 0.0f;
+    }
+
     // issue the loads of all the lane's tokens first (clamped rows: always
     // valid addresses)
     const size_t mrow = (size_t)mm * rows + row0;
@@ -129,36 +142,26 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
             sc[s] = ld_at<float>(sbase, go);
             zp[s] = ld_at<float>(zbase, go);
         }
-        if (RK > 0 && r == RK) {            // the A row as one or two vector loads
-            if (RK >= 4) {
+        // the A row, one load per slot from a clamped column (no branch on
+        // the rank: a load in a branch, or the join after it, is waited for
+        // there); slots past the rank repeat column r - 1 and meet the zero
+        // padding of B
 #pragma unroll
-                for (int c4 = 0; c4 < RKX / 4; ++c4) {
-                    const float4 a4 = ld_at<float4>(abase, (tk * RK + 4 * c4) * 4);
-                    ar[s][(4 * c4) % RKX] = a4.x;
-                    ar[s][(4 * c4 + 1) % RKX] = a4.y;
-                    ar[s][(4 * c4 + 2) % RKX] = a4.z;
-                    ar[s][(4 * c4 + 3) % RKX] = a4.w;
-                }
-            } else {
-                const float2 a2 = ld_at<float2>(abase, tk * RK * 4);
-                ar[s][0] = a2.x;
-                ar[s][1 % RKX] = a2.y;
-            }
-        } else {
-#pragma unroll
-            for (int c = 0; c < RKX; ++c) ar[s][c] = (RK > 0 && c < r) ? ld_at<float>(abase, (tk * r + c) * 4) : 0.0f;
-        }
+        for (int c = 0; c < RKX; ++c)
+            ar[s][c] = RK > 0 ? ld_at<float>(abase, (tk * r + (uint32_t)min(c, rl1)) * 4) : 0.0f;
     }
 
     {
         uint4* t4 = reinterpret_cast<uint4*>(s_s);
         for (int i = tid; i < ROWS_WG * D / 8; i += kThreads) t4[i] = make_uint4(0u, 0u, 0u, 0u);
     }
-    if (RK > 0)
-        for (int i = tid; i < D * RKX; i += kThreads) {
-            const int j = i / RKX, c = i % RKX;
-            s_b[((j % 8) * LPR + j / 8) * RKX + c] = c < r ? p.B[((size_t)mm * D + j) * r + c] : 0.0f;
+    if (RK > 0) {
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = tid + u * kThreads, j = i / RKX, c = i % RKX;
+            if (i < D * RKX) s_b[((j % 8) * LPR + j / 8) * RKX + c] = c < r ? bv[u] : 0.0f;
         }
+    }
     if (tid <= nrows) s_rp[tid] = min(max(rpv0, 0), p.k);
     if (tid + kThreads <= nrows) s_rp[tid + kThreads] = min(max(rpv1, 0), p.k);
     if constexpr (QM == 1) {
