@@ -133,68 +133,94 @@ __device__ __forceinline__ float sum_rowgroups(float v) {
 constexpr int kAttnCsrCap = 2048;   // outliers of one piece staged in LDS
 constexpr int kAU = 4;              // token steps per batch of loads
 
-// out[b][hq][:] = merge over the pair's splits of (numerators, max, sum), by
-// the kThreads threads of a workgroup: thread (j, q) takes column j of the
-// splits q, q + NQ, ... (NQ = kThreads / D), in chunks of 8 whose loads are
-// issued together (selects, not branches: a load in a branch would be
-// waited for there) and folded into running sums under a running maximum;
-// then the NQ partial results of each column are merged through LDS.
-// s_m, s_num, s_den: kThreads floats each.
+// out[b][hk G + h][:] for every query head h of the pair = merge over the
+// pair's splits of (numerators, max, sum), all G heads at once, by the
+// kThreads threads of a workgroup.  The G D columns (c = h D + j) are taken W
+// at a time: thread (c0, q) takes columns c0, c0 + W, ... of the splits
+// q, q + NQ, ... (NQ threads per column when G D < kThreads), in chunks of 8
+// splits whose loads are issued together (selects, not branches: a load in a
+// branch would be waited for there) and folded into running sums under a
+// running maximum; with NQ > 1 the partial results of a column are merged
+// through LDS.  s_m, s_num, s_den: kThreads floats each.
 template <int D, int G>
-__device__ __forceinline__ void merge_head(const AttnArgs& a, int pair, int bh, int h, float* s_m,
+__device__ __forceinline__ void merge_pair(const AttnArgs& a, int pair, int b, int hk, float* s_m,
                                            float* s_num, float* s_den) {
-    constexpr int NQ = kThreads / D, CH = 8;
+    constexpr int C = G * D, W = C < kThreads ? C : kThreads;
+    constexpr int NQ = kThreads / W, CPT = C / W, CH = CPT >= 4 ? 4 : 8;
+    static_assert(kThreads % W == 0 && C % W == 0, "thread mapping of the merge");
     const int tid = thread_id();
-    const float* base = a.partial + ((size_t)pair * a.splits * G + h) * (D + 2);
+    const int c0 = tid % W, q = tid / W;
+    const float* base = a.partial + (size_t)pair * a.splits * G * (D + 2);
     const size_t stride = (size_t)G * (D + 2);   // between splits
-    const int j = tid % D, q = tid / D;
-    float m = -INFINITY, num = 0.0f, den = 0.0f;
+    int off[CPT], offml[CPT];
+    float m[CPT], num[CPT], den[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = c0 + i * W, h = c / D;
+        off[i] = h * (D + 2) + c % D;
+        offml[i] = h * (D + 2) + D;
+        m[i] = -INFINITY;
+        num[i] = 0.0f;
+        den[i] = 0.0f;
+    }
     for (int s0 = q; s0 < a.splits; s0 += NQ * CH) {
-        float ms[CH], ls[CH], vs[CH];
+        float ms[CPT][CH], ls[CPT][CH], vs[CPT][CH];
 #pragma unroll
         for (int u = 0; u < CH; ++u) {
             const int sx = s0 + u * NQ;
             const float* part = base + (size_t)min(sx, a.splits - 1) * stride;
-            const float2 ml = *reinterpret_cast<const float2*>(part + D);
-            ms[u] = ml.x;
-            ls[u] = sx < a.splits ? ml.y : 0.0f;   // past the last split: left out
-            vs[u] = part[j];
-        }
-        float mc = m;
 #pragma unroll
-        for (int u = 0; u < CH; ++u)
-            if (ls[u] > 0.0f) mc = fmaxf(mc, ms[u]);
-        if (mc > m) {   // the running sums to the new maximum (from -inf: times 0)
-            const float f = expf(m - mc);
-            num *= f;
-            den *= f;
-            m = mc;
+            for (int i = 0; i < CPT; ++i) {
+                const float2 ml = *reinterpret_cast<const float2*>(part + offml[i]);
+                ms[i][u] = ml.x;
+                ls[i][u] = sx < a.splits ? ml.y : 0.0f;   // past the last split: left out
+                vs[i][u] = part[off[i]];
+            }
         }
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const bool in = ls[u] > 0.0f;
-            const float w = expf((in ? ms[u] : m) - m);
-            num = in ? fmaf(w, vs[u], num) : num;
-            den = in ? fmaf(w, ls[u], den) : den;
+        for (int i = 0; i < CPT; ++i) {
+            float mc = m[i];
+#pragma unroll
+            for (int u = 0; u < CH; ++u)
+                if (ls[i][u] > 0.0f) mc = fmaxf(mc, ms[i][u]);
+            if (mc > m[i]) {   // the running sums to the new maximum (from -inf: times 0)
+                const float f = expf(m[i] - mc);
+                num[i] *= f;
+                den[i] *= f;
+                m[i] = mc;
+            }
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                const bool in = ls[i][u] > 0.0f;
+                const float w = expf((in ? ms[i][u] : m[i]) - m[i]);
+                num[i] = in ? fmaf(w, vs[i][u], num[i]) : num[i];
+                den[i] = in ? fmaf(w, ls[i][u], den[i]) : den[i];
+            }
         }
     }
-    s_m[tid] = m;
-    s_num[tid] = num;
-    s_den[tid] = den;
-    __syncthreads();
-    if (q == 0) {
-        float M = m;
+    float* out = a.out + ((size_t)b * a.Hq + (size_t)hk * G) * D;   // the pair's G heads, contiguous
+    if constexpr (NQ == 1) {
 #pragma unroll
-        for (int qq = 1; qq < NQ; ++qq) M = fmaxf(M, s_m[qq * D + j]);
-        float tn = 0.0f, td = 0.0f;
+        for (int i = 0; i < CPT; ++i) out[c0 + i * W] = den[i] > 0.0f ? num[i] / den[i] : 0.0f;
+    } else {
+        s_m[tid] = m[0];
+        s_num[tid] = num[0];
+        s_den[tid] = den[0];
+        __syncthreads();
+        if (q == 0) {
+            float M = m[0];
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) {
-            const float mq = s_m[qq * D + j];
-            const float f = mq > -INFINITY ? expf(mq - M) : 0.0f;
-            tn = fmaf(f, s_num[qq * D + j], tn);
-            td = fmaf(f, s_den[qq * D + j], td);
+            for (int qq = 1; qq < NQ; ++qq) M = fmaxf(M, s_m[qq * W + c0]);
+            float tn = 0.0f, td = 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < NQ; ++qq) {
+                const float mq = s_m[qq * W + c0];
+                const float f = mq > -INFINITY ? expf(mq - M) : 0.0f;
+                tn = fmaf(f, s_num[qq * W + c0], tn);
+                td = fmaf(f, s_den[qq * W + c0], td);
+            }
+            out[c0] = td > 0.0f ? tn / td : 0.0f;
         }
-        a.out[(size_t)bh * D + j] = td > 0.0f ? tn / td : 0.0f;
     }
 }
 
@@ -207,7 +233,7 @@ __device__ __forceinline__ void merge_head(const AttnArgs& a, int pair, int bh, 
 // sparse V entries into its dequantised values through a small per-wave LDS
 // tile that is scattered, read and cleared again.  When a pair has only one
 // split here (fuse_combine), its workgroup then merges all of the pair's
-// splits into out itself (no separate combine launch).
+// splits into out itself, for all of its query heads (no combine launch).
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TILE = 4 * RPS;
@@ -221,6 +247,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) float s_tile[4 * RPS * D];
     __shared__ float s_pa[4 * G * kMaxRank];
     __shared__ float s_mg[3 * kThreads];   // merge scratch (fuse_combine)
+    __shared__ __attribute__((aligned(16))) float s_bm[D * kMaxRank];   // B of the piece's matrix, [j][c]
 
     const int tid = thread_id(), lane = tid & 63, wv = wave_id(tid);
     const int colq = lane % LPR, rl = lane / LPR;
@@ -249,33 +276,70 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         }
     }
 
-    // CSR rows [row0, row0 + len) of matrix m of p into s_rp / s_cv; an entry
-    // is packed as column (bits 0-6) | row in the piece (bits 7-15) | fp16
-    // value (bits 16-31).
+    // The LDS staging of one compressed matrix's piece (rows [row0, row0 +
+    // len) of matrix m of p): its row pointers into s_rp, its CSR entries (one
+    // contiguous range, whose ends are read first, as scalars) into s_cv as
+    // column | fp16 value << 16, and B into s_bm padded to kMaxRank columns
+    // with zeros.  stage_issue issues every load of it unconditionally, from
+    // clamped addresses (a load in a branch is waited for there), into
+    // registers; the caller then issues its first tokens' loads, and
+    // stage_store waits for the staging loads only (issued first) and stores.
+    constexpr int SCPT = kAttnCsrCap / kThreads;                // CSR entries per thread
+    constexpr int BPT = (D * kMaxRank + kThreads - 1) / kThreads;   // B slots per thread
     int csr_beg = 0, csr_cnt = 0;
     bool csr_staged = true;
-    auto stage_csr = [&](const Packed& p, int64_t m, int row0, int len) {
-        __syncthreads();
+    int32_t st_rp0 = 0, st_rp1 = 0;
+    uint16_t st_col[SCPT], st_val[SCPT];
+    float st_b[BPT];
+    auto stage_issue = [&](const Packed& p, int64_t m, int row0, int len) {
         const int32_t* rp = p.row_ptr + (size_t)m * (p.rows + 1) + row0;
-        for (int i = tid; i <= len; i += kThreads) s_rp[i] = min(max(rp[i], 0), p.k);
-        __syncthreads();
-        csr_beg = __builtin_amdgcn_readfirstlane(s_rp[0]);
-        csr_cnt = max(__builtin_amdgcn_readfirstlane(s_rp[len]) - csr_beg, 0);
+        const int kk = p.k;
+        csr_beg = min(max(rp[0], 0), kk);
+        csr_cnt = max(min(max(rp[len], 0), kk) - csr_beg, 0);
         csr_staged = csr_cnt <= kAttnCsrCap;
-        if (csr_staged) {
-            const uint16_t* cm = p.col + (size_t)m * p.k;
-            const uint16_t* vm = p.val + (size_t)m * p.k;
-            for (int i = tid; i < len; i += kThreads)
-                for (int k = s_rp[i]; k < s_rp[i + 1]; ++k)
-                    s_cv[k - csr_beg] = ((uint32_t)cm[k] & (D - 1)) | ((uint32_t)i << 7) |
-                                        ((uint32_t)vm[k] << 16);
+        st_rp0 = ld_at<int32_t>(rp, (uint32_t)min(tid, len) * 4u);
+        st_rp1 = ld_at<int32_t>(rp, (uint32_t)min(tid + kThreads, len) * 4u);
+        // (with no outliers the row pointers stand in for the CSR arrays)
+        const uint16_t* cm = kk > 0 ? p.col + (size_t)m * kk : reinterpret_cast<const uint16_t*>(rp);
+        const uint16_t* vm = kk > 0 ? p.val + (size_t)m * kk : reinterpret_cast<const uint16_t*>(rp);
+        const int klast = max(kk, 1) - 1;
+#pragma unroll
+        for (int j = 0; j < SCPT; ++j) {
+            const uint32_t off = (uint32_t)min(csr_beg + tid + j * kThreads, klast) * 2u;
+            st_col[j] = ld_at<uint16_t>(cm, off);
+            st_val[j] = ld_at<uint16_t>(vm, off);
+        }
+        // (with r = 0 the scales stand in for B)
+        const int r = p.rank, rl1 = max(r, 1) - 1;
+        const float* bsrc = r > 0 ? p.B + (size_t)m * D * r : p.scale;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = min(tid + u * kThreads, D * kMaxRank - 1);
+            st_b[u] = ld_at<float>(bsrc, (uint32_t)((i / kMaxRank) * r + min(i % kMaxRank, rl1)) * 4u);
         }
     };
-    // entry k (absolute index) of row `row` of the piece
-    auto csr_entry = [&](const Packed& p, int64_t m, int k, int row) -> uint32_t {
+    auto stage_store = [&](const Packed& p, int len) {
+        __syncthreads();   // the previous piece's reads of the staging arrays
+        if (tid <= len) s_rp[tid] = min(max(st_rp0, 0), p.k);
+        if (tid + kThreads <= len) s_rp[tid + kThreads] = min(max(st_rp1, 0), p.k);
+        if (csr_staged) {
+#pragma unroll
+            for (int j = 0; j < SCPT; ++j) {
+                const int i = tid + j * kThreads;
+                if (i < csr_cnt) s_cv[i] = ((uint32_t)st_col[j] & (D - 1)) | ((uint32_t)st_val[j] << 16);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = tid + u * kThreads;
+            if (i < D * kMaxRank) s_bm[i] = (i % kMaxRank) < p.rank ? st_b[u] : 0.0f;
+        }
+        __syncthreads();
+    };
+    // entry k (absolute index) of the piece: column | fp16 value << 16
+    auto csr_entry = [&](const Packed& p, int64_t m, int k) -> uint32_t {
         if (csr_staged) return s_cv[k - csr_beg];
-        return ((uint32_t)p.col[(size_t)m * p.k + k] & (D - 1)) | ((uint32_t)row << 7) |
-               ((uint32_t)p.val[(size_t)m * p.k + k] << 16);
+        return ((uint32_t)p.col[(size_t)m * p.k + k] & (D - 1)) | ((uint32_t)p.val[(size_t)m * p.k + k] << 16);
     };
 
     // ---------------- phase 1: raw scores q . K^_t of the split's tokens
@@ -297,7 +361,42 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qsf[h] = fmaf(q[h][e], fk[e], qsf[h]);
             }
-            stage_csr(p, pc.mk, pc.row0, pc.len);
+            const size_t mrow = (size_t)pc.mk * p.rows + pc.row0;
+            const int steps = (pc.len + TILE - 1) / TILE;
+            uint32_t word[1][kAU];
+            float sc[1][kAU], zp[1][kAU], av[1][kAU];   // av: A[t][colq] for colq < r
+            // per-piece bases (uniform); lanes use 32-bit offsets and a clamped
+            // token (always a valid address), then zero what lies past the piece
+            const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
+            const float* sbase = p.scale + mrow * ngr;
+            const float* zbase = p.zero + mrow * ngr;
+            const float* abase = r > 0 ? p.A + mrow * r : sbase;
+            const int acol = min(colq, max(r - 1, 0));
+            auto load = [&](int bf, int s0) {
+#pragma unroll
+                for (int u = 0; u < kAU; ++u) {
+                    const int tok = (s0 + u) * TILE + wv * RPS + rl;
+                    const bool ok = tok < pc.len;
+                    const uint32_t tk = (uint32_t)min(tok, pc.len - 1);
+                    // the lane's code word as two 16-bit loads at either width
+                    // (no branch on the width: its join would wait for every load)
+                    const uint32_t co = bits == 4 ? tk * (D / 2) + colq * 4 : tk * (D / 4) + colq * 2;
+                    const uint32_t wlo = ld_at<uint16_t>(cbase, co);
+                    const uint32_t whi = ld_at<uint16_t>(cbase, bits == 4 ? co + 2 : co);
+                    const uint32_t w = bits == 4 ? wlo | (whi << 16) : wlo;
+                    const uint32_t go = (tk * ngr + colq / gl) * 4;
+                    const float scv = ld_at<float>(sbase, go);
+                    const float zpv = ld_at<float>(zbase, go);
+                    const float a1 = ld_at<float>(abase, (r > 0 ? tk * r + acol : 0) * 4);
+                    word[bf][u] = ok ? w : 0u;
+                    sc[bf][u] = ok ? scv : 0.0f;
+                    zp[bf][u] = ok ? zpv : 0.0f;
+                    av[bf][u] = (ok && colq < r) ? a1 : 0.0f;
+                }
+            };
+            stage_issue(p, pc.mk, pc.row0, pc.len);
+            load(0, 0);
+            stage_store(p, pc.len);
             if (r > 0 && wv == 0) {
                 // B^T q: one token row of lanes spans all D columns
                 for (int c = 0; c < r; ++c) {
@@ -307,7 +406,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     if (rl == 0) {
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float bv = p.B[((size_t)pc.mk * D + colq * 8 + e) * r + c] * fk[e];
+                            const float bv = s_bm[(colq * 8 + e) * kMaxRank + c] * fk[e];
 #pragma unroll
                             for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], bv, part[h]);
                         }
@@ -323,36 +422,6 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             float qbl[G];   // (B^T q)[colq] for colq < r
 #pragma unroll
             for (int h = 0; h < G; ++h) qbl[h] = colq < r ? s_qb[h * kMaxRank + colq] : 0.0f;
-            const size_t mrow = (size_t)pc.mk * p.rows + pc.row0;
-            const int steps = (pc.len + TILE - 1) / TILE;
-            uint32_t word[1][kAU];
-            float sc[1][kAU], zp[1][kAU], av[1][kAU];   // av: A[t][colq] for colq < r
-            // per-piece bases (uniform); lanes use 32-bit offsets and a clamped
-            // token (always a valid address), then zero what lies past the piece
-            const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
-            const float* sbase = p.scale + mrow * ngr;
-            const float* zbase = p.zero + mrow * ngr;
-            const float* abase = p.A + mrow * r;
-            const int acol = min(colq, max(r - 1, 0));
-            auto load = [&](int bf, int s0) {
-#pragma unroll
-                for (int u = 0; u < kAU; ++u) {
-                    const int tok = (s0 + u) * TILE + wv * RPS + rl;
-                    const bool ok = tok < pc.len;
-                    const uint32_t tk = (uint32_t)min(tok, pc.len - 1);
-                    const uint32_t w = bits == 4
-                        ? ld_at<uint32_t>(cbase, tk * (D / 2) + colq * 4)
-                        : (uint32_t)ld_at<uint16_t>(cbase, tk * (D / 4) + colq * 2);
-                    const uint32_t go = (tk * ngr + colq / gl) * 4;
-                    const float scv = ld_at<float>(sbase, go);
-                    const float zpv = ld_at<float>(zbase, go);
-                    const float a1 = r > 0 ? ld_at<float>(abase, (tk * r + acol) * 4) : 0.0f;
-                    word[bf][u] = ok ? w : 0u;
-                    sc[bf][u] = ok ? scv : 0.0f;
-                    zp[bf][u] = ok ? zpv : 0.0f;
-                    av[bf][u] = (ok && colq < r) ? a1 : 0.0f;
-                }
-            };
             auto compute = [&](int bf, int s0) {
 #pragma unroll
                 for (int u = 0; u < kAU; ++u) {
@@ -395,7 +464,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 }
             };
             for (int s0 = 0; s0 < steps; s0 += kAU) {
-                load(0, s0);
+                if (s0 > 0) load(0, s0);
                 compute(0, s0);
             }
             __syncthreads();
@@ -405,7 +474,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) add[h] = 0.0f;
                 for (int k = s_rp[i]; k < s_rp[i + 1]; ++k) {
-                    const uint32_t cv = csr_entry(p, pc.mk, k, i);
+                    const uint32_t cv = csr_entry(p, pc.mk, k);
                     const int cj = (int)(cv & (D - 1));
                     const float v = h2f(cv >> 16) * (p.chan ? p.chan[(size_t)pc.mk * D + cj] : 1.0f);
 #pragma unroll
@@ -516,8 +585,6 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             const Packed& p = pc.p;
             const int r = p.rank, bits = p.bits, gl = p.group / 8, ngr = D / p.group;
             const uint32_t cmask = (1u << bits) - 1u;
-            stage_csr(p, pc.mv, pc.row0, pc.len);
-            __syncthreads();
             float fv[8];   // ZipCache: the value matrix's factors of the lane's columns
 #pragma unroll
             for (int e = 0; e < 8; ++e) fv[e] = p.chan ? p.chan[(size_t)pc.mv * D + colq * 8 + e] : 1.0f;
@@ -533,7 +600,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
             const float* sbase = p.scale + mrow * ngr;
             const float* zbase = p.zero + mrow * ngr;
-            const float* abase = p.A + mrow * r;
+            const float* abase = r > 0 ? p.A + mrow * r : sbase;
             const int acol = min(colq, max(r - 1, 0));
             auto load = [&](int bf, int s0) {
 #pragma unroll
@@ -541,19 +608,25 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     const int tok = (s0 + u) * TILE + wv * RPS + rl;
                     const bool ok = tok < pc.len;
                     const uint32_t tk = (uint32_t)min(tok, pc.len - 1);
-                    const uint32_t w = bits == 4
-                        ? ld_at<uint32_t>(cbase, tk * (D / 2) + colq * 4)
-                        : (uint32_t)ld_at<uint16_t>(cbase, tk * (D / 4) + colq * 2);
+                    // the lane's code word as two 16-bit loads at either width
+                    // (no branch on the width: its join would wait for every load)
+                    const uint32_t co = bits == 4 ? tk * (D / 2) + colq * 4 : tk * (D / 4) + colq * 2;
+                    const uint32_t wlo = ld_at<uint16_t>(cbase, co);
+                    const uint32_t whi = ld_at<uint16_t>(cbase, bits == 4 ? co + 2 : co);
+                    const uint32_t w = bits == 4 ? wlo | (whi << 16) : wlo;
                     const uint32_t go = (tk * ngr + colq / gl) * 4;
                     const float scv = ld_at<float>(sbase, go);
                     const float zpv = ld_at<float>(zbase, go);
-                    const float a1 = r > 0 ? ld_at<float>(abase, (tk * r + acol) * 4) : 0.0f;
+                    const float a1 = ld_at<float>(abase, (r > 0 ? tk * r + acol : 0) * 4);
                     word[bf][u] = ok ? w : 0u;
                     sc[bf][u] = ok ? scv : 0.0f;
                     zp[bf][u] = ok ? zpv : 0.0f;
                     av[bf][u] = (ok && colq < r) ? a1 : 0.0f;
                 }
             };
+            stage_issue(p, pc.mv, pc.row0, pc.len);
+            load(0, 0);
+            stage_store(p, pc.len);
             auto compute = [&](int bf, int s0) {
 #pragma unroll
                 for (int u = 0; u < kAU; ++u) {
@@ -566,12 +639,20 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     const int last = min(first + RPS, pc.len);
                     const int e0 = first < pc.len ? s_rp[first] : 0;
                     const int e1 = first < pc.len ? s_rp[last] : 0;
-                    for (int k = e0 + lane; k < e1; k += 64) {
+                    // the first entries of the step's rows 1 .. RPS - 1 (an entry's
+                    // row in the step: how many of them it reaches)
+                    int rs[RPS - 1];
+#pragma unroll
+                    for (int i = 1; i < RPS; ++i) rs[i - 1] = first + i <= last ? s_rp[first + i] : 0x7fffffff;
+                    auto row_of = [&](int k) {
                         int rr = 0;
-                        if (!csr_staged)
-                            while (rr + 1 < RPS && first + rr + 1 <= last && k >= s_rp[first + rr + 1]) ++rr;
-                        const uint32_t cv = csr_entry(p, pc.mv, k, first + rr);
-                        tile[(((cv >> 7) & 0x1ffu) - first) * D + (cv & (D - 1))] = h2f(cv >> 16);
+#pragma unroll
+                        for (int i = 0; i < RPS - 1; ++i) rr += k >= rs[i] ? 1 : 0;
+                        return rr;
+                    };
+                    for (int k = e0 + lane; k < e1; k += 64) {
+                        const uint32_t cv = csr_entry(p, pc.mv, k);
+                        tile[row_of(k) * D + (cv & (D - 1))] = h2f(cv >> 16);
                     }
                     __builtin_amdgcn_wave_barrier();
                     const float4 s0v = *reinterpret_cast<const float4*>(tile + rl * D + colq * 8);
@@ -579,11 +660,8 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     const float sv[8] = {s0v.x, s0v.y, s0v.z, s0v.w, s1v.x, s1v.y, s1v.z, s1v.w};
                     __builtin_amdgcn_wave_barrier();
                     for (int k = e0 + lane; k < e1; k += 64) {
-                        int rr = 0;
-                        if (!csr_staged)
-                            while (rr + 1 < RPS && first + rr + 1 <= last && k >= s_rp[first + rr + 1]) ++rr;
-                        const uint32_t cv = csr_entry(p, pc.mv, k, first + rr);
-                        tile[(((cv >> 7) & 0x1ffu) - first) * D + (cv & (D - 1))] = 0.0f;
+                        const uint32_t cv = csr_entry(p, pc.mv, k);
+                        tile[row_of(k) * D + (cv & (D - 1))] = 0.0f;
                     }
                     float pr[G];
 #pragma unroll
@@ -600,7 +678,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 }
             };
             for (int s0 = 0; s0 < steps; s0 += kAU) {
-                load(0, s0);
+                if (s0 > 0) load(0, s0);
                 compute(0, s0);
             }
             // low-rank part of this matrix: acc += B (sum_t p_t A_t), with the
@@ -623,7 +701,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                              s_pa[(2 * G + h) * kMaxRank + c] + s_pa[(3 * G + h) * kMaxRank + c];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float bv = p.B[((size_t)pc.mv * D + colq * 8 + e) * r + c] * fv[e];
+                    const float bv = s_bm[(colq * 8 + e) * kMaxRank + c] * fv[e];
 #pragma unroll
                     for (int h = 0; h < G; ++h) acc[h][e] = fmaf(tot[h], bv, acc[h][e]);
                 }
@@ -690,14 +768,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         // prompt kernel, launched before on the same stream, and this one's
         // by this workgroup (visible to it after the barrier)
         __syncthreads();
-        float* s_m = s_mg;
-        float* s_num = s_mg + kThreads;
-        float* s_den = s_num + kThreads;
-#pragma unroll 1
-        for (int h = 0; h < G; ++h) {
-            merge_head<D, G>(a, pair, b * a.Hq + hk * G + h, h, s_m, s_num, s_den);
-            __syncthreads();
-        }
+        merge_pair<D, G>(a, pair, b, hk, s_mg, s_mg + kThreads, s_mg + 2 * kThreads);
     }
 }
 
@@ -1835,10 +1906,9 @@ hipError_t launch_dg(const AttnArgs& a0, hipStream_t st) {
         D / a.prompt.p.group <= kFastGroups)
         a.split0 = min(a.splits, a.prompt.chunks * a.prompt.p.rows / kTPS);
     const unsigned pairs = (unsigned)(a.B * a.Hkv);
-    // one split of attn_split_kernel per pair and one query head per KV head:
-    // that workgroup also merges (with more heads it would merge them one
-    // after another, slower than the combine kernel's workgroup per head)
-    a.fuse_combine = (G == 1 && a.splits - a.split0 == 1) ? 1 : 0;
+    // one split of attn_split_kernel per pair: that workgroup also merges the
+    // pair's splits for all of its query heads (no combine launch)
+    a.fuse_combine = (a.splits - a.split0 == 1) ? 1 : 0;
     hipError_t e;
     {
         Timed t(kKAttnSplit, st);
