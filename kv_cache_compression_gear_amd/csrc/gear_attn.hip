@@ -302,10 +302,12 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         // (with no outliers the row pointers stand in for the CSR arrays)
         const uint16_t* cm = kk > 0 ? p.col + (size_t)m * kk : reinterpret_cast<const uint16_t*>(rp);
         const uint16_t* vm = kk > 0 ? p.val + (size_t)m * kk : reinterpret_cast<const uint16_t*>(rp);
-        const int klast = max(kk, 1) - 1;
+        // (clamped to the range's last entry: slots past the range re-read it,
+        // no further bytes)
+        const int elast = min(csr_beg + max(csr_cnt, 1) - 1, max(kk, 1) - 1);
 #pragma unroll
         for (int j = 0; j < SCPT; ++j) {
-            const uint32_t off = (uint32_t)min(csr_beg + tid + j * kThreads, klast) * 2u;
+            const uint32_t off = (uint32_t)min(csr_beg + tid + j * kThreads, elast) * 2u;
             st_col[j] = ld_at<uint16_t>(cm, off);
             st_val[j] = ld_at<uint16_t>(vm, off);
         }
@@ -973,22 +975,25 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     const uint16_t* valk = kk > 0 ? p.val + (size_t)pc.mk * kk : rps;
     const uint16_t* colv = kk > 0 ? p.col + (size_t)pc.mv * kk : rps;
     const uint16_t* valv = kk > 0 ? p.val + (size_t)pc.mv * kk : rps;
+    // (each range's loads clamped to its last entry: slots past the range
+    // re-read it, no further bytes)
     const int klast = max((int)kk, 1) - 1;
+    const int elast_k = min(beg_k + max(cnt_k, 1) - 1, klast), elast_v = min(beg_v + max(cnt_v, 1) - 1, klast);
     // K's entries now (one round trip); V's after the K phase, issued before
     // V's codes and combined after them, so that only they are waited for
     uint32_t ek[CPT], ev[CPT];
-    auto load_csr = [&](const uint16_t* colm, const uint16_t* valm, int beg, uint32_t (&e)[CPT]) {
+    auto load_csr = [&](const uint16_t* colm, const uint16_t* valm, int beg, int elast, uint32_t (&e)[CPT]) {
         uint16_t c[CPT], v[CPT];
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
-            const uint32_t off = (uint32_t)min(beg + tid + j * kFastThreads, klast) * 2u;
+            const uint32_t off = (uint32_t)min(beg + tid + j * kFastThreads, elast) * 2u;
             c[j] = ld_at<uint16_t>(colm, off);
             v[j] = ld_at<uint16_t>(valm, off);
         }
 #pragma unroll
         for (int j = 0; j < CPT; ++j) e[j] = (uint32_t)c[j] | ((uint32_t)v[j] << 16);
     };
-    load_csr(colk, valk, beg_k, ek);
+    load_csr(colk, valk, beg_k, elast_k, ek);
 
     // (B_K^T q)[h][c]: 16 lanes per (h, c), 8 columns each, summed over the
     // lane row
@@ -1068,7 +1073,7 @@ __global__ void __launch_bounds__(kFastThreads, prompt_waves<G>()) attn_prompt_k
     uint16_t vcol[CPT], vval[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const uint32_t off = (uint32_t)min(beg_v + tid + j * kFastThreads, klast) * 2u;
+        const uint32_t off = (uint32_t)min(beg_v + tid + j * kFastThreads, elast_v) * 2u;
         vcol[j] = ld_at<uint16_t>(colv, off);
         vval[j] = ld_at<uint16_t>(valv, off);
     }
@@ -1457,12 +1462,15 @@ __global__ void __launch_bounds__(kMmThreads, NGR == 1 ? 6 : 4) attn_gqa_kernel(
     const uint16_t* valk = kk > 0 ? p.val + (size_t)pc.mk * kk : rps;
     const uint16_t* colv = kk > 0 ? p.col + (size_t)pc.mv * kk : rps;
     const uint16_t* valv = kk > 0 ? p.val + (size_t)pc.mv * kk : rps;
+    // (each range's loads clamped to its last entry: slots past the range
+    // re-read it, no further bytes)
     const int klast = max((int)kk, 1) - 1;
+    const int elast_k = min(beg_k + max(cnt_k, 1) - 1, klast), elast_v = min(beg_v + max(cnt_v, 1) - 1, klast);
     uint16_t ekc[CPT], ekv[CPT], evc[CPT], evv[CPT];
 #pragma unroll
     for (int j = 0; j < CPT; ++j) {
-        const uint32_t ik = (uint32_t)min(beg_k + tid + j * kMmThreads, klast) * 2u;
-        const uint32_t iv = (uint32_t)min(beg_v + tid + j * kMmThreads, klast) * 2u;
+        const uint32_t ik = (uint32_t)min(beg_k + tid + j * kMmThreads, elast_k) * 2u;
+        const uint32_t iv = (uint32_t)min(beg_v + tid + j * kMmThreads, elast_v) * 2u;
         ekc[j] = ld_at<uint16_t>(colk, ik);
         ekv[j] = ld_at<uint16_t>(valk, ik);
         evc[j] = ld_at<uint16_t>(colv, iv);

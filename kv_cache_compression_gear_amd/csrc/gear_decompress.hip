@@ -100,11 +100,12 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     const int wsize = min(kCsrCap, (share * 3 / 2 + 128 + kThreads - 1) / kThreads * kThreads);
     const int guess = (int)((int64_t)row0 * p.k / rows) - (wsize - share) / 2;
     const int wbeg = max(min(guess, p.k - wsize), 0);
-    const int klast = max(p.k, 1) - 1;
+    // (slots past the window re-read its last entry: no further bytes)
+    const int wlast = min(wbeg + wsize, p.k) - 1 >= 0 ? min(wbeg + wsize, p.k) - 1 : 0;
     uint16_t wcol[EPT], wval[EPT];   // (combined where they are stored)
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
-        const uint32_t off = (uint32_t)min(wbeg + tid + j * kThreads, klast) * 2u;
+        const uint32_t off = (uint32_t)min(wbeg + tid + j * kThreads, wlast) * 2u;
         wcol[j] = ld_at<uint16_t>(cm, off);
         wval[j] = ld_at<uint16_t>(vm, off);
     }
