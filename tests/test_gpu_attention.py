@@ -77,6 +77,36 @@ def test_decode_attention_over_compressed_prompt(name, B, Hkv, Hq, d, n, pp):
     _attn_check(out, oc.decode_attention(q.numpy()), what=name)
 
 
+@pytest.mark.parametrize("name,Hkv,Hq,d", [
+    # the tail's workgroup merges the pair's splits for all of its query
+    # heads: G*d columns over 256 threads
+    ("fused_merge_mha_d64", 2, 2, 64),      # 64 columns, 4 threads per column
+    ("fused_merge_gqa2_d64", 2, 4, 64),     # 128 columns, 2 threads per column
+    ("fused_merge_gqa2_d128", 2, 4, 128),   # 256 columns, one per thread
+    ("fused_merge_gqa8_d128", 1, 8, 128),   # 1024 columns, 4 per thread
+])
+def test_tail_merge_every_column_mapping(name, Hkv, Hq, d):
+    B, n0 = 2, 512
+    _say(f"[attention] {name}: prompt {n0} + 3 buffer tokens, merged by the tail")
+    g = 64 if d == 64 else 128
+    pp = P(4, g, 20000, 4, 3)
+    fp = P(4, g, 20000, 2, 3)
+    syn = KVSynth(B, Hkv, d, 4 if d == 128 else 2, seed=7)
+    k, v = syn.prompt(n0)
+    q = syn.queries(Hq)
+    cache = _new_cache(B, Hkv, Hq, d, pp, fp, n0, 64, 8)
+    cache.load_prompt(k.cuda().contiguous(), v.cuda().contiguous())
+    oc = orc.OracleCache(B, Hkv, d, to_orc_params(pp), to_orc_params(fp), 64)
+    oc.load_prompt(k.numpy(), v.numpy())
+    for _ in range(3):
+        kn, vn = syn.step()
+        cache.append(kn.cuda(), vn.cuda())
+        oc.append(kn.numpy(), vn.numpy())
+    out = cache.decode_attn(q.cuda())
+    torch.cuda.synchronize()
+    _attn_check(out, oc.decode_attention(q.numpy()), what=name)
+
+
 def test_streaming_cache_against_oracle():
     B, Hkv, Hq, d, n0, steps = 2, 2, 8, 128, 256, 140
     _say(f"[stream] B={B} Hkv={Hkv} Hq={Hq} prompt={n0} steps={steps}")
