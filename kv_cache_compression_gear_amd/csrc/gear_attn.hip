@@ -133,94 +133,30 @@ __device__ __forceinline__ float sum_rowgroups(float v) {
 constexpr int kAttnCsrCap = 2048;   // outliers of one piece staged in LDS
 constexpr int kAU = 4;              // token steps per batch of loads
 
-// out[b][hk G + h][:] for every query head h of the pair = merge over the
-// pair's splits of (numerators, max, sum), all G heads at once, by the
-// kThreads threads of a workgroup.  The G D columns (c = h D + j) are taken W
-// at a time: thread (c0, q) takes columns c0, c0 + W, ... of the splits
-// q, q + NQ, ... (NQ threads per column when G D < kThreads), in chunks of 8
-// splits whose loads are issued together (selects, not branches: a load in a
-// branch would be waited for there) and folded into running sums under a
-// running maximum; with NQ > 1 the partial results of a column are merged
-// through LDS.  s_m, s_num, s_den: kThreads floats each.
-template <int D, int G>
-__device__ __forceinline__ void merge_pair(const AttnArgs& a, int pair, int b, int hk, float* s_m,
-                                           float* s_num, float* s_den) {
-    constexpr int C = G * D, W = C < kThreads ? C : kThreads;
-    constexpr int NQ = kThreads / W, CPT = C / W, CH = CPT >= 4 ? 4 : 8;
-    static_assert(kThreads % W == 0 && C % W == 0, "thread mapping of the merge");
-    const int tid = thread_id();
-    const int c0 = tid % W, q = tid / W;
-    const float* base = a.partial + (size_t)pair * a.splits * G * (D + 2);
-    const size_t stride = (size_t)G * (D + 2);   // between splits
-    int off[CPT], offml[CPT];
-    float m[CPT], num[CPT], den[CPT];
+// Folds n split results (max ms, sum ls, numerator vs; ls = 0: left out)
+// into a running (m, num, den) under a running maximum: the sums are brought
+// to a new maximum once per call, then each result adds exp(ms - m) times its
+// own.  Selects, not branches, so that loads feeding it are not waited for in
+// a branch.
+template <int N>
+__device__ __forceinline__ void fold_splits(const float (&ms)[N], const float (&ls)[N], const float (&vs)[N],
+                                            float& m, float& num, float& den) {
+    float mc = m;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int c = c0 + i * W, h = c / D;
-        off[i] = h * (D + 2) + c % D;
-        offml[i] = h * (D + 2) + D;
-        m[i] = -INFINITY;
-        num[i] = 0.0f;
-        den[i] = 0.0f;
+    for (int u = 0; u < N; ++u)
+        if (ls[u] > 0.0f) mc = fmaxf(mc, ms[u]);
+    if (mc > m) {   // (from -inf: times 0)
+        const float f = expf(m - mc);
+        num *= f;
+        den *= f;
+        m = mc;
     }
-    for (int s0 = q; s0 < a.splits; s0 += NQ * CH) {
-        float ms[CPT][CH], ls[CPT][CH], vs[CPT][CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int sx = s0 + u * NQ;
-            const float* part = base + (size_t)min(sx, a.splits - 1) * stride;
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const float2 ml = *reinterpret_cast<const float2*>(part + offml[i]);
-                ms[i][u] = ml.x;
-                ls[i][u] = sx < a.splits ? ml.y : 0.0f;   // past the last split: left out
-                vs[i][u] = part[off[i]];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            float mc = m[i];
-#pragma unroll
-            for (int u = 0; u < CH; ++u)
-                if (ls[i][u] > 0.0f) mc = fmaxf(mc, ms[i][u]);
-            if (mc > m[i]) {   // the running sums to the new maximum (from -inf: times 0)
-                const float f = expf(m[i] - mc);
-                num[i] *= f;
-                den[i] *= f;
-                m[i] = mc;
-            }
-#pragma unroll
-            for (int u = 0; u < CH; ++u) {
-                const bool in = ls[i][u] > 0.0f;
-                const float w = expf((in ? ms[i][u] : m[i]) - m[i]);
-                num[i] = in ? fmaf(w, vs[i][u], num[i]) : num[i];
-                den[i] = in ? fmaf(w, ls[i][u], den[i]) : den[i];
-            }
-        }
-    }
-    float* out = a.out + ((size_t)b * a.Hq + (size_t)hk * G) * D;   // the pair's G heads, contiguous
-    if constexpr (NQ == 1) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) out[c0 + i * W] = den[i] > 0.0f ? num[i] / den[i] : 0.0f;
-    } else {
-        s_m[tid] = m[0];
-        s_num[tid] = num[0];
-        s_den[tid] = den[0];
-        __syncthreads();
-        if (q == 0) {
-            float M = m[0];
-#pragma unroll
-            for (int qq = 1; qq < NQ; ++qq) M = fmaxf(M, s_m[qq * W + c0]);
-            float tn = 0.0f, td = 0.0f;
-#pragma unroll
-            for (int qq = 0; qq < NQ; ++qq) {
-                const float mq = s_m[qq * W + c0];
-                const float f = mq > -INFINITY ? expf(mq - M) : 0.0f;
-                tn = fmaf(f, s_num[qq * W + c0], tn);
-                td = fmaf(f, s_den[qq * W + c0], td);
-            }
-            out[c0] = td > 0.0f ? tn / td : 0.0f;
-        }
+    for (int u = 0; u < N; ++u) {
+        const bool in = ls[u] > 0.0f;
+        const float w = expf((in ? ms[u] : m) - m);
+        num = in ? fmaf(w, vs[u], num) : num;
+        den = in ? fmaf(w, ls[u], den) : den;
     }
 }
 
@@ -233,7 +169,8 @@ __device__ __forceinline__ void merge_pair(const AttnArgs& a, int pair, int b, i
 // sparse V entries into its dequantised values through a small per-wave LDS
 // tile that is scattered, read and cleared again.  When a pair has only one
 // split here (fuse_combine), its workgroup then merges all of the pair's
-// splits into out itself, for all of its query heads (no combine launch).
+// splits into out itself, for all of its query heads (no combine launch; its
+// own result is merged from LDS and never written to the workspace).
 template <int D, int G>
 __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     constexpr int LPR = D / 8, RPS = 64 / LPR, TILE = 4 * RPS;
@@ -259,10 +196,52 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     const int t0 = split * a.tokens_per_split;
     const int t1 = min(N, t0 + a.tokens_per_split);
 
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int h = i / D, j = i % D;
-        s_q[i] = h2f(a.q[((size_t)b * a.Hq + hk * G + h) * D + j]);
+    // q of the pair's G heads (contiguous), one load per slot from a clamped
+    // index, all in flight together
+    constexpr int QPT = (G * D + kThreads - 1) / kThreads;
+    const uint16_t* qg = a.q + ((size_t)b * a.Hq + (size_t)hk * G) * D;
+    uint16_t qv[QPT];
+#pragma unroll
+    for (int u = 0; u < QPT; ++u) qv[u] = ld_at<uint16_t>(qg, (uint32_t)min(tid + u * kThreads, G * D - 1) * 2u);
+
+    // With one split here per pair (fuse_combine) this workgroup merges the
+    // pair's splits at the end, for all G heads at once: the G D columns
+    // (c = h D + j) are taken MW at a time, thread (mc0, mq) taking columns
+    // mc0, mc0 + MW, ... of the splits mq, mq + MNQ, ... (MNQ threads per
+    // column when G D < kThreads).  The prompt's splits were written by the
+    // launch before this one: their first MPF per thread are loaded now and
+    // held (loaded in any case, from clamped valid slots, and left out when
+    // not needed); this split is merged from LDS.
+    constexpr int MC = G * D, MW = MC < kThreads ? MC : kThreads;
+    constexpr int MNQ = kThreads / MW, MCPT = MC / MW, MPF = MCPT >= 4 ? 2 : 8;
+    static_assert(kThreads % MW == 0 && MC % MW == 0, "thread mapping of the merge");
+    const int mc0 = tid % MW, mq = tid / MW;
+    const float* mbase = a.partial + (size_t)pair * a.splits * G * (D + 2);
+    const size_t mstride = (size_t)G * (D + 2);   // between splits
+    int moff[MCPT], mofl[MCPT];
+#pragma unroll
+    for (int i = 0; i < MCPT; ++i) {
+        const int c = mc0 + i * MW, h = c / D;
+        moff[i] = h * (D + 2) + c % D;
+        mofl[i] = h * (D + 2) + D;
     }
+    float pfm[MCPT][MPF], pfl[MCPT][MPF], pfv[MCPT][MPF];
+#pragma unroll
+    for (int u = 0; u < MPF; ++u) {
+        const int sx = mq + u * MNQ;
+        const float* part = mbase + (size_t)min(sx, max(split - 1, 0)) * mstride;
+#pragma unroll
+        for (int i = 0; i < MCPT; ++i) {
+            const float2 ml = *reinterpret_cast<const float2*>(part + mofl[i]);
+            pfm[i][u] = ml.x;
+            pfl[i][u] = sx < split ? ml.y : 0.0f;   // (this split and beyond: left out)
+            pfv[i][u] = part[moff[i]];
+        }
+    }
+
+#pragma unroll
+    for (int u = 0; u < QPT; ++u)
+        if (tid + u * kThreads < G * D) s_q[tid + u * kThreads] = h2f(qv[u]);
     for (int i = tid; i < 4 * RPS * D; i += kThreads) s_tile[i] = 0.0f;
     __syncthreads();
     float q[G][8], qs[G];
@@ -755,22 +734,84 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             for (int e = 0; e < 8; ++e) s_red[(wv * G + h) * D + colq * 8 + e] = acc[h][e];
     }
     __syncthreads();
-    float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
-    for (int i = tid; i < G * D; i += kThreads) {
-        const int h = i / D, j = i % D;
-        part[h * (D + 2) + j] = s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j] +
-                                s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j];
+    if (!a.fuse_combine) {
+        float* part = a.partial + ((size_t)pair * a.splits + split) * G * (D + 2);
+        for (int i = tid; i < G * D; i += kThreads) {
+            const int h = i / D, j = i % D;
+            part[h * (D + 2) + j] = s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j] +
+                                    s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j];
+        }
+        if (tid < G) {
+            part[tid * (D + 2) + D] = n > 0 ? s_stat[tid] : -INFINITY;
+            part[tid * (D + 2) + D + 1] = n > 0 ? s_stat[G + tid] : 0.0f;
+        }
+        return;
     }
-    if (tid < G) {
-        part[tid * (D + 2) + D] = n > 0 ? s_stat[tid] : -INFINITY;
-        part[tid * (D + 2) + D + 1] = n > 0 ? s_stat[G + tid] : 0.0f;
+    // ---------------- the pair's merge (this is its only split here): the
+    // prefetched prompt splits, any further ones in chunks of 8 loaded
+    // together, then this split from LDS (by the threads mq == 0)
+    float m[MCPT], num[MCPT], den[MCPT];
+#pragma unroll
+    for (int i = 0; i < MCPT; ++i) {
+        m[i] = -INFINITY;
+        num[i] = 0.0f;
+        den[i] = 0.0f;
+        fold_splits<MPF>(pfm[i], pfl[i], pfv[i], m[i], num[i], den[i]);
     }
-    if (a.fuse_combine) {
-        // the pair's only split here: every other split was written by the
-        // prompt kernel, launched before on the same stream, and this one's
-        // by this workgroup (visible to it after the barrier)
+    constexpr int CH = 8;
+    for (int s0 = mq + MPF * MNQ; s0 < split; s0 += MNQ * CH) {
+        float ms[MCPT][CH], ls[MCPT][CH], vs[MCPT][CH];
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            const int sx = s0 + u * MNQ;
+            const float* part = mbase + (size_t)min(sx, split - 1) * mstride;
+#pragma unroll
+            for (int i = 0; i < MCPT; ++i) {
+                const float2 ml = *reinterpret_cast<const float2*>(part + mofl[i]);
+                ms[i][u] = ml.x;
+                ls[i][u] = sx < split ? ml.y : 0.0f;
+                vs[i][u] = part[moff[i]];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < MCPT; ++i) fold_splits<CH>(ms[i], ls[i], vs[i], m[i], num[i], den[i]);
+    }
+    if (mq == 0 && n > 0) {
+#pragma unroll
+        for (int i = 0; i < MCPT; ++i) {
+            const int c = mc0 + i * MW, h = c / D, j = c % D;
+            const float own[1] = {s_red[(0 * G + h) * D + j] + s_red[(1 * G + h) * D + j] +
+                                  s_red[(2 * G + h) * D + j] + s_red[(3 * G + h) * D + j]};
+            const float om[1] = {s_stat[h]}, ol[1] = {s_stat[G + h]};
+            fold_splits<1>(om, ol, own, m[i], num[i], den[i]);
+        }
+    }
+    float* out = a.out + ((size_t)b * a.Hq + (size_t)hk * G) * D;   // the pair's G heads, contiguous
+    if constexpr (MNQ == 1) {
+#pragma unroll
+        for (int i = 0; i < MCPT; ++i) out[mc0 + i * MW] = den[i] > 0.0f ? num[i] / den[i] : 0.0f;
+    } else {
+        float* s_m = s_mg;
+        float* s_num = s_mg + kThreads;
+        float* s_den = s_mg + 2 * kThreads;
+        s_m[tid] = m[0];
+        s_num[tid] = num[0];
+        s_den[tid] = den[0];
         __syncthreads();
-        merge_pair<D, G>(a, pair, b, hk, s_mg, s_mg + kThreads, s_mg + 2 * kThreads);
+        if (mq == 0) {
+            float M = m[0];
+#pragma unroll
+            for (int qq = 1; qq < MNQ; ++qq) M = fmaxf(M, s_m[qq * MW + mc0]);
+            float tn = 0.0f, td = 0.0f;
+#pragma unroll
+            for (int qq = 0; qq < MNQ; ++qq) {
+                const float mqq = s_m[qq * MW + mc0];
+                const float f = mqq > -INFINITY ? expf(mqq - M) : 0.0f;
+                tn = fmaf(f, s_num[qq * MW + mc0], tn);
+                td = fmaf(f, s_den[qq * MW + mc0], td);
+            }
+            out[mc0] = td > 0.0f ? tn / td : 0.0f;
+        }
     }
 }
 
