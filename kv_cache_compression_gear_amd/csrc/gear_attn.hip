@@ -239,6 +239,25 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         }
     }
 
+    // the split's fp16 buffer rows (K and V), their first 4 steps, loaded now
+    // too: they depend on nothing (clamped rows: valid addresses also when
+    // the split holds no buffer token; then unused)
+    constexpr bool kPfBuf = G * D <= 512;   // (registers: at most 4 heads at d = 128)
+    const int bt0 = pt + a.fills.count * a.fills.p.rows;   // first buffer token
+    const int brow0 = max(t0, bt0) - bt0, blen = max(t1 - max(t0, bt0), 0);
+    uint4 pbk[4], pbv[4];
+    if constexpr (kPfBuf) {
+        const uint16_t* kbuf = a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
+        const uint16_t* vbuf = a.buf + (((size_t)(1 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int tok = min(u * TILE + wv * RPS + rl, max(blen, 1) - 1);
+            const uint32_t off = (uint32_t)(min(brow0 + tok, a.buf_cap - 1) * D + colq * 8) * 2u;
+            pbk[u] = ld_at<uint4>(kbuf, off);
+            pbv[u] = ld_at<uint4>(vbuf, off);
+        }
+    }
+
 #pragma unroll
     for (int u = 0; u < QPT; ++u)
         if (tid + u * kThreads < G * D) s_q[tid + u * kThreads] = h2f(qv[u]);
@@ -467,13 +486,19 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         } else {
             const uint16_t* kb = a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
             // 4 steps' rows loaded together (clamped rows, unconditional: a
-            // load under a divergent condition is waited for at once)
+            // load under a divergent condition is waited for at once); the
+            // first 4 steps' were loaded at the start
             for (int tt0 = 0; tt0 < pc.len; tt0 += 4 * TILE) {
                 uint4 wb[4];
+                if (kPfBuf && tt0 == 0) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
-                    wb[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                    for (int u = 0; u < 4; ++u) wb[u] = pbk[u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
+                        wb[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -692,10 +717,15 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             // 4 steps' rows loaded together, as for K
             for (int tt0 = 0; tt0 < pc.len; tt0 += 4 * TILE) {
                 uint4 wb[4];
+                if (kPfBuf && tt0 == 0) {
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
-                    wb[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                    for (int u = 0; u < 4; ++u) wb[u] = pbv[u];
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
+                        wb[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                    }
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
