@@ -6,10 +6,11 @@ attention layer (batch 8, 32 heads, 4096 tokens, head_dim 128; K and V, fp16 =
   gear_compress    outlier top-k + CSR, 4-bit group quantization, rank-4 fit
                    (3 power iterations) of all 512 K/V matrices
   gear_decompress  reconstruction of all 512 matrices to fp16
-  gear_append_tokens + gear_decode_attn
+  gear_append_decode_attn
                    one new token per sequence into the streaming cache (its
                    buffer is compressed every 64 steps) and decode attention of
-                   one query per head over the compressed 4096+ tokens
+                   one query per head over the compressed 4096+ tokens, in one
+                   call (the token is written by the attention launch)
 Inputs are synthetic, seeded, already resident in HBM.  `value` is fp16 KV
 bytes per step / step time (GB/s).  Prints one JSON line.
 
@@ -536,14 +537,12 @@ def _stream_decode(gear, WORKLOADS, torch):
     del warm
     t0 = time.perf_counter()
     for i in range(steps):
-        caches[0].append(nk[i], nv[i])
-        caches[0].decode_attn(qs[i], out=out)
+        caches[0].append_decode_attn(nk[i], nv[i], qs[i], out=out)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     gear.timing_enable(True)
     for i in range(steps):
-        caches[1].append(nk[i], nv[i])
-        caches[1].decode_attn(qs[i], out=out)
+        caches[1].append_decode_attn(nk[i], nv[i], qs[i], out=out)
     torch.cuda.synchronize()
     kt = gear.timing_read()
     gear.timing_enable(False)
@@ -833,8 +832,7 @@ def main():
         gear.decompress(packed, out=xhat)
         if marks:
             e[2].record()
-        cache.append(new_k[i], new_v[i])
-        cache.decode_attn(qs[i], out=out)
+        cache.append_decode_attn(new_k[i], new_v[i], qs[i], out=out)
         if marks:
             e[3].record()
 

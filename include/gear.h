@@ -292,6 +292,25 @@ gear_status gear_decode_attn(const gear_cache* cache, const void* q_f16, int32_t
                              float sm_scale, float* out_f32, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/*
+ * One decode step of the streaming cache in one call: appends one token per
+ * sequence (k_new_f16, v_new_f16: [B][Hkv][d], 16-byte aligned) and then
+ * takes decode attention as gear_decode_attn, with the same results, cache
+ * contents and errors as gear_append_tokens(..., 1, ...) followed by
+ * gear_decode_attn (source: the allpcb Q&A, Q3 "Streaming strategy" -- new
+ * tokens go to the fp16 buffer, which is compressed when full -- and Q4 --
+ * decode attention reads the compressed cache).  The token is written into
+ * the buffer by the attention launch itself, which reads it from k_new_f16 /
+ * v_new_f16 (one launch fewer per step); when it fills the buffer, the two
+ * calls are made one after the other (the buffer's compression lies between
+ * them).  workspace as for both calls (gear_cache_workspace_bytes).  On
+ * GEAR_ERR_HIP from a launch the cache is marked failed (every later call on
+ * it is refused with GEAR_ERR_INVALID_ARG), as for gear_append_tokens.
+ */
+gear_status gear_append_decode_attn(gear_cache* cache, const void* k_new_f16, const void* v_new_f16,
+                                    const void* q_f16, int32_t q_heads, float sm_scale, float* out_f32,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* Current counters and section pointers (host call, nothing launched). */
 gear_status gear_cache_get_info(const gear_cache* cache, gear_cache_info* out);
 

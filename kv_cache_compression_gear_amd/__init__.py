@@ -77,7 +77,7 @@ EXPORTS = ["gear_packed_layout", "gear_packed_bytes", "gear_compress_workspace_b
            "gear_compress", "gear_compress_noalloc", "gear_decompress",
            "gear_cache_arena_bytes", "gear_cache_workspace_bytes", "gear_cache_create",
            "gear_cache_destroy", "gear_cache_load_prompt", "gear_append_tokens",
-           "gear_decode_attn", "gear_cache_get_info", "gear_timing_enable", "gear_timing_read",
+           "gear_decode_attn", "gear_append_decode_attn", "gear_cache_get_info", "gear_timing_enable", "gear_timing_read",
            "gear_status_str", "gear_last_error"]
 
 # Kernel names accepted by gear_timing_read.
@@ -124,6 +124,8 @@ def lib():
         L.gear_append_tokens.argtypes = [P, P, P, i32, P, sz, P]
         L.gear_decode_attn.restype = S
         L.gear_decode_attn.argtypes = [P, P, i32, ctypes.c_float, P, P, sz, P]
+        L.gear_append_decode_attn.restype = S
+        L.gear_append_decode_attn.argtypes = [P, P, P, P, i32, ctypes.c_float, P, P, sz, P]
         L.gear_cache_get_info.restype = S
         L.gear_cache_get_info.argtypes = [P, ctypes.POINTER(_CacheInfo)]
         L.gear_timing_enable.restype = S
@@ -374,6 +376,25 @@ class Cache:
         scale = 1.0 / (d ** 0.5) if sm_scale is None else sm_scale
         _check(lib().gear_decode_attn(self._h, _ptr(q), Hq, ctypes.c_float(scale), _ptr(out),
                                       _ptr(self.workspace), self.workspace.numel(), _stream()))
+        return out
+
+    def append_decode_attn(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                           sm_scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+        """One decode step: append one token per sequence (k_new, v_new fp16
+        [B, Hkv, d]) and take decode attention of q (fp16 [B, Hq, d]) over the
+        cache including it; the same as append() then decode_attn()."""
+        _check_input(k_new)
+        _check_input(v_new)
+        _check_input(q)
+        if k_new.dim() != 3 or v_new.shape != k_new.shape:
+            raise ValueError("k_new, v_new must be [B, Hkv, d] (one token per sequence)")
+        B, Hq, d = q.shape
+        if out is None:
+            out = torch.empty((B, Hq, d), dtype=torch.float32, device=q.device)
+        scale = 1.0 / (d ** 0.5) if sm_scale is None else sm_scale
+        _check(lib().gear_append_decode_attn(self._h, _ptr(k_new), _ptr(v_new), _ptr(q), Hq,
+                                             ctypes.c_float(scale), _ptr(out), _ptr(self.workspace),
+                                             self.workspace.numel(), _stream()))
         return out
 
     def info(self) -> _CacheInfo:

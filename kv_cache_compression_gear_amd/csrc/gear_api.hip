@@ -645,11 +645,12 @@ gear_status gear_append_tokens(gear_cache* g, const void* k_new_f16, const void*
     return GEAR_OK;
 }
 
-gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_heads,
-                             float sm_scale, float* out_f32, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-    if (!g) return fail(GEAR_ERR_INVALID_ARG, "cache is NULL");
-    if (g->failed) return failed_cache();
+namespace {
+
+// Validates a decode-attention call and fills its arguments; `extra` tokens
+// (appended by the same launch) are counted as cached already.
+gear_status attn_args(const gear_cache* g, const void* q_f16, int32_t q_heads, float sm_scale,
+                      float* out_f32, void* workspace, size_t workspace_bytes, int extra, AttnArgs* pa) {
     const gear_cache_config& c = g->cfg;
     if (q_heads < c.kv_heads || q_heads % c.kv_heads != 0)
         return fail(GEAR_ERR_INVALID_ARG, "q_heads %d is not a multiple of kv_heads %d", q_heads,
@@ -663,8 +664,8 @@ gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_h
                     "q_f16 and out_f32 must be 16-byte, workspace 256-byte aligned");
     if (c.prompt_tokens > 0 && !g->prompt_loaded)
         return fail(GEAR_ERR_INVALID_ARG, "load the prompt before decoding");
-    const int64_t tokens = (int64_t)(c.prompt_tokens) + g->appended;
-    AttnArgs a;
+    const int64_t tokens = (int64_t)(c.prompt_tokens) + g->appended + extra;
+    AttnArgs a{};
     const size_t need = attn_workspace_bytes(c.batch, c.kv_heads, q_heads, c.head_dim, tokens,
                                              &a.splits, &a.tokens_per_split);
     if (workspace_bytes < need)
@@ -689,12 +690,68 @@ gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_h
     a.fills.chunks = 1;
     a.fills.count = g->num_fills;
     a.fills.stride = g->fill_stride;
-    a.buf = reinterpret_cast<const uint16_t*>(g->arena + g->off_buf);
+    a.buf = reinterpret_cast<uint16_t*>(g->arena + g->off_buf);
     a.buf_cap = c.buf_tokens;
-    a.buf_len = g->buf_len;
+    a.buf_len = g->buf_len + extra;
     a.partial = static_cast<float*>(workspace);
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.new_row = -1;
+    *pa = a;
+    return GEAR_OK;
+}
+
+}  // namespace
+
+gear_status gear_decode_attn(const gear_cache* g, const void* q_f16, int32_t q_heads,
+                             float sm_scale, float* out_f32, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+    if (!g) return fail(GEAR_ERR_INVALID_ARG, "cache is NULL");
+    if (g->failed) return failed_cache();
+    AttnArgs a;
+    const gear_status s = attn_args(g, q_f16, q_heads, sm_scale, out_f32, workspace, workspace_bytes, 0, &a);
+    if (s != GEAR_OK) return s;
     hipError_t e = launch_decode_attn(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode attention launch");
+    return GEAR_OK;
+}
+
+gear_status gear_append_decode_attn(gear_cache* g, const void* k_new_f16, const void* v_new_f16,
+                                    const void* q_f16, int32_t q_heads, float sm_scale, float* out_f32,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!g) return fail(GEAR_ERR_INVALID_ARG, "cache is NULL");
+    if (g->failed) return failed_cache();
+    const gear_cache_config& c = g->cfg;
+    // a token that fills the buffer: its compression runs between the two
+    if (g->buf_len + 1 >= c.buf_tokens) {
+        const gear_status s = gear_append_tokens(g, k_new_f16, v_new_f16, 1, workspace, workspace_bytes, stream);
+        if (s != GEAR_OK) return s;
+        return gear_decode_attn(g, q_f16, q_heads, sm_scale, out_f32, workspace, workspace_bytes, stream);
+    }
+    // the checks of gear_append_tokens for one token, then those of decoding
+    if (c.prompt_tokens > 0 && !g->prompt_loaded)
+        return fail(GEAR_ERR_INVALID_ARG, "load the prompt before appending tokens");
+    if (g->appended + 1 > c.max_new_tokens)
+        return fail(GEAR_ERR_CAPACITY, "appending 1 token exceeds max_new_tokens %d (have %lld)",
+                    c.max_new_tokens, (long long)g->appended);
+    if (!k_new_f16 || !v_new_f16) return fail(GEAR_ERR_INVALID_ARG, "NULL device pointer");
+    if (!aligned(k_new_f16, 16) || !aligned(v_new_f16, 16))
+        return fail(GEAR_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+    AttnArgs a;
+    const gear_status s = attn_args(g, q_f16, q_heads, sm_scale, out_f32, workspace, workspace_bytes, 1, &a);
+    if (s != GEAR_OK) return s;
+    a.k_new = static_cast<const uint16_t*>(k_new_f16);
+    a.v_new = static_cast<const uint16_t*>(v_new_f16);
+    a.new_row = g->buf_len;
+    hipError_t e = launch_decode_attn(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        // the token may or may not have reached the buffer: the cache is no
+        // longer usable (as after a failed append)
+        g->failed = true;
+        return hip_fail(e, "append + decode attention launch");
+    }
+    g->buf_len += 1;
+    g->appended += 1;
     return GEAR_OK;
 }
 

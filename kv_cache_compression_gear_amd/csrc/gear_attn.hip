@@ -242,19 +242,24 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     // the split's fp16 buffer rows (K and V), their first 4 steps, loaded now
     // too: they depend on nothing (clamped rows: valid addresses also when
     // the split holds no buffer token; then unused)
-    constexpr bool kPfBuf = G * D <= 512;   // (registers: at most 4 heads at d = 128)
+    constexpr bool kPfBuf = G * D < 512;   // (registers: 4 heads at d = 128 would drop to one wave per SIMD)
     const int bt0 = pt + a.fills.count * a.fills.p.rows;   // first buffer token
     const int brow0 = max(t0, bt0) - bt0, blen = max(t1 - max(t0, bt0), 0);
+    // buffer row `row` of K (kv = 0) or V: a token appended by this launch
+    // (row new_row) is read from the caller's array instead
+    auto brow_src = [&](int kv, int row) -> const uint16_t* {
+        const uint16_t* nw = kv == 0 ? a.k_new : a.v_new;
+        return row == a.new_row ? nw + ((size_t)b * a.Hkv + hk) * D
+                                : a.buf + (((size_t)(kv * a.B + b) * a.Hkv + hk) * a.buf_cap + row) * D;
+    };
     uint4 pbk[4], pbv[4];
     if constexpr (kPfBuf) {
-        const uint16_t* kbuf = a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
-        const uint16_t* vbuf = a.buf + (((size_t)(1 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int tok = min(u * TILE + wv * RPS + rl, max(blen, 1) - 1);
-            const uint32_t off = (uint32_t)(min(brow0 + tok, a.buf_cap - 1) * D + colq * 8) * 2u;
-            pbk[u] = ld_at<uint4>(kbuf, off);
-            pbv[u] = ld_at<uint4>(vbuf, off);
+            const int row = min(brow0 + tok, a.buf_cap - 1);
+            pbk[u] = *reinterpret_cast<const uint4*>(brow_src(0, row) + colq * 8);
+            pbv[u] = *reinterpret_cast<const uint4*>(brow_src(1, row) + colq * 8);
         }
     }
 
@@ -484,10 +489,10 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 for (int h = 0; h < G; ++h) s_sc[(base + i) * G + h] += add[h];
             }
         } else {
-            const uint16_t* kb = a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
             // 4 steps' rows loaded together (clamped rows, unconditional: a
             // load under a divergent condition is waited for at once); the
-            // first 4 steps' were loaded at the start
+            // first 4 steps' were loaded at the start.  A token appended by
+            // this launch is also written into the buffer here.
             for (int tt0 = 0; tt0 < pc.len; tt0 += 4 * TILE) {
                 uint4 wb[4];
                 if (kPfBuf && tt0 == 0) {
@@ -497,8 +502,15 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
-                        wb[u] = *reinterpret_cast<const uint4*>(kb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                        wb[u] = *reinterpret_cast<const uint4*>(brow_src(0, pc.row0 + tok) + colq * 8);
                     }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int tok = tt0 + u * TILE + wv * RPS + rl;
+                    if (tok < pc.len && pc.row0 + tok == a.new_row)
+                        *reinterpret_cast<uint4*>(a.buf + (((size_t)(0 * a.B + b) * a.Hkv + hk) * a.buf_cap +
+                                                           a.new_row) * D + colq * 8) = wb[u];
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
@@ -713,7 +725,6 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 }
             }
         } else {
-            const uint16_t* vb = a.buf + (((size_t)(1 * a.B + b) * a.Hkv + hk) * a.buf_cap) * D;
             // 4 steps' rows loaded together, as for K
             for (int tt0 = 0; tt0 < pc.len; tt0 += 4 * TILE) {
                 uint4 wb[4];
@@ -724,8 +735,15 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const int tok = min(tt0 + u * TILE + wv * RPS + rl, pc.len - 1);
-                        wb[u] = *reinterpret_cast<const uint4*>(vb + (size_t)(pc.row0 + tok) * D + colq * 8);
+                        wb[u] = *reinterpret_cast<const uint4*>(brow_src(1, pc.row0 + tok) + colq * 8);
                     }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int tok = tt0 + u * TILE + wv * RPS + rl;
+                    if (tok < pc.len && pc.row0 + tok == a.new_row)
+                        *reinterpret_cast<uint4*>(a.buf + (((size_t)(1 * a.B + b) * a.Hkv + hk) * a.buf_cap +
+                                                           a.new_row) * D + colq * 8) = wb[u];
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {

@@ -175,13 +175,19 @@ struct AttnArgs {
     float* out;            // [B][Hq][d]
     AttnSeg prompt;        // prompt.count is 0 or 1
     AttnSeg fills;         // fills.count = number of fills
-    const uint16_t* buf;   // [2][B][Hkv][cap][d]
+    uint16_t* buf;         // [2][B][Hkv][cap][d] (written only at row new_row)
     int32_t buf_cap, buf_len;
     float* partial;        // workspace: [B*Hkv][splits][G][d + 2]
     int32_t splits;
     int32_t tokens_per_split;
     int32_t split0;        // splits [0, split0) are whole prompt splits (fast kernel)
     int32_t fuse_combine;  // 1: the one split of attn_split_kernel per pair also merges
+    // one appended token per (b, kv-head), [B][Hkv][d] each, that the split
+    // holding buffer row new_row reads from here and writes into the buffer
+    // (new_row < 0: none; buf_len counts it)
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int32_t new_row;
 };
 size_t attn_workspace_bytes(int B, int Hkv, int Hq, int d, int64_t tokens, int* splits,
                             int* tokens_per_split);

@@ -113,6 +113,12 @@ int main(int argc, char** argv)
         EXPECT(gear_decode_attn(h, fake, 32, 0.1f, fake, fake, 1 << 30, NULL) == GEAR_ERR_UNSUPPORTED);
         EXPECT(gear_decode_attn(h, (char*)fake + 2, 4, 0.1f, fake, fake, 1 << 30, NULL) ==
                GEAR_ERR_INVALID_ARG);
+        EXPECT(gear_append_decode_attn(h, NULL, fake, fake, 4, 0.1f, fake, fake, 1 << 30, NULL) ==
+               GEAR_ERR_INVALID_ARG);
+        EXPECT(gear_append_decode_attn(h, fake, fake, fake, 32, 0.1f, fake, fake, 1 << 30, NULL) ==
+               (pt > 0 ? GEAR_ERR_INVALID_ARG : GEAR_ERR_UNSUPPORTED));
+        EXPECT(gear_append_decode_attn(h, fake, fake, fake, 4, 0.1f, fake, fake, 16, NULL) ==
+               (pt > 0 ? GEAR_ERR_INVALID_ARG : GEAR_ERR_WORKSPACE));
         if (pt > 0) {
             EXPECT(gear_decode_attn(h, fake, 4, 0.1f, fake, fake, 1 << 30, NULL) == GEAR_ERR_INVALID_ARG);
             EXPECT(gear_append_tokens(h, fake, fake, 1, fake, 1 << 30, NULL) == GEAR_ERR_INVALID_ARG);

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     lib = gear.lib()
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     assert sorted(gear.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -157,6 +157,50 @@ def test_cache_without_prompt_capacity():
         lib.gear_cache_destroy(h)
 
 
+def test_append_decode_attn_checks_on_the_host():
+    """The one-call decode step refuses what either of its two calls refuses,
+    before anything is enqueued: status codes 1 invalid argument, 2
+    unsupported, 3 capacity."""
+    lib = gear.lib()
+    fake = ctypes.c_void_p(0x20000000)
+    f = ctypes.c_float(0.1)
+    assert lib.gear_append_decode_attn(None, fake, fake, fake, 8, f, fake, fake, 1 << 30, None) == 1
+    c = _cfg(prompt_tokens=2048, max_new=4, B=1, H=2)
+    n = lib.gear_cache_arena_bytes(ctypes.byref(c))
+    h = ctypes.c_void_p()
+    assert lib.gear_cache_create(ctypes.byref(c), ctypes.c_void_p(0x10000000), n, ctypes.byref(h)) == 0
+    try:
+        # the prompt is not loaded yet
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 8, f, fake, fake, 1 << 30, None) == 1
+    finally:
+        lib.gear_cache_destroy(h)
+    c = _cfg(prompt_tokens=0, max_new=4, B=1, H=2)
+    n = lib.gear_cache_arena_bytes(ctypes.byref(c))
+    assert lib.gear_cache_create(ctypes.byref(c), ctypes.c_void_p(0x10000000), n, ctypes.byref(h)) == 0
+    try:
+        assert lib.gear_append_decode_attn(h, None, fake, fake, 8, f, fake, fake, 1 << 30, None) == 1
+        assert lib.gear_append_decode_attn(h, ctypes.c_void_p(0x20000008), fake, fake, 8, f, fake, fake,
+                                           1 << 30, None) == 1
+        assert b"16-byte" in lib.gear_last_error()
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 3, f, fake, fake, 1 << 30, None) == 1
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 32, f, fake, fake, 1 << 30, None) == 2
+        assert lib.gear_append_decode_attn(h, fake, fake, ctypes.c_void_p(0x20000002), 8, f, fake, fake,
+                                           1 << 30, None) == 1
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 8, f, fake, fake, 16, None) == 5
+        inf = gear._CacheInfo()
+        assert lib.gear_cache_get_info(h, ctypes.byref(inf)) == 0
+        assert inf.tokens == 0 and inf.buf_len == 0     # nothing was appended by a refused call
+    finally:
+        lib.gear_cache_destroy(h)
+    c = _cfg(prompt_tokens=0, max_new=0, B=1, H=2)
+    n = lib.gear_cache_arena_bytes(ctypes.byref(c))
+    assert lib.gear_cache_create(ctypes.byref(c), ctypes.c_void_p(0x10000000), n, ctypes.byref(h)) == 0
+    try:
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 8, f, fake, fake, 1 << 30, None) == 3
+    finally:
+        lib.gear_cache_destroy(h)
+
+
 def test_timing_registry_on_the_host():
     """Timing is opt-in; reading it with no launches recorded needs no GPU."""
     lib = gear.lib()
@@ -193,6 +237,28 @@ def _gpu_visible():
 
 
 @pytest.mark.skipif("_gpu_visible()", reason="needs a host with no GPU: the launch must fail")
+def test_failed_append_decode_launch_marks_the_cache_failed():
+    """The one-call decode step's attention launch fails with no GPU: it
+    reports GEAR_ERR_HIP, the token is not counted, and the cache is failed."""
+    lib = gear.lib()
+    c = _cfg(prompt_tokens=0, max_new=8, B=1, H=1)
+    n = lib.gear_cache_arena_bytes(ctypes.byref(c))
+    h = ctypes.c_void_p()
+    assert lib.gear_cache_create(ctypes.byref(c), ctypes.c_void_p(0x10000000), n, ctypes.byref(h)) == 0
+    try:
+        fake = ctypes.c_void_p(0x20000000)
+        f = ctypes.c_float(0.1)
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 1, f, fake, fake, 1 << 30, None) == 4
+        inf = gear._CacheInfo()
+        assert lib.gear_cache_get_info(h, ctypes.byref(inf)) == 0
+        assert inf.tokens == 0 and inf.buf_len == 0
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 1, f, fake, fake, 1 << 30, None) == 1
+        assert b"destroy the cache" in lib.gear_last_error()
+    finally:
+        lib.gear_cache_destroy(h)
+
+
+@pytest.mark.skipif("_gpu_visible()", reason="needs a host with no GPU: the launch must fail")
 def test_failed_launch_marks_the_cache_failed():
     """With no GPU the buffer-append launch fails: the call reports
     GEAR_ERR_HIP and every later call on that cache is refused with
@@ -207,6 +273,8 @@ def test_failed_launch_marks_the_cache_failed():
         assert lib.gear_append_tokens(h, fake, fake, 1, fake, 1 << 30, None) == 4
         assert lib.gear_append_tokens(h, fake, fake, 1, fake, 1 << 30, None) == 1
         assert b"destroy the cache" in lib.gear_last_error()
+        assert lib.gear_append_decode_attn(h, fake, fake, fake, 1, ctypes.c_float(0.1), fake, fake,
+                                           1 << 30, None) == 1
         assert lib.gear_decode_attn(h, fake, 1, ctypes.c_float(0.1), fake, fake, 1 << 30, None) == 1
         assert lib.gear_cache_load_prompt(h, fake, fake, fake, 1 << 30, None) == 1
     finally:

@@ -107,6 +107,59 @@ def test_tail_merge_every_column_mapping(name, Hkv, Hq, d):
     _attn_check(out, oc.decode_attention(q.numpy()), what=name)
 
 
+def _buffer_rows(cache, B, Hkv, d):
+    """The used rows of a cache's fp16 buffer: [2, B, Hkv, buf_len, d]."""
+    inf = cache.info()
+    cap = cache.cfg.buf_tokens
+    buf = cache._view(inf.buffer_f16, 2 * B * Hkv * cap * d * 2).view(torch.float16)
+    return buf.view(2, B, Hkv, cap, d)[:, :, :, :inf.buf_len]
+
+
+@pytest.mark.parametrize("name,Hkv,Hq,d,n0", [
+    ("fused_step_gqa4", 2, 8, 128, 256),
+    ("fused_step_mha", 2, 2, 128, 512),
+    ("fused_step_gqa8", 1, 8, 128, 256),     # buffer rows read per batch, not at the start
+    ("fused_step_d64", 2, 4, 64, 256),
+    ("fused_step_no_prompt", 2, 4, 128, 0),
+])
+def test_append_decode_attn_matches_separate_calls(name, Hkv, Hq, d, n0):
+    """gear_append_decode_attn (the token written by the attention launch)
+    against gear_append_tokens + gear_decode_attn on a twin cache, over 140
+    steps (two buffer fills, taken by the two-call path): identical outputs,
+    counters, buffer rows and fills."""
+    B, steps = 2, 140
+    _say(f"[attention] {name}: {steps} fused steps vs separate calls")
+    g = 64 if d == 64 else 128
+    pp = P(4, g, 20000, 4, 3)
+    fp = P(4, g, 20000, 2, 3)
+    syn = KVSynth(B, Hkv, d, 4 if d == 128 else 2, seed=11)
+    c1 = _new_cache(B, Hkv, Hq, d, pp, fp, n0, 64, steps)
+    c2 = _new_cache(B, Hkv, Hq, d, pp, fp, n0, 64, steps)
+    if n0:
+        k, v = syn.prompt(n0)
+        k, v = k.cuda().contiguous(), v.cuda().contiguous()
+    else:
+        k = v = torch.empty(0, dtype=torch.float16, device="cuda")
+    c1.load_prompt(k, v)
+    c2.load_prompt(k, v)
+    for s in range(1, steps + 1):
+        kn, vn = syn.step()
+        kn, vn = kn.cuda().contiguous(), vn.cuda().contiguous()
+        q = syn.queries(Hq).cuda().contiguous()
+        c1.append(kn, vn)
+        o1 = c1.decode_attn(q)
+        o2 = c2.append_decode_attn(kn, vn, q)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"step {s}: max diff {(o1 - o2).abs().max().item()}"
+        i1, i2 = c1.info(), c2.info()
+        assert (i1.tokens, i1.buf_len, i1.num_fills) == (i2.tokens, i2.buf_len, i2.num_fills)
+        assert torch.equal(_buffer_rows(c1, B, Hkv, d), _buffer_rows(c2, B, Hkv, d)), f"step {s}"
+    assert c2.info().num_fills == 2
+    for f in range(2):
+        for a, b in zip(c1.fill_packed(f).sections(), c2.fill_packed(f).sections()):
+            assert torch.equal(a, b), f"fill {f}"
+
+
 def test_streaming_cache_against_oracle():
     B, Hkv, Hq, d, n0, steps = 2, 2, 8, 128, 256, 140
     _say(f"[stream] B={B} Hkv={Hkv} Hq={Hq} prompt={n0} steps={steps}")
