@@ -66,6 +66,9 @@ SMALL = [
     ("all_outliers", 1, 1, 64, 64, P(4, 64, 1000000, 2, 2), 2, 8.0),
     ("fill_64_r2", 2, 2, 64, 128, P(4, 128, 20000, 2, 3), 4, 8.0),
     ("n5000_d64_r8", 1, 1, 5000, 64, P(4, 64, 20000, 8, 2), 2, 8.0),
+    # a rank that fills only part of its 8 slots (the A rows' spare slots
+    # repeat the last column and meet B's zero padding in the reconstruction)
+    ("n600_g64_r6", 1, 2, 600, 128, P(4, 64, 20000, 6, 2), 4, 8.0),
 ]
 
 
