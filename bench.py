@@ -79,6 +79,9 @@ KERNEL_SYMBOL = {"select": "select_kernel", "compress": "compress_kernel",
                  "attn_prompt": "attn_prompt_kernel", "attn_gqa": "attn_gqa_kernel",
                  "attn_split": "attn_split_kernel",
                  "attn_combine": "attn_combine_kernel", "buffer_append": "buffer_append_kernel"}
+# further device symbols of a kernel key: the decompress launch is
+# decompress_mm_kernel with a low-rank term, decompress_kernel without
+KERNEL_ALIASES = {"decompress": ("decompress_mm_kernel",)}
 SQ_PASSES = [
     ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_WAVE_CYCLES",
      "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"],
@@ -109,8 +112,9 @@ def source_digest(kernel: str) -> str:
 def _kernel_key(name: str):
     # the symbol as a whole identifier: compress_kernel is not decompress_kernel
     for k, sym in KERNEL_SYMBOL.items():
-        if re.search(r"(?<![A-Za-z0-9_])" + sym + r"(?![A-Za-z0-9_])", name):
-            return k
+        for s_ in (sym,) + KERNEL_ALIASES.get(k, ()):
+            if re.search(r"(?<![A-Za-z0-9_])" + s_ + r"(?![A-Za-z0-9_])", name):
+                return k
     return None
 
 

@@ -100,6 +100,7 @@ def test_kernel_stats_table_last_launches(tmp_path):
 
 def test_kernel_names_match_whole_symbols():
     assert bench._kernel_key("void gear::(anonymous namespace)::decompress_kernel<128, 4>(x)") == "decompress"
+    assert bench._kernel_key("void gear::(anonymous namespace)::decompress_mm_kernel<128, 4, 0, 4>(x)") == "decompress"
     assert bench._kernel_key(COMP) == "compress"
     assert bench._kernel_key("void at::native::elementwise_kernel<4>(x)") is None
 
