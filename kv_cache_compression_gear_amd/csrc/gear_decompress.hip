@@ -5,25 +5,22 @@
 // "Cites" list, sentence quoted under the Zafrir et al. entry: low-rank for the
 // coherent error, sparse for the outliers).
 //
-// HBM-bound streaming kernel.  A workgroup reconstructs a block of tokens of
-// one matrix: every lane
-// -- owning 8 consecutive columns of a token, D/8 lanes per token -- issues the
-// loads of all its tokens (one 32- or 16-bit code word, the group's scale and
-// zero, the token's A row) and the block's row pointers before computing.
-// The block's CSR entries (one contiguous range) are then loaded coalesced
-// into LDS and written into a dense fp16 LDS tile (each row's entries shared
-// out over kThreads / rows threads), read back as 8 values per lane; each lane
-// writes 8 fp16 values as one 16-byte store.
+// HBM-bound streaming kernels.  A workgroup reconstructs a block of tokens of
+// one matrix: every lane -- owning 8 consecutive columns of a token, D/8
+// lanes per token -- issues the loads of all its tokens (one 32- or 16-bit
+// code word, the group's scale and zero) and the block's row pointers and
+// CSR entries before computing, and writes 8 fp16 values as one 16-byte
+// store.  Without a low-rank term (decompress_kernel) the block's outliers
+// are scattered into a dense fp16 LDS tile and read back as 8 values per
+// lane; with one (decompress_mm_kernel) A B^T is taken on the matrix cores
+// into an fp32 LDS tile per 16-row step, into which that step's outliers are
+// added.
 #include "gear_internal.h"
 
 namespace gear {
 namespace {
 
-// token rows per lane: 8, or 4 with rank 8 (the A rows of all steps are held
-// in registers)
-constexpr int steps_for(int rk) { return rk >= 8 ? 4 : 8; }
 constexpr int kCsrCap = 1024;    // CSR entries of a block staged in LDS
-constexpr bool kMmLowRank = true;   // A B^T on the matrix cores (decompress_mm_kernel)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float h2f(uint32_t b) {
@@ -47,15 +44,13 @@ __device__ __forceinline__ float ubyte_f(uint32_t x) {
 // (GEAR's own); 1: groups of p.group tokens of a channel (KIVI keys; scale and
 // zero [rows / group][D]); 2: as 0, on a matrix whose channels were divided
 // by the factors p.chan (ZipCache), multiplied back here.
-template <int D, int RK, int QM, int BITS>
+// No low-rank term (rank 0).
+template <int D, int QM, int BITS>
 __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t* out, int64_t m0) {
-    constexpr int kSteps = steps_for(RK);
+    constexpr int kSteps = 8;
     constexpr int LPR = D / 8, RPS = 64 / LPR;
     constexpr int ROWS_STEP = 4 * RPS;
     constexpr int ROWS_WG = kSteps * ROWS_STEP;
-    constexpr int RKX = RK > 0 ? RK : 1;
-    // B as [e][colq][c]: lane colq reads B[colq * 8 + e][0..RKX) contiguously
-    __shared__ __attribute__((aligned(16))) float s_b[D * RKX];
     // S of the block's rows as a dense fp16 tile (the outliers are fp16 values)
     __shared__ __attribute__((aligned(16))) uint16_t s_s[ROWS_WG * D];
     __shared__ int32_t s_rp[ROWS_WG + 1];
@@ -72,7 +67,7 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
     const int64_t mm = m0 + group_id_x() / blocks_per_mat;
     const int row0 = (int)(group_id_x() % blocks_per_mat) * ROWS_WG;
     const int nrows = min(ROWS_WG, rows - row0);
-    const int r = p.rank, gl = p.group / 8, ngr = D / p.group;
+    const int gl = p.group / 8, ngr = D / p.group;
     constexpr int bits = BITS;   // (a template parameter: one load per code word)
 
     // Every load below is unconditional, from a clamped (always valid)
@@ -111,28 +106,14 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         wval[j] = ld_at<uint16_t>(vm, off);
     }
 
-    // B (D x r), one element per slot of B's padded rows, from a clamped
-    // column: issued with the first round so that staging it does not wait
-    // for the tokens' loads
-    constexpr int BPT = (D * RKX + kThreads - 1) / kThreads;
-    const int rl1 = max(r, 1) - 1;
-    const float* bsrc = RK > 0 ? p.B + (size_t)mm * D * r : p.scale;
-    float bv[BPT];
-#pragma unroll
-    for (int u = 0; u < BPT; ++u) {
-        const int i = min(tid + u * kThreads, D * RKX - 1);
-        bv[u] = RK > 0 ? ld_at<float>(bsrc, (uint32_t)((i / RKX) * r + min(i % RKX, rl1)) * 4u) : 0.0f;
-    }
-
     // issue the loads of all the lane's tokens first (clamped rows: always
     // valid addresses)
     const size_t mrow = (size_t)mm * rows + row0;
     const unsigned char* cbase = p.codes + mrow * (D * bits / 8);
     const float* sbase = p.scale + mrow * ngr;
     const float* zbase = p.zero + mrow * ngr;
-    const float* abase = p.A + mrow * r;
     uint32_t word[kSteps];
-    float sc[kSteps], zp[kSteps], ar[kSteps][RKX];
+    float sc[kSteps], zp[kSteps];
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         const int lr = s * ROWS_STEP + wv * RPS + rl;
@@ -144,25 +125,11 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
             sc[s] = ld_at<float>(sbase, go);
             zp[s] = ld_at<float>(zbase, go);
         }
-        // the A row, one load per slot from a clamped column (no branch on
-        // the rank: a load in a branch, or the join after it, is waited for
-        // there); slots past the rank repeat column r - 1 and meet the zero
-        // padding of B
-#pragma unroll
-        for (int c = 0; c < RKX; ++c)
-            ar[s][c] = RK > 0 ? ld_at<float>(abase, (tk * r + (uint32_t)min(c, rl1)) * 4) : 0.0f;
     }
 
     {
         uint4* t4 = reinterpret_cast<uint4*>(s_s);
         for (int i = tid; i < ROWS_WG * D / 8; i += kThreads) t4[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (RK > 0) {
-#pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int i = tid + u * kThreads, j = i / RKX, c = i % RKX;
-            if (i < D * RKX) s_b[((j % 8) * LPR + j / 8) * RKX + c] = c < r ? bv[u] : 0.0f;
-        }
     }
     if (tid <= nrows) s_rp[tid] = min(max(rpv0, 0), p.k);
     if (tid + kThreads <= nrows) s_rp[tid + kThreads] = min(max(rpv1, 0), p.k);
@@ -218,7 +185,6 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
             }
         }
     }
-    float Bm[8][RKX];
     float one = 1.0f;   // opaque 1: keeps the outlier add a single mixed fma
     asm volatile("" : "+s"(one));
     float cfac[8];      // QM 2: the channel factors of the lane's columns
@@ -228,11 +194,7 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         cfac[0] = f0.x, cfac[1] = f0.y, cfac[2] = f0.z, cfac[3] = f0.w;
         cfac[4] = f1.x, cfac[5] = f1.y, cfac[6] = f1.z, cfac[7] = f1.w;
     }
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int c = 0; c < RKX; ++c) Bm[e][c] = RK > 0 ? s_b[(e * LPR + colq) * RKX + c] : 0.0f;
+    __syncthreads();   // the dense tile is complete
 
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -265,9 +227,7 @@ __global__ void __launch_bounds__(kThreads) decompress_kernel(Packed p, uint16_t
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            float v = QM == 1 ? fmaf(cf[e], csc[e], czp[e]) : fmaf(cf[e], sc[s], zp[s]);
-#pragma unroll
-            for (int c = 0; c < RKX; ++c) v = fmaf(ar[s][c], Bm[e][c], v);
+            const float v = QM == 1 ? fmaf(cf[e], csc[e], czp[e]) : fmaf(cf[e], sc[s], zp[s]);
             // + the fp16 outlier value (fp16 operand of a mixed fma)
             x[e] = fmaf(h2f(sw[e >> 1] >> (16 * (e & 1))), one, v);
             if (QM == 2) x[e] *= cfac[e];   // a power of two: exact
@@ -521,7 +481,7 @@ __global__ void __launch_bounds__(kThreads) decompress_mm_kernel(Packed p, uint1
 
 template <int D, int RK, int QM>
 hipError_t launch_drq(const Packed& p, uint16_t* out, int64_t m0, int64_t m1, hipStream_t st) {
-    if constexpr (RK > 0 && kMmLowRank) {
+    if constexpr (RK > 0) {
         constexpr int ROWS_WG = 8 * 4 * (64 / (D / 8));
         const int64_t blocks = (m1 - m0) * ((p.rows + ROWS_WG - 1) / ROWS_WG);
         if (blocks <= 0) return hipSuccess;
@@ -534,19 +494,20 @@ hipError_t launch_drq(const Packed& p, uint16_t* out, int64_t m0, int64_t m1, hi
             hipLaunchKernelGGL((decompress_mm_kernel<D, RK, QM, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, st,
                                p, out, m0);
         return hipGetLastError();
+    } else {
+        constexpr int ROWS_WG = 8 * 4 * (64 / (D / 8));
+        const int64_t blocks = (m1 - m0) * ((p.rows + ROWS_WG - 1) / ROWS_WG);
+        if (blocks <= 0) return hipSuccess;
+        if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+        Timed t(kKDecompress, st);
+        if (p.bits == 4)
+            hipLaunchKernelGGL((decompress_kernel<D, QM, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
+                               out, m0);
+        else
+            hipLaunchKernelGGL((decompress_kernel<D, QM, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
+                               out, m0);
+        return hipGetLastError();
     }
-    constexpr int ROWS_WG = steps_for(RK) * 4 * (64 / (D / 8));
-    const int64_t blocks = (m1 - m0) * ((p.rows + ROWS_WG - 1) / ROWS_WG);
-    if (blocks <= 0) return hipSuccess;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    Timed t(kKDecompress, st);
-    if (p.bits == 4)
-        hipLaunchKernelGGL((decompress_kernel<D, RK, QM, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
-                           out, m0);
-    else
-        hipLaunchKernelGGL((decompress_kernel<D, RK, QM, 2>), dim3((unsigned)blocks), dim3(kThreads), 0, st, p,
-                           out, m0);
-    return hipGetLastError();
 }
 
 template <int D, int RK>
