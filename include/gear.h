@@ -136,7 +136,8 @@ typedef struct {
  *   scale   f32 [M][rows][head_dim/group]   (KIVI keys: [M][rows/group][head_dim])
  *   zero    f32 [M][rows][head_dim/group]   (= group minimum; layout as scale)
  *   row_ptr i32 [M][rows+1]                 CSR of S, offsets into col/val of
- *                                           the same matrix; row_ptr[rows] = k
+ *                                           the same matrix; row_ptr[0] = 0,
+ *                                           row_ptr[rows] = k
  *   col     u16 [M][k]                      ascending within a token
  *   val     f16 [M][k]                      the original entries, exact
  *   A       f32 [M][rows][rank]

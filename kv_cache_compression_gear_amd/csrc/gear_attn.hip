@@ -297,8 +297,15 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     auto stage_issue = [&](const Packed& p, int64_t m, int row0, int len) {
         const int32_t* rp = p.row_ptr + (size_t)m * (p.rows + 1) + row0;
         const int kk = p.k;
-        csr_beg = min(max(rp[0], 0), kk);
-        csr_cnt = max(min(max(rp[len], 0), kk) - csr_beg, 0);
+        if (row0 == 0 && len == p.rows) {
+            // a whole matrix (every fill): its range is [0, k), known without
+            // waiting for its row pointers at both ends
+            csr_beg = 0;
+            csr_cnt = kk;
+        } else {
+            csr_beg = min(max(rp[0], 0), kk);
+            csr_cnt = max(min(max(rp[len], 0), kk) - csr_beg, 0);
+        }
         csr_staged = csr_cnt <= kAttnCsrCap;
         st_rp0 = ld_at<int32_t>(rp, (uint32_t)min(tid, len) * 4u);
         st_rp1 = ld_at<int32_t>(rp, (uint32_t)min(tid + kThreads, len) * 4u);
@@ -402,25 +409,25 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             stage_issue(p, pc.mk, pc.row0, pc.len);
             load(0, 0);
             stage_store(p, pc.len);
-            if (r > 0 && wv == 0) {
-                // B^T q: one token row of lanes spans all D columns
-                for (int c = 0; c < r; ++c) {
-                    float part[G];
+            if (r > 0) {
+                // B^T q: row group g = wv RPS + rl (one token row of lanes
+                // spans all D columns) takes rank column g, all at once (B is
+                // zero-padded to kMaxRank columns in LDS)
+                static_assert(kThreads / LPR >= kMaxRank, "a row group per rank column");
+                const int g = wv * RPS + rl, c = min(g, kMaxRank - 1);
+                float part[G];
 #pragma unroll
-                    for (int h = 0; h < G; ++h) part[h] = 0.0f;
-                    if (rl == 0) {
+                for (int h = 0; h < G; ++h) part[h] = 0.0f;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float bv = s_bm[(colq * 8 + e) * kMaxRank + c] * fk[e];
+                for (int e = 0; e < 8; ++e) {
+                    const float bv = s_bm[(colq * 8 + e) * kMaxRank + c] * fk[e];
 #pragma unroll
-                            for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], bv, part[h]);
-                        }
-                    }
+                    for (int h = 0; h < G; ++h) part[h] = fmaf(q[h][e], bv, part[h]);
+                }
 #pragma unroll
-                    for (int h = 0; h < G; ++h) {
-                        const float v = row_allreduce<LPR>(part[h]);
-                        if (lane == 0) s_qb[h * kMaxRank + c] = v;
-                    }
+                for (int h = 0; h < G; ++h) {
+                    const float v = row_allreduce<LPR>(part[h]);
+                    if (g < r && colq == 0) s_qb[h * kMaxRank + c] = v;
                 }
             }
             __syncthreads();
@@ -473,20 +480,31 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                 compute(0, s0);
             }
             __syncthreads();
-            // sparse term, one thread per token, entries in CSR order
-            for (int i = tid; i < pc.len; i += kThreads) {
+            // sparse term: four threads per token (every fourth entry, in CSR
+            // order), their sums added within the quad
+            for (int i0 = 0; i0 < pc.len; i0 += kThreads / 4) {   // (workgroup-uniform)
+                const int i = i0 + tid / 4, sub = tid & 3;
                 float add[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h) add[h] = 0.0f;
-                for (int k = s_rp[i]; k < s_rp[i + 1]; ++k) {
-                    const uint32_t cv = csr_entry(p, pc.mk, k);
-                    const int cj = (int)(cv & (D - 1));
-                    const float v = h2f(cv >> 16) * (p.chan ? p.chan[(size_t)pc.mk * D + cj] : 1.0f);
+                if (i < pc.len) {
+                    for (int k = s_rp[i] + sub; k < s_rp[i + 1]; k += 4) {
+                        const uint32_t cv = csr_entry(p, pc.mk, k);
+                        const int cj = (int)(cv & (D - 1));
+                        const float v = h2f(cv >> 16) * (p.chan ? p.chan[(size_t)pc.mk * D + cj] : 1.0f);
 #pragma unroll
-                    for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
+                        for (int h = 0; h < G; ++h) add[h] = fmaf(s_q[h * D + cj], v, add[h]);
+                    }
                 }
 #pragma unroll
-                for (int h = 0; h < G; ++h) s_sc[(base + i) * G + h] += add[h];
+                for (int h = 0; h < G; ++h) {
+                    add[h] += dpp<0xB1>(add[h]);   // quad_perm(1,0,3,2)
+                    add[h] += dpp<0x4E>(add[h]);   // quad_perm(2,3,0,1)
+                }
+                if (i < pc.len && sub == 0) {
+#pragma unroll
+                    for (int h = 0; h < G; ++h) s_sc[(base + i) * G + h] += add[h];
+                }
             }
         } else {
             // 4 steps' rows loaded together (clamped rows, unconditional: a
@@ -541,9 +559,14 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
     }
     __syncthreads();
 
-    // ---------------- softmax inside the split (scores scaled here)
+    // ---------------- softmax inside the split (scores scaled here).  The
+    // waves' maxima go to s_red[0, 4G) and their sums to s_red[4G, 8G); every
+    // thread combines the four maxima itself, so that two barriers suffice
+    // (the total sum, in s_stat, is read only after phase 2's barriers).
     const int n = max(t1 - t0, 0);
     {
+        float* s_wmax = s_red;
+        float* s_wsum = s_red + 4 * G;
         float mx[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) mx[h] = -INFINITY;
@@ -556,37 +579,34 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) mx[h] = fmaxf(mx[h], __shfl_xor(mx[h], off, 64));
-            if (lane == 0) s_red[wv * G + h] = mx[h];
+            mx[h] = wave_max(mx[h]);
+            if (lane == 0) s_wmax[wv * G + h] = mx[h];
         }
         __syncthreads();
-        if (tid < G) {
-            float m = s_red[tid];
-            for (int w = 1; w < 4; ++w) m = fmaxf(m, s_red[w * G + tid]);
-            s_stat[tid] = m;
-        }
-        __syncthreads();
-        float sm[G];
+        auto max4 = [&](int h) {
+            return fmaxf(fmaxf(s_wmax[h], s_wmax[G + h]), fmaxf(s_wmax[2 * G + h], s_wmax[3 * G + h]));
+        };
+        float gm[G], sm[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) sm[h] = 0.0f;
+        for (int h = 0; h < G; ++h) {
+            gm[h] = max4(h);
+            sm[h] = 0.0f;
+        }
+        if (tid < G) s_stat[tid] = max4(tid);
         for (int i = tid; i < n; i += kThreads)
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float pv = expf(s_sc[i * G + h] - s_stat[h]);
+                const float pv = expf(s_sc[i * G + h] - gm[h]);
                 s_sc[i * G + h] = pv;
                 sm[h] += pv;
             }
-        __syncthreads();
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) sm[h] += __shfl_xor(sm[h], off, 64);
-            if (lane == 0) s_red[wv * G + h] = sm[h];
+            sm[h] = wave_sum(sm[h]);
+            if (lane == 0) s_wsum[wv * G + h] = sm[h];
         }
         __syncthreads();
-        if (tid < G) s_stat[G + tid] = s_red[tid] + s_red[G + tid] + s_red[2 * G + tid] + s_red[3 * G + tid];
-        __syncthreads();
+        if (tid < G) s_stat[G + tid] = s_wsum[tid] + s_wsum[G + tid] + s_wsum[2 * G + tid] + s_wsum[3 * G + tid];
     }
 
     // ---------------- phase 2: probability-weighted sum of V^
@@ -668,7 +688,17 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                         for (int i = 0; i < RPS - 1; ++i) rr += k >= rs[i] ? 1 : 0;
                         return rr;
                     };
-                    for (int k = e0 + lane; k < e1; k += 64) {
+                    // (the lane's first entry is kept for the clearing, which
+                    // then reads no entry again; a step rarely has more than
+                    // 64 entries)
+                    const int k0 = e0 + lane;
+                    int cell0 = -1;
+                    if (k0 < e1) {
+                        const uint32_t cv = csr_entry(p, pc.mv, k0);
+                        cell0 = row_of(k0) * D + (int)(cv & (D - 1));
+                        tile[cell0] = h2f(cv >> 16);
+                    }
+                    for (int k = k0 + 64; k < e1; k += 64) {
                         const uint32_t cv = csr_entry(p, pc.mv, k);
                         tile[row_of(k) * D + (cv & (D - 1))] = h2f(cv >> 16);
                     }
@@ -677,7 +707,8 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
                     const float4 s1v = *reinterpret_cast<const float4*>(tile + rl * D + colq * 8 + 4);
                     const float sv[8] = {s0v.x, s0v.y, s0v.z, s0v.w, s1v.x, s1v.y, s1v.z, s1v.w};
                     __builtin_amdgcn_wave_barrier();
-                    for (int k = e0 + lane; k < e1; k += 64) {
+                    if (cell0 >= 0) tile[cell0] = 0.0f;
+                    for (int k = k0 + 64; k < e1; k += 64) {
                         const uint32_t cv = csr_entry(p, pc.mv, k);
                         tile[row_of(k) * D + (cv & (D - 1))] = 0.0f;
                     }
@@ -702,9 +733,7 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
             // low-rank part of this matrix: acc += B (sum_t p_t A_t), with the
             // sums over the piece's tokens gathered per rank column c = colq
 #pragma unroll
-            for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-                for (int h = 0; h < G; ++h) pa[h] += __shfl_xor(pa[h], off, 64);
+            for (int h = 0; h < G; ++h) pa[h] = sum_rowgroups<LPR>(pa[h]);
             if (rl == 0 && colq < r) {
 #pragma unroll
                 for (int h = 0; h < G; ++h) s_pa[(wv * G + h) * kMaxRank + colq] = pa[h];
@@ -767,13 +796,12 @@ __global__ void __launch_bounds__(kThreads) attn_split_kernel(AttnArgs a) {
         }
         t += pc.len;
     }
-    // reduce over the row groups of the wave, then over the waves
+    // reduce over the row groups of the wave (lane swaps, no LDS), then over
+    // the waves
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
+    for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off, 64);
+        for (int e = 0; e < 8; ++e) acc[h][e] = sum_rowgroups<LPR>(acc[h][e]);
     __syncthreads();
     if (rl == 0) {
 #pragma unroll
