@@ -1325,7 +1325,10 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
     // all of B's rows in registers)
     constexpr bool VPATH = RK <= 4 && ONEG;
     float Bv[VPATH ? 1 : CPL];                // MFMA B operand: Bf[c0 + j][n = rr]
-    __shared__ __attribute__((aligned(16))) float s_bm[VPATH ? D * 4 : 4];   // Bf rows, padded to 4
+    // Bf rows, padded to 4 columns, one empty row after every CPL rows: the
+    // four lane groups read rows CPL apart at once, which would otherwise
+    // fall on the same LDS banks
+    __shared__ __attribute__((aligned(16))) float s_bm[VPATH ? (D + D / CPL) * 4 : 4];
     // CH: the per-channel scales and zeros of the token groups of this
     // workgroup's rows (groups of at least 16 tokens: a 16-row step lies in one)
     constexpr int kChG = CH ? ROWS_WG / 16 : 1;
@@ -1348,7 +1351,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
             f4v v = {0.0f, 0.0f, 0.0f, 0.0f};
             if (RK == 4) v = *reinterpret_cast<const f4v*>(src);
             else v = f4v{src[0], src[1], 0.0f, 0.0f};
-            reinterpret_cast<f4v*>(s_bm)[tid] = v;
+            reinterpret_cast<f4v*>(s_bm)[tid + tid / CPL] = v;
         }
         __syncthreads();
     } else {
@@ -1507,7 +1510,7 @@ __global__ void __launch_bounds__(kThreads) lowrank_a_kernel(CompressArgs a) {
                 const float xz = fmaf(h2f(dm[e >> 1] >> (16 * (e & 1))), one, -zpv);
                 const float R = fmaf(-cf[e], scv, xz);
                 if constexpr (VPATH) {
-                    const f4v bm = reinterpret_cast<const f4v*>(s_bm)[c0 + jj];
+                    const f4v bm = reinterpret_cast<const f4v*>(s_bm)[c0 + jj + q];
 #pragma unroll
                     for (int c2 = 0; c2 < RK; ++c2) av[c2] = fmaf(R, bm[c2], av[c2]);
                 } else {
