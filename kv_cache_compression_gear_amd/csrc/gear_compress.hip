@@ -571,12 +571,13 @@ __global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
 // and forms the residual R = D - deq(Q).  With a low-rank term, R (scaled by
 // 2^ex so that fp16 covers it) is split into fp16 hi + lo parts and written
 // row-major into an LDS slab; after a workgroup barrier every wave adds its
-// share of the 32x32 blocks of C = R^T R over the slab with
-// v_mfma_f32_32x32x16_f16 (hi*hi + hi*lo + lo*hi; the products are exact in
-// fp32, lo*lo is below 2^-22 of the total).  The operands are read with
-// ds_read_b64_tr_b16, which turns the row-major slab into the MFMA's
-// "8 consecutive k per lane" layout; chunks of 8 bytes are XOR-swizzled by row
-// so that the transposing reads hit distinct LDS banks.
+// share of the 16x16 blocks of C = R^T R over the slab with
+// v_mfma_f32_16x16x32_f16 (hi*hi + hi*lo + lo*hi; the products are exact in
+// fp32, lo*lo is below 2^-22 of the total), nine blocks per SIMD at d = 128.
+// The operands are read with ds_read_b64_tr_b16, which turns the row-major
+// slab into the MFMA's "8 consecutive k per lane" layout; chunks of 8 bytes
+// are XOR-swizzled by row so that the transposing reads hit distinct LDS
+// banks.
 //
 // After the pass C is in LDS and the t power steps of the PowerSGD-style fit
 // run on it in fp64: W = C B (= R^T P with P = R B), G = B^T W (= P^T P),
@@ -590,6 +591,7 @@ typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 typedef short s4v __attribute__((ext_vector_type(4)));
 typedef float f16v __attribute__((ext_vector_type(16)));
+typedef float f4v __attribute__((ext_vector_type(4)));
 typedef short s2v __attribute__((ext_vector_type(2)));
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) s4v lds_s4v;
@@ -598,22 +600,27 @@ constexpr int kSlabRows = 64;     // 8 rows from each of the 8 waves
 constexpr int kWaveSlab = kSlabRows / kCompressWaves;
 constexpr int kCompressThreads = kCompressWaves * 64;
 
-// 8-byte chunk c8 of slab row `row`, XOR-swizzled: the 4 rows a half-wave
-// reads in one transposing load land in 4 disjoint groups of 16 banks.
+// 8-byte chunk c8 of slab row `row`, XOR-swizzled so that the transposing
+// loads below are free of bank conflicts: at d = 128 the 16 lanes of a group
+// read 16 distinct chunks of 4 rows, and the two groups of a half-wave
+// (rows 8 apart) the other half of the banks (bit 2 of the chunk flipped
+// by bit 3 of the row).  Bit 0 is never changed, so a lane's 16-byte store
+// of chunks 2c, 2c + 1 stays contiguous.
 template <int D>
 __device__ __forceinline__ int swz_chunk(int row, int c8) {
-    return D == 128 ? (c8 ^ ((row & 3) << 3)) : (c8 ^ (((row >> 1) & 1) << 3));
+    return D == 128 ? (c8 ^ ((row & 3) << 3) ^ (((row >> 3) & 1) << 2)) : (c8 ^ (((row >> 1) & 1) << 3));
 }
 
-// MFMA operand for columns [cb, cb + 32) over slab rows [kb, kb + 16): lane l
-// receives R[kb + 8 (l / 32) + i][cb + l % 32], i = 0..7.  Each transposing
-// load serves 4 rows: within a group of 16 lanes, lane p supplies the address
-// of 4 consecutive columns of row p / 4 and receives column p of the 4 rows.
+// Operand of v_mfma_f32_16x16x32_f16 (either side) for columns [16 X,
+// 16 X + 16) over slab rows [kb, kb + 32): lane l receives
+// R[kb + 8 (l / 16) + i][16 X + l % 16], i = 0..7.  Each transposing load
+// serves 4 rows: within a group of 16 lanes, lane p supplies the address of 4
+// consecutive columns of row p / 4 and receives column p of the 4 rows.
 template <int D>
-__device__ __forceinline__ h8v read_operand(const unsigned char* plane, int kb, int cb, int lane) {
+__device__ __forceinline__ h8v read_operand(const unsigned char* plane, int kb, int X, int lane) {
     const int g = lane >> 4, p = lane & 15;
-    const int c8 = (cb + 16 * (g & 1) + 4 * (p & 3)) >> 2;
-    const int r0 = kb + 8 * (g >> 1) + (p >> 2);
+    const int c8 = 4 * X + (p & 3);
+    const int r0 = kb + 8 * g + (p >> 2);
     const int r1 = r0 + 4;
     const s4v v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s4v*)(plane + r0 * (D * 2) + swz_chunk<D>(r0, c8) * 8));
@@ -623,61 +630,61 @@ __device__ __forceinline__ h8v read_operand(const unsigned char* plane, int kb, 
                                    0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-__device__ __forceinline__ f16v mma3(const h8v& hi_i, const h8v& lo_i, const h8v& hi_j,
-                                     const h8v& lo_j, f16v acc) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi_i, hi_j, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(hi_i, lo_j, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(lo_i, hi_j, acc, 0, 0, 0);
+// The three products that make R_I^T R_J exact in fp32 from the hi and lo
+// parts (lo^T lo is below 2^-22 of the total).
+__device__ __forceinline__ f4v mma3(const h8v& hi_i, const h8v& lo_i, const h8v& hi_j,
+                                    const h8v& lo_j, f4v acc) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi_i, hi_j, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(hi_i, lo_j, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(lo_i, hi_j, acc, 0, 0, 0);
     return acc;
 }
 
-// This wave's 32x32 blocks of C = R^T R, in column units of 32: a diagonal
-// block (X, X) and/or an off-diagonal block (X, Y) (C is symmetric, so (X, Y)
-// also gives (Y, X)).  D = 128 (10 blocks): waves 0..3 take (w, w) and
-// (w, (w + 1) mod 4), waves 4 and 5 take (w - 4, w - 2).  D = 64 (3 blocks):
-// wave 0 takes (0, 0), wave 1 (0, 1), wave 2 (1, 1).
-struct WaveBlocks {
-    int X, Y;
-    bool diag, off;
-};
+// Gram blocks of 16 x 16 over NCB = D / 16 column blocks: the NCB (NCB + 1) / 2
+// unordered pairs {i, j}, taken as {q, q + b mod NCB}.  Wave q < NCB takes
+// b = 0 .. NCB / 2 - 1, and the waves q < NCB / 2 also {q, q + NCB / 2}: at
+// d = 128 five or four blocks per wave, nine per SIMD (waves q and q + 4
+// share one).  A wave's first operand (column block q) is read once per
+// 32-row chunk and serves all of its blocks.
 template <int D>
-__device__ __forceinline__ WaveBlocks wave_blocks(int wv) {
-    if (D == 128) {
-        if (wv < 4) return {wv, (wv + 1) & 3, true, true};
-        return {wv - 4, wv - 2, false, wv < 6};
-    }
-    return {wv == 2 ? 1 : 0, 1, wv != 1 && wv < 3, wv == 1};
+struct GramPlan {
+    static constexpr int NCB = D / 16, HC = NCB / 2, NBW = HC + 1;
+};
+// Block b of wave q: rows i, columns j; false if the wave has no block b.
+template <int D>
+__device__ __forceinline__ bool gram_block(int q, int b, int& i, int& j) {
+    constexpr int NCB = GramPlan<D>::NCB, HC = GramPlan<D>::HC;
+    i = q;
+    j = (q + b) % NCB;
+    return q < NCB && (b < HC || q < HC);
 }
 
-// This wave's Gram blocks over one slab: acc[0] += the diagonal block,
-// acc[1] += the off-diagonal one.  Per 16-row chunk the hi and lo operands of
-// column blocks X (and Y) are read once, and the next chunk's operands are
-// read while this chunk's MFMAs run (two register sets, alternating).  Each
-// accumulator has one update, skipped or not as a whole (wave-uniform), and
-// never a choice between two updates: the compiler would give the two their
-// own registers and copy the result back, waiting for the MFMAs to finish.
+// This wave's Gram blocks over one 64-row slab (two 32-row chunks).
 template <int D>
-__device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane, f16v (&acc)[2]) {
+__device__ __forceinline__ void slab_mma(const unsigned char* slab, int wv, int lane,
+                                         f4v (&acc)[GramPlan<D>::NBW]) {
     constexpr int kPlane = kSlabRows * D * 2;
+    constexpr int NCB = GramPlan<D>::NCB, HC = GramPlan<D>::HC;
     const unsigned char* hi = slab;
     const unsigned char* lo = slab + kPlane;
-    const WaveBlocks wb = wave_blocks<D>(wv);
-    h8v xh[2], xl[2], yh[2], yl[2];
-    auto rd = [&](int kc, int buf, bool withY) {
-        xh[buf] = read_operand<D>(hi, 16 * kc, 32 * wb.X, lane);
-        xl[buf] = read_operand<D>(lo, 16 * kc, 32 * wb.X, lane);
-        if (withY) {
-            yh[buf] = read_operand<D>(hi, 16 * kc, 32 * wb.Y, lane);
-            yl[buf] = read_operand<D>(lo, 16 * kc, 32 * wb.Y, lane);
-        }
-    };
-    rd(0, 0, wb.off);
+    const int q = wv;
+    if (q >= NCB) return;   // wave-uniform
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-        const int c = kc & 1;
-        if (kc < 3) rd(kc + 1, c ^ 1, wb.off);
-        if (wb.diag) acc[0] = mma3(xh[c], xl[c], xh[c], xl[c], acc[0]);
-        if (wb.off) acc[1] = mma3(xh[c], xl[c], yh[c], yl[c], acc[1]);
+    for (int kc = 0; kc < 2; ++kc) {
+        const int kb = 32 * kc;
+        const h8v ah = read_operand<D>(hi, kb, q, lane), al = read_operand<D>(lo, kb, q, lane);
+        acc[0] = mma3(ah, al, ah, al, acc[0]);
+#pragma unroll
+        for (int b = 1; b < HC; ++b) {
+            const int j = (q + b) % NCB;
+            const h8v bh = read_operand<D>(hi, kb, j, lane), bl = read_operand<D>(lo, kb, j, lane);
+            acc[b] = mma3(ah, al, bh, bl, acc[b]);
+        }
+        if (q < HC) {   // wave-uniform
+            const int j = q + HC;
+            const h8v bh = read_operand<D>(hi, kb, j, lane), bl = read_operand<D>(lo, kb, j, lane);
+            acc[HC] = mma3(ah, al, bh, bl, acc[HC]);
+        }
     }
 }
 
@@ -827,11 +834,10 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     int32_t* rp = o.row_ptr + (size_t)mm * (rows + 1);
     uint16_t* cm = o.col + (size_t)mm * kk;
     uint16_t* vm = o.val + (size_t)mm * kk;
-    f16v acc[2];
+    constexpr int NBW = GramPlan<D>::NBW;
+    f4v acc[NBW];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+    for (int b = 0; b < NBW; ++b) acc[b] = f4v{0.0f, 0.0f, 0.0f, 0.0f};
     uint32_t ties_seen = 0;
 
     // per-channel parameters (CH) of the group the wave's slab slice lies in
@@ -870,9 +876,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             if (exs < ex) {
                 const float f = pow2f(2 * (exs - ex));   // >= 2^-80: exact
 #pragma unroll
-                for (int b = 0; b < 2; ++b)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[b][v] *= f;
+                for (int b = 0; b < NBW; ++b) acc[b] *= f;
                 ex = exs;
                 sx = pow2f(ex);
                 rsx = pow2f(-ex);
@@ -1129,16 +1133,16 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     __syncthreads();
     float* Cm = reinterpret_cast<float*>(s_big);
     {
-        const WaveBlocks wb = wave_blocks<D>(wv);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            if (!(b == 0 ? wb.diag : wb.off)) continue;
-            const int I = wb.X, J = b == 0 ? wb.X : wb.Y;
+        for (int b = 0; b < NBW; ++b) {
+            int I, J;
+            if (!gram_block<D>(wv, b, I, J)) continue;   // wave-uniform
+            // lane l holds rows 4 (l / 16) + v, column l % 16 of the block
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = 8 * (v / 4) + 4 * (lane / 32) + (v % 4), n = lane % 32;
-                Cm[(32 * I + m) * D + 32 * J + n] = acc[b][v];
-                if (I != J) Cm[(32 * J + n) * D + 32 * I + m] = acc[b][v];
+            for (int v = 0; v < 4; ++v) {
+                const int m = 4 * (lane / 16) + v, n = lane % 16;
+                Cm[(16 * I + m) * D + 16 * J + n] = acc[b][v];
+                if (I != J) Cm[(16 * J + n) * D + 16 * I + m] = acc[b][v];
             }
         }
     }
