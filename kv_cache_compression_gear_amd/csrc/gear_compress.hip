@@ -570,8 +570,9 @@ __global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
 // applies the outlier mask, emits the row's CSR entries, quantizes the groups
 // and forms the residual R = D - deq(Q).  With a low-rank term, R (scaled by
 // 2^ex so that fp16 covers it) is split into fp16 hi + lo parts and written
-// row-major into an LDS slab; after a workgroup barrier every wave adds its
-// share of the 16x16 blocks of C = R^T R over the slab with
+// row-major into an LDS slab; after a workgroup barrier, and issued among the
+// next slab's vector work, every wave adds its share of the 16x16 blocks of
+// C = R^T R over the slab with
 // v_mfma_f32_16x16x32_f16 (hi*hi + hi*lo + lo*hi; the products are exact in
 // fp32, lo*lo is below 2^-22 of the total), nine blocks per SIMD at d = 128.
 // The operands are read with ds_read_b64_tr_b16, which turns the row-major
@@ -865,6 +866,12 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
 
     auto do_slab = [&](const uint4 (&xr)[SS], const uint4 (&xn)[SS], int sl) {
         unsigned char* slab = s_big + (sl & 1) * 2 * kPlane;
+        // The Gram products of the previous slab (complete in LDS since the
+        // barrier that ended it) are issued inside this slab's vector work;
+        // a change of the running exponent rescales the accumulators after
+        // them (they are in the previous slab's units).
+        const unsigned char* prev = s_big + ((sl + 1) & 1) * 2 * kPlane;
+        float accf = 1.0f;   // rescaling of the accumulators, wave-uniform
         float chsc[8], chzp[8];
         if constexpr (CH) load_chp(chsc, chzp, sl);
         if (slab_ex) {   // wave-uniform
@@ -874,9 +881,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 max(max(max(e0.x, e0.y), max(e0.z, e0.w)), max(max(e1.x, e1.y), max(e1.z, e1.w))));
             const int exs = key == 0u ? kExNone : residual_exponent(h2f(key));
             if (exs < ex) {
-                const float f = pow2f(2 * (exs - ex));   // >= 2^-80: exact
-#pragma unroll
-                for (int b = 0; b < NBW; ++b) acc[b] *= f;
+                accf = pow2f(2 * (exs - ex));   // >= 2^-80: exact
                 ex = exs;
                 sx = pow2f(ex);
                 rsx = pow2f(-ex);
@@ -986,6 +991,11 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
                 const int row = wr0 + sl * kWaveSlab + u * RPS + rl;
                 if (row < rows && colq == 0) st_at<int32_t>(rp, (uint32_t)row * 4, 0);
             }
+        }
+        if (LR && sl > 0) slab_mma<D>(prev, wv, lane, acc);
+        if (accf != 1.0f) {   // wave-uniform
+#pragma unroll
+            for (int b = 0; b < NBW; ++b) acc[b] *= accf;
         }
 #pragma unroll
         for (int u = 0; u < SS; ++u) {
@@ -1105,7 +1115,6 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
         if (LR) {
             if (slab_ex && lane == 0) s_ex[(sl + 1) & 1][wv] = wave_max_key<SS>(xn);
             __syncthreads();
-            slab_mma<D>(slab, wv, lane, acc);
         }
     };
 
@@ -1126,6 +1135,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
             }
         }
     }
+    if (LR && nslab > 0) slab_mma<D>(s_big + ((nslab - 1) & 1) * 2 * kPlane, wv, lane, acc);
     if (tid == 0) rp[rows] = (int32_t)kk;
     if (!LR) return;
 
