@@ -252,15 +252,20 @@ def test_gear_l_exponent_falls_mid_matrix():
     """Without outliers the residual's scaling comes from each 64-row slab's
     largest |x| and only decreases: magnitudes growing down the rows (the
     exponent falls at almost every slab), 1000 zero rows before the data,
-    and one large slab between small ones."""
+    one large slab between small ones, and one large row in the last slab."""
     rng = np.random.default_rng(33)
     n, d = 4096, 128
-    z = rng.standard_normal((3, n, d))
+    z = rng.standard_normal((4, n, d))
     x = np.empty_like(z)
     x[0] = z[0] * np.exp2(np.arange(n) / 512.0)[:, None] * 1e-3
     x[1] = z[1]
     x[1, :1000] = 0.0
     x[2] = z[2] * 1e-3
     x[2, 2048:2112] = z[2, 2048:2112] * 300.0
+    # a large row in the last 64-row slab only (the last rows of the first
+    # wave's block): the exponent falls there, after every earlier slab's
+    # Gram products were taken in the larger units
+    x[3] = z[3] * 1e-3
+    x[3, 511] = z[3, 511] * 300.0
     _run_x("GEAR-L falling exponent", _f16_bits(x), P(4, 128, 0, 4, 3))
     _run_x("GEAR-L falling exponent, 2-bit rank 8", _f16_bits(x), P(2, 64, 0, 8, 2))
