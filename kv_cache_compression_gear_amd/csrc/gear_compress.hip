@@ -303,7 +303,11 @@ __global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
         }
     };
 
-    // ---- sample: every 16th step of each wave's range
+    // ---- sample: every 16th step of each wave's range.  The window pass's
+    // first batch is issued here too, so that it is in flight while the
+    // sample's histogram is built and searched.
+    uint4 xw0[U];
+    bool okw0[U];
     uint32_t nsamp = 0;
     for (int s0 = sb; s0 < se; s0 += 4 * kSampleEvery) {   // 4 sampled rows in flight
         uint4 xr[4];
@@ -316,6 +320,7 @@ __global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
             const uint32_t rc = (uint32_t)min(row, rows - 1);
             xr[q] = ld_at<uint4>(xm, (rc * D + colq * 8) * 2);
         }
+        if (s0 == sb) load(xw0, okw0, sb);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (!ok[q]) continue;
@@ -380,7 +385,12 @@ __global__ void __launch_bounds__(NT, NT / 128) select_kernel(CompressArgs a) {
     {
         uint4 xa[U], xb[U];
         bool oka[U], okb[U];
-        load(xa, oka, sb);
+        if (sb >= se) load(xw0, okw0, sb);   // (no sample loop ran: an empty range)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            xa[u] = xw0[u];
+            oka[u] = okw0[u];
+        }
         for (int s0 = sb; s0 < se; s0 += 2 * U) {
             load(xb, okb, s0 + U);
             window(xa, oka);
