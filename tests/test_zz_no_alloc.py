@@ -53,3 +53,40 @@ def test_noalloc_compress_matches_workspace_compress(order):
         xb = gear.decompress(got).float()
         torch.cuda.synchronize()
         assert torch.equal(xa, xb)
+
+
+def test_noalloc_compress_and_decompress_under_graph_capture():
+    """The callers the allocation-free entry point is for: compress (no
+    workspace) and decompress captured into one HIP graph and replayed three
+    times, the program's own eager work and synchronisations in between; every
+    replay gives the eager call's packed bytes and reconstruction exactly."""
+    p = gear.Params(4, 128, 20000, 4, 3)
+    x = _stack(2, 4, 1024, 128, 4, 7)
+    M, n, d = x.shape
+    L = gear.packed_layout(p, M, n, d)
+    ref = gear.compress(x, p)
+    ref_x = gear.decompress(ref)
+    pk = gear.Packed(torch.empty(L.total_bytes, dtype=torch.uint8, device="cuda"), p, M, n, d, L)
+    xh = torch.empty_like(x)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # first calls (the scratch address lookup) outside the capture
+        gear.compress_noalloc(x, p, out=pk)
+        gear.decompress(pk, out=xh)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        gear.compress_noalloc(x, p, out=pk)
+        gear.decompress(pk, out=xh)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        _say(f"[noalloc graph] replay {rep}")
+        pk.buf.fill_(0xAB)
+        xh.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ref.sections(), pk.sections())):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"section {i} differs (replay {rep})"
+        assert torch.equal(xh.view(torch.int16), ref_x.view(torch.int16)), f"reconstruction differs (replay {rep})"
