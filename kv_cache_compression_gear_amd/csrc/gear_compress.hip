@@ -777,7 +777,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
     constexpr int kBig = LR ? (4 * kPlane > D * D * 4 ? 4 * kPlane : D * D * 4) : 16;
     __shared__ __attribute__((aligned(16))) unsigned char s_big[kBig];  // 2 slabs, then C
     __shared__ float s_b[LR ? D * RKX : 1];
-    __shared__ double s_w[LR ? (NH - 1) * D * RKX : 1];
+    __shared__ double s_w[LR ? (NH - 1) * D * RKX : 1];   // [part][c][j]: a wave's j contiguous
     __shared__ double s_g[RKX * RKX];
     __shared__ double s_m[RKX * RKX];
     __shared__ uint32_t s_ex[2][kCompressWaves];   // per slab: each wave's largest key
@@ -1200,20 +1200,20 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
         }
         if (h > 0 && h < NH) {
 #pragma unroll
-            for (int c = 0; c < RKX; ++c) s_w[((h - 1) * D + j) * RKX + c] = wp[c];
+            for (int c = 0; c < RKX; ++c) s_w[((h - 1) * RKX + c) * D + j] = wp[c];
         }
         __syncthreads();
         if (h == 0) {
             for (int hh = 1; hh < NH; ++hh)
 #pragma unroll
-                for (int c = 0; c < RKX; ++c) wp[c] += s_w[((hh - 1) * D + j) * RKX + c];
+                for (int c = 0; c < RKX; ++c) wp[c] += s_w[((hh - 1) * RKX + c) * D + j];
 #pragma unroll
             for (int c = 0; c < RKX; ++c) wp[c] *= cscale;
         }
         __syncthreads();
         if (h == 0) {
 #pragma unroll
-            for (int c = 0; c < RKX; ++c) s_w[j * RKX + c] = wp[c];
+            for (int c = 0; c < RKX; ++c) s_w[c * D + j] = wp[c];
         }
         __syncthreads();
         if (tid < NP * LPP) {   // whole aligned groups of LPP lanes
@@ -1228,7 +1228,7 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
 #pragma unroll 4
             for (int i = 0; i < D / LPP; ++i) {
                 const int jj = sub + LPP * i;
-                g += (double)s_b[jj * RKX + c1] * s_w[jj * RKX + c2];
+                g += (double)s_b[jj * RKX + c1] * s_w[c2 * D + jj];
             }
             g = row_sum64<LPP>(g);
             if (sub == 0) {
