@@ -1190,12 +1190,21 @@ __global__ void __launch_bounds__(kCompressThreads, 4) compress_kernel(CompressA
 #pragma unroll
         for (int c = 0; c < RKX; ++c) wp[c] = 0.0;
         if (h < NH) {
-#pragma unroll 8
-            for (int i = 0; i < CPH; ++i) {
-                const int c0 = h * CPH + i;
-                const double cv = (double)Cm[c0 * D + j];   // C[j][c0], by symmetry
+            // products summed 8 at a time in fp32 (C and B are fp32), the
+            // partial sums accumulated in fp64: one conversion per 8 products
+            for (int i0 = 0; i0 < CPH; i0 += 8) {
+                float wf[RKX];
 #pragma unroll
-                for (int c = 0; c < RKX; ++c) wp[c] += cv * (double)s_b[c0 * RKX + c];
+                for (int c = 0; c < RKX; ++c) wf[c] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int c0 = h * CPH + i0 + i;
+                    const float cv = Cm[c0 * D + j];   // C[j][c0], by symmetry
+#pragma unroll
+                    for (int c = 0; c < RKX; ++c) wf[c] = fmaf(cv, s_b[c0 * RKX + c], wf[c]);
+                }
+#pragma unroll
+                for (int c = 0; c < RKX; ++c) wp[c] += (double)wf[c];
             }
         }
         if (h > 0 && h < NH) {
