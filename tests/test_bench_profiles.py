@@ -120,3 +120,16 @@ def test_sweep_table_from_a_sweep_line(tmp_path):
     row = [l for l in t.splitlines() if l.startswith("gear_4bit ")][0].split()
     assert row[1] == "1000.0" and row[2] == "200" and float(row[4]) == 2.5
     assert "(300, oom, -)" in t
+
+
+@pytest.mark.parametrize("workload", ["7b_layer", "2bit", "long_ctx", "stream_gqa"])
+def test_committed_profiles_match_the_current_kernel_sources(workload):
+    """The benchmark line's roofline and compress-phase objects take measured
+    bytes and counters from the committed profiles only while their source
+    digests match the kernels as they are now: after a kernel change the
+    profiles must be made again (bench.py --make-profiles)."""
+    for kind in ("hbm_bytes", "sq_counters"):
+        for kernel in ("select", "compress", "lowrank_a", "decompress"):
+            row = bench.read_profile_row(kind, workload, kernel)
+            assert row is not None, (f"profiles/gear_kernels_{workload}_{kind}.txt has no {kernel} row "
+                                     f"for the current sources ({bench.source_digest(kernel)})")
